@@ -1,0 +1,202 @@
+"""fp64 CPU oracle for the learnable butterfly rotation and its quantizer.
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, by the smoke check and
+by the CPU-baseline leg of the benchmark.  The product library never imports,
+links or calls anything here, and nothing here imports the product package.
+
+The arithmetic lives in ``bflyref.c`` (plain C, fp64, one loop iteration per
+Givens pair); this module only builds it with gcc and marshals numpy arrays.
+Each function cites the passage of the pages it follows:
+
+* forward / kron_forward -- "ButterflyQuant" abstract (Fugu-MT page,
+  arXiv 2509.09679): orthogonal Q from continuous Givens angles,
+  n log n / 2 parameters, O(n log n) work; duidaima.com write-up, section
+  "butterfly": Hadamard special case and the Kronecker composite for 5120.
+* quantize -- WUSH page (gist.science), technical summary section 2: RTN
+  quantizer with absmax block scaling; ButterflyQuant abstract: transforms
+  are applied before quantization.
+* backward -- ButterflyQuant abstract and duidaima.com section "training and
+  results": the angles are learned by gradient descent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bflyref.c")
+_LIB = os.path.join(_HERE, "libbflyref.so")
+
+F32 = 0
+BF16 = 1
+SYM = 0
+ASYM = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        vp, i64, i32, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.bflyref_forward.argtypes = [vp, ctypes.c_int, dp, i64, i32, vp]
+        lib.bflyref_kron_forward.argtypes = [vp, ctypes.c_int, dp, i64, i32, i32, vp, vp]
+        lib.bflyref_quantize.argtypes = [dp, i64, i32, i32, i32, i32, i32, vp, vp, vp, dp, dp, dp]
+        lib.bflyref_backward.argtypes = [vp, vp, i64, i32, vp, dp, dp, dp, dp]
+        lib.bflyref_round_bf16.argtypes = [dp, vp, i64]
+        lib.bflyref_round_fp16.argtypes = [dp, vp, i64]
+        lib.bflyref_fp16_value.argtypes = [ctypes.c_uint16]
+        lib.bflyref_fp16_value.restype = ctypes.c_double
+        lib.bflyref_num_threads.restype = ctypes.c_int
+        for f in (lib.bflyref_forward, lib.bflyref_kron_forward, lib.bflyref_quantize,
+                  lib.bflyref_backward):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _x_dtype(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:  # bf16 bit patterns
+        return BF16
+    raise TypeError("oracle input must be float32 or uint16 (bf16 bits), got %s" % x.dtype)
+
+
+def num_threads() -> int:
+    return _load().bflyref_num_threads()
+
+
+def forward(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
+    """y = Q(theta) x for every row, fp64.  x: float32 or bf16 bits [rows][n];
+    theta: float32 [log2 n][n/2]."""
+    x = np.ascontiguousarray(x)
+    theta = np.ascontiguousarray(theta, dtype=np.float32)
+    rows, n = x.shape
+    y = np.empty((rows, n), dtype=np.float64)
+    rc = _load().bflyref_forward(_ptr(x), _x_dtype(x), _ptr(y), rows, n, _ptr(theta))
+    if rc != 0:
+        raise ValueError("bflyref_forward rejected its arguments")
+    return y
+
+
+def kron_forward(x: np.ndarray, theta_b: np.ndarray, mix: np.ndarray) -> np.ndarray:
+    """y = (O kron B(theta_b)) x, index i = a*nb + b; fp64."""
+    x = np.ascontiguousarray(x)
+    theta_b = np.ascontiguousarray(theta_b, dtype=np.float32)
+    mix = np.ascontiguousarray(mix, dtype=np.float32)
+    m = mix.shape[0]
+    rows, n = x.shape
+    nb = n // m
+    y = np.empty((rows, n), dtype=np.float64)
+    rc = _load().bflyref_kron_forward(_ptr(x), _x_dtype(x), _ptr(y), rows, m, nb,
+                                       _ptr(theta_b), _ptr(mix))
+    if rc != 0:
+        raise ValueError("bflyref_kron_forward rejected its arguments")
+    return y
+
+
+def quantize(y: np.ndarray, bits: int, group: int, mode: int, scales=None, zeros=None,
+             want_v: bool = False):
+    """Per-group RTN quantization of fp64 rows.
+
+    Returns a dict with codes (uint8), scales (uint16 fp16 bits), zeros (asym),
+    s_pre (fp64 scale before rounding), z_pre (asym) and optionally v (y/scale).
+    If ``scales`` (and ``zeros``) are given, the codes are computed at those
+    scales instead of the oracle's own."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    rows, n = y.shape
+    ng = n // group
+    codes = np.zeros((rows, n * bits // 8), dtype=np.uint8)
+    use_given = scales is not None
+    sc = np.ascontiguousarray(scales, dtype=np.uint16).copy() if use_given else \
+        np.zeros((rows, ng), dtype=np.uint16)
+    if mode == ASYM:
+        zr = np.ascontiguousarray(zeros, dtype=np.uint16).copy() if use_given else \
+            np.zeros((rows, ng), dtype=np.uint16)
+    else:
+        zr = None
+    s_pre = np.empty((rows, ng), dtype=np.float64)
+    z_pre = np.zeros((rows, ng), dtype=np.float64) if mode == ASYM else None
+    v = np.empty((rows, n), dtype=np.float64) if want_v else None
+    rc = _load().bflyref_quantize(_ptr(y), rows, n, group, bits, mode, 1 if use_given else 0,
+                                   _ptr(codes), _ptr(sc), _ptr(zr), _ptr(s_pre), _ptr(z_pre),
+                                   _ptr(v))
+    if rc != 0:
+        raise ValueError("bflyref_quantize rejected its arguments")
+    out = {"codes": codes, "scales": sc, "s_pre": s_pre}
+    if mode == ASYM:
+        out["zeros"] = zr
+        out["z_pre"] = z_pre
+    if want_v:
+        out["v"] = v
+    return out
+
+
+def backward(x: np.ndarray, g: np.ndarray, theta: np.ndarray, want_y=True, want_dx=True):
+    """Returns dict(y, dx, dtheta, dabs) in fp64 (see bflyref_backward)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    theta = np.ascontiguousarray(theta, dtype=np.float32)
+    rows, n = x.shape
+    L = theta.shape[0]
+    y = np.empty((rows, n), dtype=np.float64) if want_y else None
+    dx = np.empty((rows, n), dtype=np.float64) if want_dx else None
+    dth = np.empty((L, n // 2), dtype=np.float64)
+    dab = np.empty((L, n // 2), dtype=np.float64)
+    rc = _load().bflyref_backward(_ptr(x), _ptr(g), rows, n, _ptr(theta), _ptr(y), _ptr(dx),
+                                   _ptr(dth), _ptr(dab))
+    if rc != 0:
+        raise ValueError("bflyref_backward rejected its arguments")
+    return {"y": y, "dx": dx, "dtheta": dth, "dabs": dab}
+
+
+def round_bf16(y: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest even, directly from fp64."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint16)
+    _load().bflyref_round_bf16(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def round_fp16(y: np.ndarray) -> np.ndarray:
+    """fp64 -> fp16 bits, round to nearest even, directly from fp64."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint16)
+    _load().bflyref_round_fp16(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def fp16_value(h: int) -> float:
+    return _load().bflyref_fp16_value(int(h))
+
+
+def dense_q(theta: np.ndarray) -> np.ndarray:
+    """Dense Q (n x n) built column by column from unit vectors: column k is
+    Q e_k.  For tests at small n only."""
+    theta = np.asarray(theta, dtype=np.float32)
+    n = theta.shape[1] * 2
+    eye = np.eye(n, dtype=np.float32)
+    return forward(eye, theta).T.copy()

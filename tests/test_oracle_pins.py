@@ -1,0 +1,424 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+None of these compares the oracle with itself: each check is a closed form,
+an invariant, a textbook/library routine, brute force, or a value worked out
+by hand (tests/golden/).  A plausible slip anywhere in the oracle (dropped
+term, wrong sign, wrong pair index or stage order, transposed operand, bad
+rounding) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from learnable_butterfly_rotation_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def rand_theta(n, rng=RNG):
+    L = int(math.log2(n))
+    return rng.uniform(-math.pi, math.pi, size=(L, n // 2)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Rounding helpers (the oracle's own fp64 -> bf16 / fp16 conversions)
+# ---------------------------------------------------------------------------
+
+def test_fp16_rounding_matches_numpy():
+    # numpy converts float64 -> float16 directly with round-to-nearest-even
+    vals = np.concatenate([
+        RNG.standard_normal(20000) * 10.0 ** RNG.integers(-9, 5, 20000),
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e-8, 2.0 ** -24, 2.0 ** -25,
+                  3 * 2.0 ** -26, 2.0 ** -14, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11]),
+    ])
+    got = oracle.round_fp16(vals)
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_hand_values_and_fp32_grid():
+    # ties to even at the bf16 grid near 1 (spacing 2^-7)
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,          # midpoint 1 | 1+2^-7 -> even (1.0)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,      # midpoint 1+2^-7 | 1+2^-6 -> even
+        1.0 + 2.0 ** -8 + 2.0 ** -40: 0x3F81,  # just above the midpoint -> up
+        -1.0: 0xBF80,
+        0.0: 0x0000,
+        2.0 ** -133: 0x0001,              # smallest bf16 subnormal
+        3.0 * 2.0 ** -134: 0x0002,        # tie between 1 and 2 subnormal units -> even
+    }
+    for v, want in cases.items():
+        assert oracle.round_bf16(np.array([v]))[0] == want, v
+    # on values exactly representable in fp32 there is no double rounding, so
+    # the textbook fp32 bit trick must agree
+    x32 = (RNG.standard_normal(50000) * 10.0 ** RNG.integers(-30, 30, 50000)).astype(np.float32)
+    got = oracle.round_bf16(x32.astype(np.float64))
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(x32))
+
+
+# ---------------------------------------------------------------------------
+# Forward: Q(theta)
+# ---------------------------------------------------------------------------
+
+def test_n2_is_textbook_rotation():
+    for t in [0.3, -2.5, 1.0471975511965976, math.pi / 2]:
+        th = np.array([[t]], dtype=np.float32)
+        q = oracle.dense_q(th)
+        tt = float(np.float32(t))
+        want = np.array([[math.cos(tt), -math.sin(tt)], [math.sin(tt), math.cos(tt)]])
+        assert np.abs(q - want).max() < 1e-15
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_orthogonal_and_norm_preserving(n):
+    th = rand_theta(n)
+    q = oracle.dense_q(th)
+    assert np.abs(q.T @ q - np.eye(n)).max() <= 1e-12
+    assert np.abs(q @ q.T - np.eye(n)).max() <= 1e-12
+    x = RNG.standard_normal((5, n)).astype(np.float32)
+    y = oracle.forward(x, th)
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)
+    assert np.abs(np.linalg.norm(y, axis=1) - nx).max() <= 1e-13 * nx.max()
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
+def test_quarter_pi_is_sylvester_hadamard(n):
+    """All angles pi/4: Q D = H_n, D = diag((-1)^popcount(i)), Sylvester order;
+    every |Q_ij| = 1/sqrt(n) (optimal coherence)."""
+    L = int(math.log2(n))
+    th = np.full((L, n // 2), math.pi / 4, dtype=np.float32)
+    q = oracle.dense_q(th)
+    h = np.array([[1.0]])
+    for _ in range(L):
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    h /= math.sqrt(n)
+    d = np.array([(-1.0) ** bin(i).count("1") for i in range(n)])
+    # fp32(pi/4) is not exactly pi/4: cos/sin are off by ~2e-8
+    assert np.abs(q * d[None, :] - h).max() < 1e-7
+    assert np.abs(np.abs(q) - 1 / math.sqrt(n)).max() < 1e-7
+
+
+def test_hadamard_golden_n8():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "hadamard_sylvester_n8.txt"))
+            if l.strip() and not l.startswith("#")]
+    h8 = np.array([[float(v) for v in r] for r in rows]) / math.sqrt(8)
+    th = np.full((3, 4), math.pi / 4, dtype=np.float32)
+    q = oracle.dense_q(th)
+    d = np.array([(-1.0) ** bin(i).count("1") for i in range(8)])
+    assert np.abs(q * d[None, :] - h8).max() < 1e-7
+
+
+def test_hand_worked_examples():
+    for line in open(os.path.join(GOLDEN, "butterfly_hand_examples.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        n_s, th_s, x_s, y_s = [f.strip() for f in line.split("|")]
+        n = int(n_s)
+        th = np.array([[float(v) for v in st.split()] for st in th_s.split(";")],
+                      dtype=np.float32)
+        x = np.array([[float(v) for v in x_s.split()]], dtype=np.float32)
+        want = np.array([float(v) for v in y_s.split()])
+        got = oracle.forward(x, th)[0]
+        assert got.shape == (n,)
+        assert np.abs(got - want).max() < 1e-6, (line, got)
+
+
+def test_zero_angles_identity():
+    th = np.zeros((6, 32), dtype=np.float32)
+    assert np.array_equal(oracle.dense_q(th), np.eye(64))
+
+
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_single_angle_places_one_givens_block(n):
+    """One nonzero angle theta[s][p]: Q is the identity except the 2x2
+    rotation on the p-th pair (i, i + 2^s) of stage s, pairs listed by
+    increasing i (found here by enumeration, not by the closed form)."""
+    L = int(math.log2(n))
+    for s in range(L):
+        pairs = [(i, i + (1 << s)) for i in range(n) if not (i >> s) & 1]
+        for p, (i, j) in enumerate(pairs):
+            th = np.zeros((L, n // 2), dtype=np.float32)
+            th[s, p] = 0.7
+            t = float(np.float32(0.7))
+            want = np.eye(n)
+            want[i, i] = want[j, j] = math.cos(t)
+            want[i, j] = -math.sin(t)
+            want[j, i] = math.sin(t)
+            assert np.abs(oracle.dense_q(th) - want).max() < 1e-15, (s, p)
+
+
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_stage_order_is_product_of_stage_matrices(n):
+    """Q = B_{L-1} ... B_1 B_0 where B_s is the dense stage matrix (identity
+    with one rotation block per pair); built here as single-angle matrices
+    multiplied with numpy, so a reversed stage order or a per-pair index slip
+    fails."""
+    L = int(math.log2(n))
+    th = rand_theta(n)
+    q = np.eye(n)
+    for s in range(L):
+        bs = np.eye(n)
+        for p in range(n // 2):
+            t = np.zeros((L, n // 2), dtype=np.float32)
+            t[s, p] = th[s, p]
+            bs = oracle.dense_q(t) @ bs  # disjoint blocks commute
+        q = bs @ q
+    assert np.abs(oracle.dense_q(th) - q).max() < 1e-14
+
+
+def test_computational_invariance():
+    """(W Q^T)(Q x) = W x, with W Q^T computed by applying the same row
+    forward to W's rows (ButterflyQuant abstract)."""
+    n = 128
+    th = rand_theta(n)
+    w = RNG.standard_normal((48, n)).astype(np.float32)
+    x = RNG.standard_normal((7, n)).astype(np.float32)
+    wq = oracle.forward(w, th)          # rows of W Q^T
+    qx = oracle.forward(x, th)          # rows of Q x
+    lhs = qx @ wq.T
+    rhs = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(rhs).max()
+
+
+def test_bf16_input_widening():
+    n = 64
+    th = rand_theta(n)
+    x32 = RNG.standard_normal((3, n)).astype(np.float32)
+    xb = inputs.f32_to_bf16_bits(x32)
+    got = oracle.forward(xb, th)
+    want = oracle.forward(inputs.bf16_bits_to_f32(xb).reshape(3, n), th)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("m,nb", [(3, 8), (5, 16), (1, 32)])
+def test_kron_equals_numpy_kron(m, nb):
+    th = rand_theta(nb)
+    mix = inputs.mixing_factor(RNG, m)
+    b = oracle.dense_q(th)
+    want_q = np.kron(mix.astype(np.float64), b)
+    x = RNG.standard_normal((4, m * nb)).astype(np.float32)
+    got = oracle.kron_forward(x, th, mix)
+    want = x.astype(np.float64) @ want_q.T
+    assert np.abs(got - want).max() < 1e-13 * np.abs(want).max()
+
+
+def test_kron_orthogonal_with_fp64_mix():
+    # the fp32 O5 is orthonormal only to ~1e-7; with an exactly orthonormal
+    # O (a signed permutation) the composite is orthogonal to 1e-12
+    nb, m = 16, 4
+    th = rand_theta(nb)
+    perm = np.zeros((m, m), dtype=np.float32)
+    for a, a2 in enumerate([2, 0, 3, 1]):
+        perm[a, a2] = -1.0 if a % 2 else 1.0
+    eye = np.eye(m * nb, dtype=np.float32)
+    q = oracle.kron_forward(eye, th, perm).T
+    assert np.abs(q.T @ q - np.eye(m * nb)).max() <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Quantizer
+# ---------------------------------------------------------------------------
+
+def _parse_quant_golden():
+    for line in open(os.path.join(GOLDEN, "quant_hand_examples.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        head, y_s, s_s, z_s, c_s = [f.strip() for f in line.split("|")]
+        bits, mode = head.split()
+        yield (int(bits), oracle.SYM if mode == "sym" else oracle.ASYM,
+               np.array([[float(v) for v in y_s.split()]]), int(s_s, 16),
+               None if z_s == "-" else int(z_s, 16), bytes.fromhex(c_s.replace(" ", "")))
+
+
+def test_quant_hand_examples():
+    for bits, mode, y, s16, z16, codes in _parse_quant_golden():
+        q = oracle.quantize(y, bits, y.shape[1], mode)
+        assert q["scales"][0, 0] == s16
+        if z16 is not None:
+            assert q["zeros"][0, 0] == z16
+        assert bytes(q["codes"][0]) == codes, (y, q["codes"])
+
+
+def unpack(codes, bits, n, signed):
+    per = 8 // bits
+    out = np.zeros((codes.shape[0], n), dtype=np.int64)
+    for e in range(n):
+        v = (codes[:, e // per].astype(np.int64) >> (bits * (e % per))) & ((1 << bits) - 1)
+        if signed:
+            v = np.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
+        out[:, e] = v
+    return out
+
+
+def half_to_float(h):
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("bits,mode", [(4, oracle.SYM), (2, oracle.SYM), (4, oracle.ASYM),
+                                       (2, oracle.ASYM)])
+def test_quant_brute_force_nearest_level(bits, mode):
+    """Every code is the nearest representable level to y (searched over all
+    codes), with ties only at exact midpoints; error <= scale/2 unclamped."""
+    group, rows = 16, 300
+    y = RNG.standard_normal((rows, 64)) * np.exp(RNG.uniform(-3, 3, (rows, 1)))
+    q = oracle.quantize(y, bits, group, mode, want_v=True)
+    sc = np.repeat(half_to_float(q["scales"]), group, axis=1)
+    signed = mode == oracle.SYM
+    codes = unpack(q["codes"], bits, 64, signed)
+    if signed:
+        qmax = (1 << (bits - 1)) - 1
+        levels = np.arange(-qmax, qmax + 1)
+        zero = np.zeros_like(sc)
+    else:
+        levels = np.arange(0, (1 << bits))
+        zero = np.repeat(half_to_float(q["zeros"]), group, axis=1)
+        assert np.all(zero == np.round(zero)) and np.all((zero >= 0) & (zero < (1 << bits)))
+    recon = (codes - zero) * sc
+    # brute force: best level for each element
+    cand = (levels[None, None, :] - zero[..., None]) * sc[..., None]
+    dist = np.abs(cand - y[..., None])
+    best = dist.min(axis=2)
+    assert np.all(np.abs(recon - y) <= best + 1e-12 * np.abs(y))
+    # unclamped elements (inside the level range) are within scale/2
+    inside = (y >= cand.min(axis=2)) & (y <= cand.max(axis=2))
+    assert np.all(np.abs(recon - y)[inside] <= sc[inside] / 2 * (1 + 1e-12))
+    # the scale is the fp16-rounded pre-scale
+    assert np.array_equal(q["scales"], oracle.round_fp16(q["s_pre"]))
+    if signed:
+        a = np.abs(y).reshape(rows, -1, group).max(axis=2)
+        assert np.allclose(q["s_pre"], a / ((1 << (bits - 1)) - 1), rtol=1e-15, atol=0)
+    else:
+        yy = y.reshape(rows, -1, group)
+        assert np.allclose(q["s_pre"], (yy.max(2) - yy.min(2)) / ((1 << bits) - 1),
+                           rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_byte_count_and_roundtrip(bits):
+    """Packed bytes per row = n * bits / 8 (16-bit -> 2-bit is 8x smaller);
+    unpacking then re-packing by hand returns the same bytes."""
+    n, group = 256, 128
+    y = RNG.standard_normal((9, n))
+    q = oracle.quantize(y, bits, group, oracle.SYM)
+    assert q["codes"].shape == (9, n * bits // 8)
+    assert (n * 2) / q["codes"].shape[1] == 16 / bits
+    c = unpack(q["codes"], bits, n, signed=False)
+    per = 8 // bits
+    repacked = np.zeros_like(q["codes"])
+    for e in range(n):
+        repacked[:, e // per] |= (c[:, e] << (bits * (e % per))).astype(np.uint8)
+    assert np.array_equal(repacked, q["codes"])
+
+
+def test_quant_requantize_at_given_scale():
+    y = RNG.standard_normal((4, 128))
+    q = oracle.quantize(y, 4, 128, oracle.SYM)
+    q2 = oracle.quantize(y, 4, 128, oracle.SYM, scales=q["scales"])
+    assert np.array_equal(q["codes"], q2["codes"])
+    bumped = q["scales"] + 1  # next fp16 up: codes may move, never beyond +-7
+    q3 = oracle.quantize(y, 4, 128, oracle.SYM, scales=bumped, want_v=True)
+    sc = np.repeat(half_to_float(bumped), 128, axis=1)
+    assert np.allclose(q3["v"], y / sc, rtol=0, atol=1e-15)
+
+
+def test_scale_saturates_at_fp16_max():
+    y = np.full((1, 8), 1e6)
+    y[0, 1] = -1e6
+    q = oracle.quantize(y, 4, 8, oracle.SYM)
+    assert q["scales"][0, 0] == 0x7BFF
+    assert bytes(q["codes"][0]) == bytes([0x97, 0x77, 0x77, 0x77])
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [4, 16])
+def test_backward_matches_finite_differences(n):
+    """dtheta against central differences of L = sum(G * Q(theta) X), with
+    Richardson extrapolation; the perturbed angles are fp32, so the exact
+    fp32 step is used as the denominator."""
+    L = int(math.log2(n))
+    th = rand_theta(n)
+    x = RNG.standard_normal((3, n)).astype(np.float32)
+    g = RNG.standard_normal((3, n)).astype(np.float32)
+    out = oracle.backward(x, g, th)
+    g64 = g.astype(np.float64)
+
+    def loss(t):
+        return float((oracle.forward(x, t) * g64).sum())
+
+    def fd(s, p, h):
+        tp, tm = th.copy(), th.copy()
+        tp[s, p] = np.float32(th[s, p] + h)
+        tm[s, p] = np.float32(th[s, p] - h)
+        return (loss(tp) - loss(tm)) / (float(tp[s, p]) - float(tm[s, p]))
+
+    for s in range(L):
+        for p in range(n // 2):
+            d1, d2 = fd(s, p, 2.0 ** -7), fd(s, p, 2.0 ** -8)
+            rich = (4 * d2 - d1) / 3
+            assert abs(rich - out["dtheta"][s, p]) < 1e-6 * (1 + abs(rich)), (s, p)
+
+
+def test_backward_dx_is_dense_transpose_and_y_is_forward():
+    n = 32
+    th = rand_theta(n)
+    x = RNG.standard_normal((6, n)).astype(np.float32)
+    g = RNG.standard_normal((6, n)).astype(np.float32)
+    out = oracle.backward(x, g, th)
+    q = oracle.dense_q(th)
+    assert np.abs(out["dx"] - g.astype(np.float64) @ q).max() < 1e-13
+    assert np.abs(out["y"] - x.astype(np.float64) @ q.T).max() < 1e-13
+    # dabs bounds |dtheta| term by term
+    assert np.all(np.abs(out["dtheta"]) <= out["dabs"] * (1 + 1e-12))
+
+
+def test_backward_invariant_g_equals_y():
+    """With G = Y the loss 0.5 ||Q X||^2 = 0.5 ||X||^2 does not depend on the
+    angles: dtheta = 0 exactly (up to rounding) and dX = X."""
+    n = 64
+    th = rand_theta(n)
+    x = RNG.standard_normal((5, n)).astype(np.float32)
+    # G must be fp32: feed G = fp32(Y) and compare against the exact identity
+    # within the fp32 rounding of G
+    y = oracle.forward(x, th)
+    g = y.astype(np.float32)
+    out = oracle.backward(x, g, th)
+    assert np.abs(out["dtheta"]).max() <= 1e-6 * out["dabs"].max()
+    assert np.abs(out["dx"] - x.astype(np.float64)).max() < 1e-6
+
+
+def test_backward_rows_additive():
+    n = 16
+    th = rand_theta(n)
+    x = RNG.standard_normal((10, n)).astype(np.float32)
+    g = RNG.standard_normal((10, n)).astype(np.float32)
+    a = oracle.backward(x, g, th)["dtheta"]
+    b = oracle.backward(x[:4], g[:4], th)["dtheta"] + oracle.backward(x[4:], g[4:], th)["dtheta"]
+    assert np.abs(a - b).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Generators (no method arithmetic; shapes and determinism only)
+# ---------------------------------------------------------------------------
+
+def test_generators_are_prefix_stable_and_seeded():
+    a = inputs.act_int4(rows=16)
+    b = inputs.act_int4(rows=40)
+    assert np.array_equal(a["x"], b["x"][:16])
+    assert np.array_equal(a["theta"], b["theta"])
+    assert a["theta"].shape == (12, 2048) and a["theta"].dtype == np.float32
+    assert len(a["outliers"]) == 4
+    c = inputs.CalibFP32()
+    x1 = np.concatenate([xc for _, xc, _ in c.chunks(7, limit_rows=20)])
+    x2 = np.concatenate([xc for _, xc, _ in c.chunks(20, limit_rows=20)])
+    assert np.array_equal(x1, x2)
+    k = inputs.kron_int4(rows=4)
+    assert np.abs(k["mix"].astype(np.float64) @ k["mix"].T - np.eye(5)).max() < 1e-6
+    assert k["theta_b"].shape == (10, 512)
