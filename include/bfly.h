@@ -1,0 +1,174 @@
+/*
+ * bfly.h -- C ABI of libbfly: the learnable butterfly rotation and its fused
+ * round-to-nearest quantization, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are the pages' titles and sections):
+ *
+ *   Q(theta) is the product of L = log2(n) Givens stages, Q = B_{L-1} ... B_0.
+ *   Stage s rotates, for every i whose bit s is clear, the pair (i, j = i + 2^s)
+ *   by its own angle t = theta[s][p], where p = (i >> (s+1)) * 2^s + (i mod 2^s)
+ *   ranks the pair among the stage's pairs by increasing i:
+ *       (u_i, u_j) <- (cos t * u_i - sin t * u_j,  sin t * u_i + cos t * u_j).
+ *   That is n log2(n) / 2 angles and O(n log n) work per row, orthogonal for
+ *   every theta ("ButterflyQuant: Ultra-low-bit LLM Quantization through
+ *   Learnable Orthogonal Butterfly Transforms", abstract).  With every angle
+ *   pi/4, Q times diag((-1)^popcount(i)) is the Sylvester Hadamard matrix
+ *   (duidaima.com write-up of ButterflyQuant, section "butterfly").
+ *
+ *   Rows are rotated independently.  Applied to activation rows this gives
+ *   Q x; applied to the rows of a weight matrix W it gives the rows of W Q^T,
+ *   so that W x = (W Q^T)(Q x) (ButterflyQuant abstract, computational
+ *   invariance).  The stage order (s = 0 first), the pairing, the sign of the
+ *   rotation and the angle layout are conventions the pages leave open.
+ *
+ * Conventions common to every call:
+ *   - All data pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major with a row stride of n elements (bytes for codes: n*bits/8).
+ *     x, y, codes and g/dx must be 16-byte aligned; scales and zeros 2-byte.
+ *   - y == x (in place) is allowed, as is dx == g; no other aliasing.
+ *   - theta: fp32 angles [log2 n][n/2] on the device.
+ *   - coeffs: optional device table prepared from theta by bfly_prepare().
+ *     When coeffs is non-NULL, theta is not read (it may be NULL) and no
+ *     preparation runs.  When coeffs is NULL the call prepares the table
+ *     itself from theta into stream-ordered scratch taken with
+ *     hipMallocAsync/hipFreeAsync on hip_stream (bfly_backward uses its
+ *     workspace instead and allocates nothing).
+ *   - hip_stream: a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     and return; results are valid once the stream is synchronised.
+ *   - rows == 0 is a no-op returning BFLY_OK (bfly_backward then writes
+ *     zeros to dtheta); the row-data pointers may then be NULL.
+ *   - Every argument is validated before any HIP call; a validation failure
+ *     returns its code and enqueues nothing.  A failed HIP call returns
+ *     BFLY_ERR_HIP; the HIP error code is then available from
+ *     bfly_last_hip_error() on the calling thread.
+ *   - Supported sizes: n a power of two in [64, 4096] (smaller powers of
+ *     two and 8192 return BFLY_ERR_UNSUPPORTED); for the Kronecker call
+ *     m in [1, 8] and nb a power of two with m * nb <= 8192, nb in
+ *     [256, 4096] for m >= 2 and in [64, 4096] for m = 1.
+ *   - Results do not depend on the launch configuration or on the device's
+ *     compute-unit count (the angle-gradient reduction order is fixed).
+ */
+#ifndef BFLY_H
+#define BFLY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BFLY_OK = 0,
+    BFLY_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    BFLY_ERR_SIZE = 2,        /* rows < 0, n not a power of two, m*nb mismatch ... */
+    BFLY_ERR_DTYPE = 3,       /* dtype not in bfly_dtype                           */
+    BFLY_ERR_ALIGN = 4,       /* a pointer is not aligned as stated above          */
+    BFLY_ERR_QUANT = 5,       /* bits / group / mode / zeros combination invalid   */
+    BFLY_ERR_WORKSPACE = 6,   /* workspace or coefficient buffer too small         */
+    BFLY_ERR_UNSUPPORTED = 7, /* a valid size this build does not handle           */
+    BFLY_ERR_HIP = 8          /* a HIP runtime call failed                         */
+} bfly_status;
+
+typedef enum { BFLY_F32 = 0, BFLY_BF16 = 1 } bfly_dtype;
+
+/* Quantizer modes (WUSH page, technical summary section 2: round-to-nearest
+ * with absmax block scaling; ButterflyQuant abstract: 2-bit weights).
+ *   BFLY_SYM_ABSMAX : scale = fp16(absmax / qmax), qmax = 2^(bits-1) - 1,
+ *                     q = clamp(rne(y / scale), -qmax, qmax), stored as a
+ *                     two's-complement bit field.
+ *   BFLY_ASYM_MINMAX: scale = fp16((max - min) / (2^bits - 1)),
+ *                     zero  = clamp(rne(-min / scale), 0, 2^bits - 1) (an
+ *                     integer, stored exactly as fp16),
+ *                     q = clamp(rne(y / scale) + zero, 0, 2^bits - 1).
+ *   A scale above 65504 saturates to 65504; a zero scale gives zero codes
+ *   (and a zero point of 0).  rne = round to nearest, ties to even; the
+ *   quantized value is the fp32 y before any bf16 rounding of the output. */
+typedef enum { BFLY_SYM_ABSMAX = 0, BFLY_ASYM_MINMAX = 1 } bfly_qmode;
+
+/* ---- angle preparation ------------------------------------------------- */
+
+/* Bytes of the coefficient table for a butterfly of length n (0 if n is not
+ * supported). */
+size_t bfly_coeff_bytes(int32_t n);
+
+/* Turn angles theta (device fp32 [log2 n][n/2]) into the device coefficient
+ * table `coeffs` (caller-owned, >= bfly_coeff_bytes(n) bytes, 16-byte
+ * aligned).  The table depends only on theta; it stays valid for any number
+ * of calls with the same angles.  Passage: ButterflyQuant abstract
+ * (continuous Givens rotation angles). */
+bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coeff_bytes,
+                         void* hip_stream);
+
+/* ---- forward ------------------------------------------------------------ */
+
+/* y[r] = Q(theta) x[r] for r < rows.  x_dt, y_dt in {BFLY_F32, BFLY_BF16};
+ * bf16 outputs are rounded to nearest even from fp32.  Passage: ButterflyQuant
+ * abstract (Q x and W Q^T). */
+bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                         int64_t rows, int32_t n, const float* theta, const void* coeffs,
+                         void* hip_stream);
+
+/* The forward, fused with per-group round-to-nearest quantization of y.
+ *   y      : may be NULL (codes only); else [rows][n] of y_dt
+ *   codes  : u8 [rows][n*bits/8], element e of a byte group in bits
+ *            [bits*e, bits*(e+1)) (little-endian packing)
+ *   scales : fp16 bit patterns [rows][n/group]
+ *   zeros  : fp16 bit patterns [rows][n/group] for BFLY_ASYM_MINMAX; must be
+ *            NULL for BFLY_SYM_ABSMAX
+ *   bits   : 2 or 4; group: 8, 16, 32, 64, 128, 256 or 512, dividing n;
+ *            groups are runs of `group` consecutive output elements.
+ * Passages: ButterflyQuant abstract (orthogonal transforms applied before
+ * quantization), WUSH technical summary section 2 (RTN absmax quantizer). */
+bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                               uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                               int64_t rows, int32_t n, const float* theta, const void* coeffs,
+                               int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
+
+/* Kronecker composite for widths n = m * nb that are not a power of two
+ * (duidaima.com write-up, section "butterfly": LLaMA-2-13B's 5120):
+ *   y[r] = (O kron B(theta_b)) x[r], index i = a * nb + b (a < m, b < nb):
+ *   the butterfly B (angles theta_b [log2 nb][nb/2], or its prepared table
+ *   coeffs_b) acts on each segment a, then the dense m x m factor
+ *   mix (device fp32, row-major) mixes the segments column by column:
+ *   y[a*nb + b] = sum_a' mix[a][a'] z[a'*nb + b].
+ * codes == NULL => no quantization (scales and zeros must then be NULL);
+ * otherwise as in bfly_forward_quant, with group dividing nb. */
+bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                              uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                              int64_t rows, int32_t m, int32_t nb, const float* theta_b,
+                              const void* coeffs_b, const float* mix,
+                              int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
+
+/* ---- backward ----------------------------------------------------------- */
+
+/* Gradients for learning the angles (ButterflyQuant abstract: smooth
+ * optimisation of the continuous angles; duidaima.com write-up, section
+ * "training and results").  Given X and G = dL/dY (device fp32 [rows][n]),
+ * with Y = Q(theta) X row by row:
+ *   y      : Y (optional, may be NULL)            fp32 [rows][n]
+ *   dx     : Q^T G                                fp32 [rows][n]
+ *   dtheta : sum over rows of dL/dtheta           fp32 [log2 n][n/2], OVERWRITTEN
+ * For the pair (i, j) of stage s, with v that stage's output and g the
+ * gradient w.r.t. it, dL/dtheta[s][p] = g_j v_i - g_i v_j.  The row sum is a
+ * fixed-order two-pass reduction: bit-identical results from run to run.
+ * workspace: device scratch of >= bfly_backward_workspace_bytes(rows, n)
+ * bytes, 16-byte aligned; the call allocates nothing. */
+bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, float* dtheta,
+                          int64_t rows, int32_t n, const float* theta, const void* coeffs,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n);
+
+/* ---- diagnostics -------------------------------------------------------- */
+
+const char* bfly_status_string(bfly_status s);
+
+/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t bfly_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFLY_H */

@@ -1,1 +1,170 @@
-"""learnable_butterfly_rotation_amd: MI355X (gfx950) butterfly rotation + fused RTN quantization."""
+"""learnable_butterfly_rotation_amd -- MI355X (gfx950) learnable butterfly
+rotation fused with round-to-nearest group quantization.
+
+Thin ctypes binding over the C ABI of ``libbfly.so`` (include/bfly.h).  The
+functions carry the C names; they only marshal torch tensors into pointers,
+sizes and the current HIP stream -- every step of the computation runs in the
+library's HIP kernels.  There is no CPU fallback: if the library is missing
+or no GPU is present the calls raise.
+
+Build the library with ``python -m learnable_butterfly_rotation_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
+    "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_forward", "bfly_forward_quant",
+    "bfly_kron_forward", "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
+    "bfly_last_hip_error",
+]
+
+BFLY_F32 = 0
+BFLY_BF16 = 1
+BFLY_SYM_ABSMAX = 0
+BFLY_ASYM_MINMAX = 1
+
+STATUS_NAMES = {0: "BFLY_OK", 1: "BFLY_ERR_NULL", 2: "BFLY_ERR_SIZE", 3: "BFLY_ERR_DTYPE",
+                4: "BFLY_ERR_ALIGN", 5: "BFLY_ERR_QUANT", 6: "BFLY_ERR_WORKSPACE",
+                7: "BFLY_ERR_UNSUPPORTED", 8: "BFLY_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libbfly.so")
+_lib = None
+
+
+class BflyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s: %s (%s)" % (where, STATUS_NAMES.get(status, status), bfly_status_string(status))
+        if status == 8:
+            msg += ", hipError %d" % bfly_last_hip_error()
+        super().__init__(msg)
+
+
+def lib():
+    """The loaded libbfly.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError("libbfly.so is not built: run "
+                               "`python -m learnable_butterfly_rotation_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.bfly_coeff_bytes.argtypes = [i32]
+        L.bfly_coeff_bytes.restype = sz
+        L.bfly_prepare.argtypes = [vp, i32, vp, sz, vp]
+        L.bfly_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, vp]
+        L.bfly_forward_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
+                                         vp, vp, i32, i32, ctypes.c_int, vp]
+        L.bfly_kron_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
+                                        i32, vp, vp, vp, i32, i32, ctypes.c_int, vp]
+        L.bfly_backward.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
+        L.bfly_backward_workspace_bytes.argtypes = [i64, i32]
+        L.bfly_backward_workspace_bytes.restype = sz
+        L.bfly_status_string.argtypes = [ctypes.c_int]
+        L.bfly_status_string.restype = ctypes.c_char_p
+        L.bfly_last_hip_error.restype = i32
+        for f in (L.bfly_prepare, L.bfly_forward, L.bfly_forward_quant, L.bfly_kron_forward,
+                  L.bfly_backward):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.float32:
+        return BFLY_F32
+    if t.dtype == torch.bfloat16:
+        return BFLY_BF16
+    raise TypeError("libbfly takes float32 or bfloat16 rows, got %s" % t.dtype)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(status, where):
+    if status != 0:
+        raise BflyError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one function per entry point
+# ---------------------------------------------------------------------------
+
+def bfly_coeff_bytes(n: int) -> int:
+    return lib().bfly_coeff_bytes(n)
+
+
+def bfly_prepare(theta, n: int, coeffs, stream=None) -> None:
+    """coeffs (uint8 tensor of >= bfly_coeff_bytes(n) bytes) <- table of theta."""
+    _check(lib().bfly_prepare(_ptr(theta), n, _ptr(coeffs), coeffs.numel() * coeffs.element_size(),
+                              _stream(stream)), "bfly_prepare")
+
+
+def bfly_forward(x, y, theta=None, coeffs=None, stream=None) -> None:
+    """y[r] = Q(theta) x[r]; x, y: [rows, n] float32/bfloat16 on the GPU."""
+    rows, n = x.shape
+    _check(lib().bfly_forward(_ptr(x), _dt(x), _ptr(y), _dt(y), rows, n, _ptr(theta),
+                              _ptr(coeffs), _stream(stream)), "bfly_forward")
+
+
+def bfly_forward_quant(x, y, codes, scales, zeros=None, theta=None, coeffs=None, bits=4,
+                       group=128, mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+    """Forward fused with per-group RTN quantization (y may be None)."""
+    rows, n = x.shape
+    _check(lib().bfly_forward_quant(_ptr(x), _dt(x), _ptr(y), _dt(y) if y is not None else 0,
+                                    _ptr(codes), _ptr(scales), _ptr(zeros), rows, n, _ptr(theta),
+                                    _ptr(coeffs), bits, group, mode, _stream(stream)),
+           "bfly_forward_quant")
+
+
+def bfly_kron_forward(x, y, mix, codes=None, scales=None, zeros=None, theta_b=None, coeffs_b=None,
+                      bits=4, group=128, mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+    """(O kron B) on rows of n = m * nb; mix: [m, m] float32 on the GPU."""
+    rows, n = x.shape
+    m = mix.shape[0]
+    _check(lib().bfly_kron_forward(_ptr(x), _dt(x), _ptr(y), _dt(y) if y is not None else 0,
+                                   _ptr(codes), _ptr(scales), _ptr(zeros), rows, m, n // m,
+                                   _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), bits, group, mode,
+                                   _stream(stream)), "bfly_kron_forward")
+
+
+def bfly_backward_workspace_bytes(rows: int, n: int) -> int:
+    return lib().bfly_backward_workspace_bytes(rows, n)
+
+
+def bfly_backward(x, g, y, dx, dtheta, workspace, theta=None, coeffs=None, stream=None) -> None:
+    """y = Q x (optional), dx = Q^T g, dtheta = sum over rows of dL/dtheta."""
+    rows, n = x.shape
+    _check(lib().bfly_backward(_ptr(x), _ptr(g), _ptr(y), _ptr(dx), _ptr(dtheta), rows, n,
+                               _ptr(theta), _ptr(coeffs), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "bfly_backward")
+
+
+def bfly_status_string(status: int) -> str:
+    return lib().bfly_status_string(status).decode()
+
+
+def bfly_last_hip_error() -> int:
+    return lib().bfly_last_hip_error()

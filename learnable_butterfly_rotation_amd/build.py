@@ -1,0 +1,62 @@
+"""Build libbfly.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m learnable_butterfly_rotation_amd.build
+Each translation unit is compiled in parallel, then linked into a shared
+library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libbfly.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["bfly_api.hip", "bfly_bwd.hip", "bfly_fwd_plain.hip", "bfly_fwd_kron_a.hip",
+           "bfly_fwd_kron_b.hip"]
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    # no packed fp32 (v_pk_*_f32) code generation
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False, extra=None) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    t0 = time.time()
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.STDOUT, text=True)))
+    objs, failed = [], []
+    for src, obj, p in procs:
+        out, _ = p.communicate()
+        if verbose and out.strip():
+            print(out, file=sys.stderr)
+        if p.returncode != 0:
+            failed.append((src, out))
+        objs.append(obj)
+    if failed:
+        for src, out in failed:
+            print("---- %s ----\n%s" % (src, out), file=sys.stderr)
+        raise RuntimeError("hipcc failed for: " + ", ".join(s for s, _ in failed))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp],
+                   check=True)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built %s in %.1f s" % (LIB, time.time() - t0), file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

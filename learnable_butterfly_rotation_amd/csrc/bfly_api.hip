@@ -1,0 +1,270 @@
+// C ABI of libbfly (include/bfly.h): argument validation, workspace
+// accounting and dispatch to the kernel instantiations.  Every argument is
+// checked before the first HIP call, so all error paths can be exercised on
+// a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/bfly.h"
+#include "bfly_internal.h"
+
+namespace bfly {
+hipError_t launch_forward_plain(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_a(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_b(const FwdParams& p, hipStream_t s);
+
+bool forward_supported(int lognb, int m) {
+  if (m == 1) return lognb >= 6 && lognb <= 12;
+  if (m < 2 || m > 8) return false;
+  return lognb >= 8 && lognb <= 12 && ((int64_t)m << lognb) <= 8192;
+}
+
+hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
+  if (p.m == 1) return launch_forward_plain(p, s);
+  if (p.m <= 4) return launch_forward_kron_a(p, s);
+  return launch_forward_kron_b(p, s);
+}
+}  // namespace bfly
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bfly_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return BFLY_ERR_HIP;
+}
+
+int log2_pow2(int64_t n) {
+  if (n < 1 || (n & (n - 1)) != 0) return -1;
+  int l = 0;
+  while ((int64_t(1) << l) < n) ++l;
+  return l;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Butterfly length: power of two in [64, 8192] (smaller powers of two are
+// valid sizes this build does not handle).
+bfly_status check_n(int64_t n, int max_log, int* logn) {
+  const int l = log2_pow2(n);
+  if (l < 1) return BFLY_ERR_SIZE;
+  if (l < 6 || l > max_log) return BFLY_ERR_UNSUPPORTED;
+  *logn = l;
+  return BFLY_OK;
+}
+
+bool dtype_ok(int d) { return d == BFLY_F32 || d == BFLY_BF16; }
+
+size_t coeff_bytes_l(int logn) { return (size_t)logn * ((size_t)1 << (logn - 1)) * 8; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Rows handled together by one backward workgroup (threads per row = n / 8).
+int bwd_rows_per_block(int logn) {
+  const int t = (1 << logn) >> 3;
+  return (256 / t) > 0 ? 256 / t : 1;
+}
+
+// Data pointers may be NULL when there are no rows (empty tensors).
+bfly_status check_quant(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                        int64_t rows, int64_t n, int64_t seg, int logseg, int32_t bits,
+                        int32_t group, bfly_qmode mode) {
+  if (rows > 0 && (!codes || !scales)) return BFLY_ERR_NULL;
+  if (bits != 2 && bits != 4) return BFLY_ERR_QUANT;
+  if (mode != BFLY_SYM_ABSMAX && mode != BFLY_ASYM_MINMAX) return BFLY_ERR_QUANT;
+  if (rows > 0 && (mode == BFLY_ASYM_MINMAX) != (zeros != nullptr)) return BFLY_ERR_QUANT;
+  if (rows == 0 && mode == BFLY_SYM_ABSMAX && zeros != nullptr) return BFLY_ERR_QUANT;
+  const int lg = log2_pow2(group);
+  if (lg < 3 || lg > 9 || group > seg || seg % group != 0 || n % group != 0) return BFLY_ERR_QUANT;
+  if ((group * bits) % 8 != 0) return BFLY_ERR_QUANT;
+  // a thread holds 16 elements at length 8192 (8 elsewhere): groups of 8 would split it
+  if (logseg >= 13 && group < 16) return BFLY_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16)) return BFLY_ERR_ALIGN;
+  if (!aligned(scales, 2) || (zeros && !aligned(zeros, 2))) return BFLY_ERR_ALIGN;
+  return BFLY_OK;
+}
+
+// Runs `launch` with the coefficient table `coeffs`, or -- when coeffs is
+// NULL -- prepares the table from theta into stream-ordered scratch first.
+template <class F>
+bfly_status with_table(const float* theta, const void* coeffs, int logn, hipStream_t s, F launch) {
+  if (coeffs) {
+    const hipError_t e = launch(static_cast<const float2*>(coeffs));
+    return e == hipSuccess ? BFLY_OK : hip_fail(e);
+  }
+  void* tab = nullptr;
+  hipError_t e = hipMallocAsync(&tab, coeff_bytes_l(logn), s);
+  if (e != hipSuccess) return hip_fail(e);
+  const int64_t count = (int64_t)logn << (logn - 1);
+  e = bfly::launch_prepare(theta, static_cast<float2*>(tab), count, s);
+  if (e == hipSuccess) e = launch(static_cast<const float2*>(tab));
+  const hipError_t ef = hipFreeAsync(tab, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return BFLY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bfly_coeff_bytes(int32_t n) {
+  int l = 0;
+  if (check_n(n, 13, &l) != BFLY_OK) return 0;
+  return coeff_bytes_l(l);
+}
+
+bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coeff_bytes,
+                         void* hip_stream) {
+  if (!theta || !coeffs) return BFLY_ERR_NULL;
+  int l = 0;
+  const bfly_status st = check_n(n, 13, &l);
+  if (st != BFLY_OK) return st;
+  if (coeff_bytes < coeff_bytes_l(l)) return BFLY_ERR_WORKSPACE;
+  if (!aligned(coeffs, 16) || !aligned(theta, 4)) return BFLY_ERR_ALIGN;
+  const hipError_t e = bfly::launch_prepare(theta, static_cast<float2*>(coeffs),
+                                            (int64_t)l << (l - 1), (hipStream_t)hip_stream);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                  uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                                  int32_t m, int32_t nb, const float* theta, const void* coeffs,
+                                  const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
+                                  bool quant, void* hip_stream) {
+  if (rows > 0 && !x) return BFLY_ERR_NULL;
+  if (!theta && !coeffs) return BFLY_ERR_NULL;
+  if (rows > 0 && !y && !quant) return BFLY_ERR_NULL;
+  if (!dtype_ok(x_dt) || (y && !dtype_ok(y_dt))) return BFLY_ERR_DTYPE;
+  if (rows < 0) return BFLY_ERR_SIZE;
+  int lognb = 0;
+  bfly_status st = check_n(nb, 13, &lognb);
+  if (st != BFLY_OK) return st;
+  const int64_t n = (int64_t)m * nb;
+  if (n > 8192) return BFLY_ERR_UNSUPPORTED;
+  if (quant) {
+    st = check_quant(codes, scales, zeros, rows, n, nb, lognb, bits, group, mode);
+    if (st != BFLY_OK) return st;
+  }
+  if (!bfly::forward_supported(lognb, m)) return BFLY_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (y && !aligned(y, 16))) return BFLY_ERR_ALIGN;
+  if ((coeffs && !aligned(coeffs, 16)) || (theta && !aligned(theta, 4)) ||
+      (mix && !aligned(mix, 4)))
+    return BFLY_ERR_ALIGN;
+  if (rows == 0) return BFLY_OK;
+
+  bfly::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.y = y;
+  p.codes = quant ? codes : nullptr;
+  p.scales = quant ? scales : nullptr;
+  p.zeros = quant ? zeros : nullptr;
+  p.mix = mix;
+  p.rows = rows;
+  p.m = m;
+  p.lognb = lognb;
+  p.x_bf16 = x_dt == BFLY_BF16;
+  p.y_kind = !y ? bfly::Y_NONE : (y_dt == BFLY_BF16 ? bfly::Y_BF16 : bfly::Y_F32);
+  p.bits = quant ? bits : 0;
+  p.group = quant ? group : 0;
+  p.asym = quant && mode == BFLY_ASYM_MINMAX;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  return with_table(theta, coeffs, lognb, s, [&](const float2* cs) {
+    p.cs = cs;
+    return bfly::launch_forward(p, s);
+  });
+}
+
+bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt, int64_t rows,
+                         int32_t n, const float* theta, const void* coeffs, void* hip_stream) {
+  if (rows > 0 && !y) return BFLY_ERR_NULL;
+  return forward_common(x, x_dt, y, y_dt, nullptr, nullptr, nullptr, rows, 1, n, theta, coeffs,
+                        nullptr, 0, 0, BFLY_SYM_ABSMAX, false, hip_stream);
+}
+
+bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                               uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                               int32_t n, const float* theta, const void* coeffs, int32_t bits,
+                               int32_t group, bfly_qmode mode, void* hip_stream) {
+  return forward_common(x, x_dt, y, y_dt, codes, scales, zeros, rows, 1, n, theta, coeffs,
+                        nullptr, bits, group, mode, true, hip_stream);
+}
+
+bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                              uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                              int32_t m, int32_t nb, const float* theta_b, const void* coeffs_b,
+                              const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
+                              void* hip_stream) {
+  if (!mix) return BFLY_ERR_NULL;
+  if (m < 1 || m > 8) return BFLY_ERR_SIZE;
+  if (!codes && (scales || zeros)) return BFLY_ERR_QUANT;
+  if (log2_pow2(nb) >= 13) return BFLY_ERR_UNSUPPORTED;
+  return forward_common(x, x_dt, y, y_dt, codes, scales, zeros, rows, m, nb, theta_b, coeffs_b,
+                        mix, bits, group, mode, codes != nullptr, hip_stream);
+}
+
+size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n) {
+  int l = 0;
+  if (rows < 0 || check_n(n, 12, &l) != BFLY_OK) return 0;
+  const size_t slots = (size_t)bfly::backward_blocks(rows, l) * bwd_rows_per_block(l);
+  return align_up(coeff_bytes_l(l), 256) + slots * coeff_bytes_l(l) / 2;
+}
+
+bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, float* dtheta,
+                          int64_t rows, int32_t n, const float* theta, const void* coeffs,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if ((rows > 0 && (!x || !g || !dx)) || !dtheta || !workspace) return BFLY_ERR_NULL;
+  if (!theta && !coeffs) return BFLY_ERR_NULL;
+  if (rows < 0) return BFLY_ERR_SIZE;
+  int l = 0;
+  const bfly_status st = check_n(n, 12, &l);
+  if (st != BFLY_OK) return st;
+  if (workspace_bytes < bfly_backward_workspace_bytes(rows, n)) return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(dx, 16) || !aligned(y, 16) ||
+      !aligned(workspace, 16) || !aligned(dtheta, 4) || (coeffs && !aligned(coeffs, 16)) ||
+      (theta && !aligned(theta, 4)))
+    return BFLY_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  const float2* cs = static_cast<const float2*>(coeffs);
+  if (!cs) {
+    const hipError_t e = bfly::launch_prepare(theta, reinterpret_cast<float2*>(ws),
+                                              (int64_t)l << (l - 1), s);
+    if (e != hipSuccess) return hip_fail(e);
+    cs = reinterpret_cast<const float2*>(ws);
+  }
+  bfly::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.g = g;
+  p.y = y;
+  p.dx = dx;
+  p.partials = reinterpret_cast<float*>(ws + align_up(coeff_bytes_l(l), 256));
+  p.cs = cs;
+  p.rows = rows;
+  p.logn = l;
+  p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);
+  const hipError_t e = bfly::launch_backward(p, dtheta, s);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+const char* bfly_status_string(bfly_status s) {
+  switch (s) {
+    case BFLY_OK: return "ok";
+    case BFLY_ERR_NULL: return "a required pointer is NULL";
+    case BFLY_ERR_SIZE: return "invalid size (rows, n, m or nb)";
+    case BFLY_ERR_DTYPE: return "invalid dtype";
+    case BFLY_ERR_ALIGN: return "misaligned pointer";
+    case BFLY_ERR_QUANT: return "invalid quantization arguments";
+    case BFLY_ERR_WORKSPACE: return "workspace or coefficient buffer too small";
+    case BFLY_ERR_UNSUPPORTED: return "size not supported by this build";
+    case BFLY_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t bfly_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// Backward of the butterfly for learning the angles, fp32, plus the angle
+// preparation kernel.
+//
+// Pass 1, per row (team of T threads, E elements each, (cos, sin) resident
+// in VGPRs as in the forward):
+//   v <- x (load/store layout), forward phases -> v = Q x in the last
+//   phase's layout, y stored from there; g <- dL/dY loaded directly in that
+//   layout; then the stages in reverse: for each pair (lo, hi) of stage s
+//   with stage output v and output gradient g,
+//       acc[s][pair] += g_hi v_lo - g_lo v_hi,
+//   then v <- B_s^T v (undoing the stage) and g <- B_s^T g.  After stage 0,
+//   g = Q^T dL/dY = dL/dX in the load/store layout.  Each thread keeps one
+//   fp32 accumulator per pair it owns across all rows of its workgroup and
+//   writes them to the workgroup's slot of the partials buffer at the end.
+// Pass 2: dtheta[k] = sum over slots of partials[slot][k], slot order fixed,
+// accumulated in fp64 -- the result is bit-identical from run to run and
+// independent of the device (the slot count depends only on rows and n).
+#include "bfly_common.h"
+
+namespace bfly {
+
+template <int LOGN>
+struct BwdShape {
+  static constexpr int LOGE = 3;
+  static constexpr int E = 1 << LOGE;
+  static constexpr int N = 1 << LOGN;
+  static constexpr int T = N >> LOGE;
+  static constexpr int R = (256 / T) > 0 ? (256 / T) : 1;
+  static constexpr int NT = T * R;
+  static constexpr int L = LOGN;
+  static constexpr int NPH = (L + LOGE - 1) / LOGE;
+  // two buffers (double-buffered) of v and g for each of the R rows
+  static constexpr int W = lds_words(N);  // padded LDS words per row
+  static constexpr size_t LDS_BYTES = 2ull * 2 * R * W * sizeof(float);
+};
+
+__device__ __forceinline__ void givens_t(float& a, float& b, float c, float s) {
+  const float na = fmaf(c, a, s * b);
+  const float nb = fmaf(-s, a, c * b);
+  a = na;
+  b = nb;
+}
+
+__device__ __forceinline__ void givens_f(float& a, float& b, float c, float s) {
+  const float na = fmaf(c, a, -(s * b));
+  const float nb = fmaf(s, a, c * b);
+  a = na;
+  b = nb;
+}
+
+template <int LOGE>
+__device__ __forceinline__ void put(float* buf, const float (&v)[1 << LOGE], int t, int b) {
+  constexpr int E = 1 << LOGE;
+  if (b == 0) {
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c)
+      *reinterpret_cast<float4*>(buf + lds_addr(t * E + 4 * c)) =
+          make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) buf[lds_addr(lay<LOGE>(t, e, b))] = v[e];
+  }
+}
+
+template <int LOGE>
+__device__ __forceinline__ void get(const float* buf, float (&v)[1 << LOGE], int t, int b) {
+  constexpr int E = 1 << LOGE;
+  if (b == 0) {
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      const float4 q = *reinterpret_cast<const float4*>(buf + lds_addr(t * E + 4 * c));
+      v[4 * c] = q.x;
+      v[4 * c + 1] = q.y;
+      v[4 * c + 2] = q.z;
+      v[4 * c + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = buf[lds_addr(lay<LOGE>(t, e, b))];
+  }
+}
+
+template <int LOGN>
+__global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
+  using S = BwdShape<LOGN>;
+  constexpr int LOGE = S::LOGE, E = S::E, T = S::T, N = S::N, R = S::R, L = S::L;
+  constexpr int NPH = S::NPH, W = S::W;
+  constexpr int BL = phase_base(NPH - 1, L, LOGE);  // layout of the last phase
+  extern __shared__ float4 lds_raw[];
+  float* lds = reinterpret_cast<float*>(lds_raw);
+
+  const int tid = threadIdx.x;
+  const int team = tid / T;
+  const int t = tid - team * T;
+
+  float cc[L][E / 2], ss[L][E / 2], acc[L][E / 2];
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const int b = phase_base(s / LOGE, L, LOGE);
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int ilo = lay<LOGE>(t, pair_lo(j, s - b), b);
+      const float2 c = P.cs[s * (N / 2) + pair_rank(ilo, s)];
+      cc[s][j] = c.x;
+      ss[s][j] = c.y;
+      acc[s][j] = 0.f;
+    }
+  }
+
+  const int64_t rows = P.rows;
+  const int64_t ngrp = (rows + R - 1) / R;
+  // Input registers of the current row; refilled with the next row as soon
+  // as they have been copied out (zeros past the end, which contribute
+  // nothing to the angle gradients).
+  float4 xc[E / 4];
+  float gc[E];
+  auto load = [&](int64_t grp, float4 (&xd)[E / 4], float (&gd)[E]) {
+    const int64_t row = grp * R + team;
+    const bool ok = row < rows;
+    const float4* xs = reinterpret_cast<const float4*>(P.x + (ok ? row : 0) * N + (int64_t)t * E);
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) xd[c] = ok ? xs[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* gs = P.g + (ok ? row : 0) * N;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gd[e] = ok ? gs[lay<LOGE>(t, e, BL)] : 0.f;
+  };
+
+  int64_t grp = blockIdx.x;
+  if (grp < ngrp) load(grp, xc, gc);
+  int bufsel = 0;
+  for (; grp < ngrp; grp += gridDim.x) {
+    const int64_t gnext = grp + gridDim.x;
+    const int64_t row = grp * R + team;
+    const bool valid = row < rows;
+
+    float v[E], g[E];
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      v[4 * c] = xc[c].x;
+      v[4 * c + 1] = xc[c].y;
+      v[4 * c + 2] = xc[c].z;
+      v[4 * c + 3] = xc[c].w;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) g[e] = gc[e];
+    if (gnext < ngrp) load(gnext, xc, gc);
+
+    // forward
+#pragma unroll
+    for (int k = 0; k < NPH; ++k) {
+      const int b = phase_base(k, L, LOGE);
+      if (k > 0) {
+        float* buf = lds + (size_t)((bufsel * 2) * R + team) * W;
+        put<LOGE>(buf, v, t, phase_base(k - 1, L, LOGE));
+        __syncthreads();
+        get<LOGE>(buf, v, t, b);
+        bufsel ^= 1;
+      }
+      const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
+#pragma unroll
+      for (int s = k * LOGE; s < s_end; ++s) {
+        const int q = s - b;
+#pragma unroll
+        for (int j = 0; j < E / 2; ++j) {
+          const int lo = pair_lo(j, q), hi = lo | (1 << q);
+          givens_f(v[lo], v[hi], cc[s][j], ss[s][j]);
+        }
+      }
+    }
+    if (valid && P.y != nullptr) {
+      float* yr = P.y + row * N;
+#pragma unroll
+      for (int e = 0; e < E; ++e) yr[lay<LOGE>(t, e, BL)] = v[e];
+    }
+
+    // reverse sweep
+#pragma unroll
+    for (int k = NPH - 1; k >= 0; --k) {
+      const int b = phase_base(k, L, LOGE);
+      const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
+#pragma unroll
+      for (int s = s_end - 1; s >= k * LOGE; --s) {
+        const int q = s - b;
+#pragma unroll
+        for (int j = 0; j < E / 2; ++j) {
+          const int lo = pair_lo(j, q), hi = lo | (1 << q);
+          acc[s][j] = fmaf(g[hi], v[lo], acc[s][j]);
+          acc[s][j] = fmaf(-g[lo], v[hi], acc[s][j]);
+          givens_t(v[lo], v[hi], cc[s][j], ss[s][j]);
+          givens_t(g[lo], g[hi], cc[s][j], ss[s][j]);
+        }
+      }
+      if (k > 0) {
+        float* bv = lds + (size_t)((bufsel * 2) * R + team) * W;
+        float* bg = lds + (size_t)((bufsel * 2 + 1) * R + team) * W;
+        const int bp = phase_base(k - 1, L, LOGE);
+        put<LOGE>(bv, v, t, b);
+        put<LOGE>(bg, g, t, b);
+        __syncthreads();
+        get<LOGE>(bv, v, t, bp);
+        get<LOGE>(bg, g, t, bp);
+        bufsel ^= 1;
+      }
+    }
+    if (valid) {
+      float4* dst = reinterpret_cast<float4*>(P.dx + row * N + (int64_t)t * E);
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c)
+        dst[c] = make_float4(g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3]);
+    }
+  }
+
+  float* part = P.partials + ((int64_t)blockIdx.x * R + team) * (L * (N / 2));
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const int b = phase_base(s / LOGE, L, LOGE);
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int ilo = lay<LOGE>(t, pair_lo(j, s - b), b);
+      part[s * (N / 2) + pair_rank(ilo, s)] = acc[s][j];
+    }
+  }
+}
+
+__global__ void reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ dtheta,
+                                       int nslots, int count) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= count) return;
+  double sum = 0.0;
+  for (int sl = 0; sl < nslots; ++sl) sum += (double)partials[(int64_t)sl * count + k];
+  dtheta[k] = (float)sum;
+}
+
+__global__ void prepare_kernel(const float* __restrict__ theta, float2* __restrict__ cs, int64_t count) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= count) return;
+  double sn, cn;
+  sincos((double)theta[k], &sn, &cn);
+  cs[k] = make_float2((float)cn, (float)sn);
+}
+
+hipError_t launch_prepare(const float* theta, float2* cs, int64_t count, hipStream_t s) {
+  const int threads = 256;
+  const int64_t blocks = (count + threads - 1) / threads;
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, theta, cs, count);
+  return hipGetLastError();
+}
+
+int backward_blocks(int64_t rows, int logn) {
+  const int T = (1 << logn) >> 3;
+  const int R = (256 / T) > 0 ? (256 / T) : 1;
+  const int64_t ngrp = (rows + R - 1) / R;
+  const int64_t cap = 1024;
+  return (int)(ngrp < cap ? (ngrp > 0 ? ngrp : 1) : cap);
+}
+
+template <int LOGN>
+static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t s) {
+  using S = BwdShape<LOGN>;
+  static hipError_t lds_ok = allow_lds(reinterpret_cast<const void*>(bwd_kernel<LOGN>), S::LDS_BYTES);
+  if (lds_ok != hipSuccess) return lds_ok;
+  if (p.nblk > 0) {
+    hipLaunchKernelGGL(bwd_kernel<LOGN>, dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int count = S::L * (S::N / 2);
+  const int nslots = p.nblk * S::R;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((count + 255) / 256), dim3(256), 0, s,
+                     p.partials, dtheta, nslots, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s) {
+  switch (p.logn) {
+    case 6: return launch_bwd_inst<6>(p, dtheta, s);
+    case 7: return launch_bwd_inst<7>(p, dtheta, s);
+    case 8: return launch_bwd_inst<8>(p, dtheta, s);
+    case 9: return launch_bwd_inst<9>(p, dtheta, s);
+    case 10: return launch_bwd_inst<10>(p, dtheta, s);
+    case 11: return launch_bwd_inst<11>(p, dtheta, s);
+    case 12: return launch_bwd_inst<12>(p, dtheta, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bfly

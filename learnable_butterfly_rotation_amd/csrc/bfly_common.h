@@ -1,0 +1,72 @@
+// Device helpers shared by the forward and backward kernels: the register /
+// LDS layouts of a row, the LDS swizzle, bf16 packing.
+#pragma once
+
+#include "bfly_internal.h"
+
+namespace bfly {
+
+// A row of NB = 2^LOGNB elements is owned by a team of T = NB / E threads,
+// each holding E = 2^LOGE elements in registers.  In "phase" k the register
+// index e of thread t carries the E index bits starting at bit b_k:
+//     i = (t mod 2^b) | (e << b) | ((t >> b) << (b + LOGE)),
+// so the Givens stages whose pair bit lies in [b, b + LOGE) are done entirely
+// in registers.  Phase k performs stages [k LOGE, min((k+1) LOGE, L)) with
+// b_k = min(k LOGE, L - LOGE); between phases the row goes through LDS.
+// Layout b = 0 (E consecutive elements per thread) is the load/store layout.
+template <int LOGE>
+__device__ __forceinline__ int lay(int t, int e, int b) {
+  return (t & ((1 << b) - 1)) | (e << b) | ((t >> b) << (b + LOGE));
+}
+
+__host__ __device__ constexpr int phase_base(int k, int L, int LOGE) {
+  return (k * LOGE < L - LOGE) ? k * LOGE : L - LOGE;
+}
+
+// LDS word address of row element i: 4 pad words after every 32 and 16
+// more after every 256.  The padding is linear in the index bits, so in
+// every layout the address of register e is (thread part) + (constant for
+// e) and needs one base register plus immediate offsets.  Every transpose
+// access is conflict-free: layout b = 0 is accessed as aligned 16-byte
+// vectors (8 lanes cover 32 distinct banks), every other layout as 4-byte
+// words whose 32 consecutive lanes land in 32 distinct banks.
+__host__ __device__ constexpr int lds_addr(int i) { return i + 4 * (i >> 5) + 16 * (i >> 8); }
+
+// Words of LDS one padded segment of nb elements occupies.
+__host__ __device__ constexpr int lds_words(int nb) { return nb + 4 * (nb >> 5) + 16 * (nb >> 8); }
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Rank of the pair (i, i + 2^s) among the stage-s pairs ordered by i.
+__device__ __forceinline__ int pair_rank(int i, int s) {
+  return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
+}
+
+// Register index of the lower element of pair j (0 <= j < E/2) when the
+// pair bit is local bit q: insert a zero at bit q of j.
+__device__ __forceinline__ int pair_lo(int j, int q) {
+  return ((j >> q) << (q + 1)) | (j & ((1 << q) - 1));
+}
+
+// Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has
+// 160 KiB per CU); fails if the device cannot provide `bytes`.
+inline hipError_t allow_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  int dev = 0, maxb = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&maxb, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  if ((size_t)maxb < bytes) return hipErrorInvalidConfiguration;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace bfly

@@ -131,27 +131,45 @@ def kron_int4(rows: int = 8192, m: int = 5, nb: int = 1024, seed: int = 3):
 class CalibFP32:
     """Calibration forward+backward: 128 samples x 2048 tokens = 262144 rows of
     n=4096 fp32 (N(0,1) with 0.1% x50 outlier channels) and an upstream
-    gradient of the same shape ~ N(0,1).  Rows are produced in chunks so the
-    4 GiB tensors never have to sit in host memory at once; chunk k of X and
-    of G always holds the same rows whatever the chunk size, because each
-    tensor draws from its own sequential stream."""
+    gradient of the same shape ~ N(0,1).  Rows come in blocks of BLOCK rows;
+    block k of X and of G is drawn from its own child stream, so blocks can be
+    drawn in any order or in parallel and the 4 GiB tensors never have to sit
+    in host memory at once."""
+
+    BLOCK = 4096
 
     def __init__(self, rows: int = 128 * 2048, n: int = 4096, seed: int = 4):
         self.rows, self.n, self.seed = rows, n, seed
-        r_theta, _rx, r_cols, _rg = _streams(seed, 4)
-        self.theta = angles(r_theta, n)
-        self.outliers = outlier_columns(r_cols, n)
+        s_theta, s_x, s_cols, s_g = np.random.SeedSequence(seed).spawn(4)
+        self.theta = angles(np.random.Generator(np.random.PCG64(s_theta)), n)
+        self.outliers = outlier_columns(np.random.Generator(np.random.PCG64(s_cols)), n)
+        nblocks = (rows + self.BLOCK - 1) // self.BLOCK
+        self._xs = s_x.spawn(nblocks)
+        self._gs = s_g.spawn(nblocks)
+        self.nblocks = nblocks
         self.name = "calib_n4096_fp32_fwd_bwd"
 
-    def chunks(self, chunk_rows: int, limit_rows: int | None = None):
-        """Yield (row0, x_chunk, g_chunk) float32 arrays."""
-        _rt, r_x, _rc, r_g = _streams(self.seed, 4)
+    def block(self, k: int):
+        """(row0, x, g) float32 arrays of block k."""
+        r0 = k * self.BLOCK
+        m = min(self.BLOCK, self.rows - r0)
+        x = np.random.Generator(np.random.PCG64(self._xs[k])).standard_normal(size=(m, self.n))
+        x[:, self.outliers] *= 50.0
+        g = np.random.Generator(np.random.PCG64(self._gs[k])).standard_normal(size=(m, self.n))
+        return r0, x.astype(np.float32), g.astype(np.float32)
+
+    def blocks(self, limit_rows: int | None = None, threads: int = 8):
+        """Yield (row0, x, g) for the leading blocks, in order, drawing up to
+        `threads` blocks concurrently."""
+        from concurrent.futures import ThreadPoolExecutor
         total = self.rows if limit_rows is None else min(limit_rows, self.rows)
-        r0 = 0
-        while r0 < total:
-            k = min(chunk_rows, total - r0)
-            x = r_x.standard_normal(size=(k, self.n))
-            x[:, self.outliers] *= 50.0
-            g = r_g.standard_normal(size=(k, self.n))
-            yield r0, x.astype(np.float32), g.astype(np.float32)
-            r0 += k
+        nb = (total + self.BLOCK - 1) // self.BLOCK
+        with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+            futs = [ex.submit(self.block, k) for k in range(min(nb, threads))]
+            for k in range(nb):
+                r0, x, g = futs[k].result()
+                futs[k] = None
+                if k + threads < nb:
+                    futs.append(ex.submit(self.block, k + threads))
+                m = min(x.shape[0], total - r0)
+                yield r0, x[:m], g[:m]

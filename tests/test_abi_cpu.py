@@ -1,0 +1,157 @@
+"""The C-ABI library loads, exports every symbol include/bfly.h declares, and
+rejects bad arguments with the documented codes -- all before any HIP call,
+so these run on a machine without a GPU.  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import learnable_butterfly_rotation_amd as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bfly.h")
+
+OK, NULL, SIZE, DTYPE, ALIGN, QUANT, WORKSPACE, UNSUPPORTED, HIP = range(9)
+
+# fake, well-aligned device addresses: validation never dereferences them
+X, Y, C, S, Z, TH, MIX, WS, CO = (ctypes.c_void_p(a) for a in
+                                  (0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000,
+                                   0x70000, 0x80000, 0x90000))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bfly_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.library_path):
+        pytest.skip("libbfly.so not built")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_backward",
+            "bfly_prepare", "bfly_coeff_bytes", "bfly_backward_workspace_bytes",
+            "bfly_status_string", "bfly_last_hip_error"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert B.bfly_status_string(s)
+    assert B.bfly_status_string(99) == "unknown status"
+    assert B.bfly_last_hip_error() == 0
+
+
+def test_sizes(L):
+    assert B.bfly_coeff_bytes(4096) == 12 * 2048 * 8
+    assert B.bfly_coeff_bytes(256) == 8 * 128 * 8
+    assert B.bfly_coeff_bytes(100) == 0
+    assert B.bfly_coeff_bytes(32) == 0
+    ws = B.bfly_backward_workspace_bytes(262144, 4096)
+    assert ws >= 12 * 2048 * 8 + 12 * 2048 * 4  # table + at least one partial slot
+    assert B.bfly_backward_workspace_bytes(10, 4096) < ws
+    assert B.bfly_backward_workspace_bytes(-1, 4096) == 0
+    assert B.bfly_backward_workspace_bytes(100, 8192) == 0
+
+
+def fwd(L, x=X, xd=0, y=Y, yd=0, rows=4, n=256, th=TH, co=None):
+    return L.bfly_forward(x, xd, y, yd, rows, n, th, co, None)
+
+
+def test_forward_validation(L):
+    assert fwd(L, rows=0) == OK                       # valid, nothing to do
+    assert fwd(L, rows=0, x=None, y=None) == OK       # empty tensors carry NULL
+    assert fwd(L, x=None) == NULL
+    assert fwd(L, y=None) == NULL
+    assert fwd(L, th=None, co=None) == NULL
+    assert fwd(L, th=None, co=CO, rows=0) == OK
+    assert fwd(L, xd=2) == DTYPE
+    assert fwd(L, yd=-1) == DTYPE
+    assert fwd(L, rows=-1) == SIZE
+    assert fwd(L, n=100) == SIZE
+    assert fwd(L, n=0) == SIZE
+    assert fwd(L, n=32) == UNSUPPORTED
+    assert fwd(L, n=8192) == UNSUPPORTED
+    assert fwd(L, n=16384) == UNSUPPORTED
+    assert fwd(L, x=ctypes.c_void_p(0x10008)) == ALIGN
+    assert fwd(L, y=ctypes.c_void_p(0x20004)) == ALIGN
+    assert fwd(L, co=ctypes.c_void_p(0x90008), rows=0) == ALIGN
+
+
+def fq(L, y=Y, c=C, s=S, z=None, bits=4, group=128, mode=0, n=4096, rows=0):
+    return L.bfly_forward_quant(X, 1, y, 1, c, s, z, rows, n, TH, None, bits, group, mode, None)
+
+
+def test_forward_quant_validation(L):
+    assert fq(L) == OK
+    assert fq(L, y=None) == OK                        # codes only
+    assert fq(L, c=None, rows=1) == NULL
+    assert fq(L, c=None, s=None, y=None) == OK        # no rows: pointers unused
+    assert fq(L, s=None, rows=1) == NULL
+    assert fq(L, bits=3) == QUANT
+    assert fq(L, bits=8) == QUANT
+    assert fq(L, mode=2) == QUANT
+    assert fq(L, mode=1, rows=1) == QUANT             # asym needs zeros
+    assert fq(L, mode=1, z=Z) == OK
+    assert fq(L, mode=0, z=Z) == QUANT                # sym must not get zeros
+    assert fq(L, group=100) == QUANT
+    assert fq(L, group=4) == QUANT
+    assert fq(L, group=1024) == QUANT
+    assert fq(L, group=512, n=256) == QUANT           # group larger than the row
+    for g in (8, 16, 32, 64, 128, 256, 512):
+        assert fq(L, group=g) == OK
+    assert fq(L, c=ctypes.c_void_p(0x30004)) == ALIGN
+    assert fq(L, s=ctypes.c_void_p(0x40001)) == ALIGN
+
+
+def kf(L, m=5, nb=1024, c=C, s=S, z=None, mix=MIX, group=128, rows=0):
+    return L.bfly_kron_forward(X, 1, Y, 1, c, s, z, rows, m, nb, TH, None, mix, 4, group, 0, None)
+
+
+def test_kron_validation(L):
+    assert kf(L) == OK
+    assert kf(L, c=None, s=None) == OK                # no quantization
+    assert kf(L, c=None) == QUANT                     # scales without codes
+    assert kf(L, mix=None) == NULL
+    assert kf(L, m=0) == SIZE
+    assert kf(L, m=9) == SIZE
+    assert kf(L, nb=1000) == SIZE
+    assert kf(L, m=3, nb=4096) == UNSUPPORTED         # 12288 > 8192
+    assert kf(L, nb=8192, m=1) == UNSUPPORTED
+    assert kf(L, m=1, nb=4096) == OK
+    assert kf(L, m=5, nb=256, group=512) == QUANT     # group must divide nb
+    for m in range(2, 9):
+        assert kf(L, m=m, nb=512) == OK
+
+
+def bw(L, x=X, g=X, y=None, dx=Y, dth=C, rows=16, n=4096, th=TH, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = B.bfly_backward_workspace_bytes(max(rows, 0), n)
+    return L.bfly_backward(x, g, y, dx, dth, rows, n, th, None, ws, wsb, None)
+
+
+def test_backward_validation(L):
+    assert bw(L, x=None) == NULL
+    assert bw(L, dth=None) == NULL
+    assert bw(L, ws=None) == NULL
+    assert bw(L, th=None) == NULL
+    assert bw(L, rows=-1, wsb=1 << 30) == SIZE
+    assert bw(L, n=100, wsb=1 << 30) == SIZE
+    assert bw(L, n=8192, wsb=1 << 30) == UNSUPPORTED
+    assert bw(L, wsb=B.bfly_backward_workspace_bytes(16, 4096) - 1) == WORKSPACE
+    assert bw(L, dx=ctypes.c_void_p(0x20008)) == ALIGN
+
+
+def test_prepare_validation(L):
+    assert L.bfly_prepare(None, 256, CO, 1 << 20, None) == NULL
+    assert L.bfly_prepare(TH, 256, None, 1 << 20, None) == NULL
+    assert L.bfly_prepare(TH, 255, CO, 1 << 20, None) == SIZE
+    assert L.bfly_prepare(TH, 256, CO, 100, None) == WORKSPACE
+    assert L.bfly_prepare(TH, 256, ctypes.c_void_p(0x90008), 1 << 20, None) == ALIGN

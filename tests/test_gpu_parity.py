@@ -1,0 +1,402 @@
+"""GPU parity: libbfly's HIP kernels against the fp64 oracle, element by
+element, on seeded inputs -- small shapes spanning several tiles with ragged
+tails, every edge case, and the five workloads at full size in the launch
+configuration the benchmark times.  Every call goes through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import learnable_butterfly_rotation_amd as B
+from learnable_butterfly_rotation_amd import inputs
+
+from parity import check_bf16, check_dtheta, check_f32, check_quant
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()  # fail loudly if the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a: np.ndarray):
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+def row_norms(x: np.ndarray):
+    xf = inputs.bf16_bits_to_f32(x).reshape(x.shape) if x.dtype == np.uint16 else x
+    xf = xf.astype(np.float64)
+    return np.abs(xf).max(axis=1), np.linalg.norm(xf, axis=1)
+
+
+def rand_theta(rng, n):
+    return inputs.angles(rng, n)
+
+
+def run_quant(x, theta, bits, group, mode, y_dtype=torch.bfloat16, with_y=True, coeffs=False):
+    rows, n = x.shape
+    xd = dev(x)
+    y = empty((rows, n), y_dtype) if with_y else None
+    codes = torch.zeros((rows, n * bits // 8), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((rows, n // group), dtype=torch.float16, device="cuda")
+    zeros = torch.zeros((rows, n // group), dtype=torch.float16, device="cuda") if mode else None
+    th = dev(theta)
+    if coeffs:
+        tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+        B.bfly_prepare(th, n, tab)
+        B.bfly_forward_quant(xd, y, codes, scales, zeros, coeffs=tab, bits=bits, group=group,
+                             mode=mode)
+    else:
+        B.bfly_forward_quant(xd, y, codes, scales, zeros, theta=th, bits=bits, group=group,
+                             mode=mode)
+    out = {"codes": host(codes), "scales": host(scales)}
+    if zeros is not None:
+        out["zeros"] = host(zeros)
+    if y is not None:
+        out["y"] = host(y)
+    return out
+
+
+def assert_forward(y_gpu, y64, x, n):
+    xinf, xl2 = row_norms(x)
+    if y_gpu.dtype == np.uint16:
+        r = check_bf16(y_gpu, y64, xl2, n)
+    else:
+        r = check_f32(y_gpu, y64, xinf, n)
+    assert r["ok"], r
+    return r
+
+
+def assert_quant(out, y64, bits, group, mode):
+    r = check_quant(y64, out["codes"], out["scales"], out.get("zeros"), bits, group, mode)
+    assert r["ok"], r
+    return r
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_workload_full():
+    w = inputs.tiny_fp32()
+    x, th = w["x"], w["theta"]
+    y = empty(x.shape, torch.float32)
+    B.bfly_forward(dev(x), y, theta=dev(th))
+    y_gpu = host(y)
+    r = assert_forward(y_gpu, oracle.forward(x, th), x, 256)
+    print("tiny n=256 fp32:", r)
+    # a prepared table gives bit-identical results
+    tab = torch.empty(B.bfly_coeff_bytes(256), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare(dev(th), 256, tab)
+    y2 = empty(x.shape, torch.float32)
+    B.bfly_forward(dev(x), y2, coeffs=tab)
+    assert np.array_equal(host(y2), y_gpu)
+
+
+@pytest.mark.parametrize("n", [64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("x_dt,y_dt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
+                                       ("f32", "bf16")])
+def test_forward_sizes_and_dtypes(n, x_dt, y_dt):
+    rng = np.random.default_rng(1000 + n)
+    th = rand_theta(rng, n)
+    for rows in (1, 37, 301):
+        xf = (rng.standard_normal((rows, n)) * 3).astype(np.float32)
+        x = inputs.f32_to_bf16_bits(xf) if x_dt == "bf16" else xf
+        y = empty((rows, n), torch.bfloat16 if y_dt == "bf16" else torch.float32)
+        B.bfly_forward(dev(x), y, theta=dev(th))
+        assert_forward(host(y), oracle.forward(x, th), x, n)
+
+
+@pytest.mark.parametrize("n", [64, 256, 1024, 4096])
+@pytest.mark.parametrize("bits,mode", [(4, 0), (2, 1), (4, 1), (2, 0)])
+def test_forward_quant_modes(n, bits, mode):
+    rng = np.random.default_rng(7 * n + bits + 10 * mode)
+    th = rand_theta(rng, n)
+    for group in sorted(g for g in {8, 32, 128, 512, n} if g <= min(n, 512)):
+        rows = 67
+        xf = (rng.standard_normal((rows, n)) * np.exp(rng.uniform(-4, 4, (rows, 1)))).astype(np.float32)
+        x = inputs.f32_to_bf16_bits(xf)
+        out = run_quant(x, th, bits, group, mode)
+        y64 = oracle.forward(x, th)
+        assert_forward(out["y"], y64, x, n)
+        assert_quant(out, y64, bits, group, mode)
+
+
+def test_act_int4_workload_full():
+    """n=4096, 8192 bf16 rows with outlier channels, sym INT4 g128: all rows."""
+    w = inputs.act_int4()
+    x, th = w["x"], w["theta"]
+    out = run_quant(x, th, 4, 128, 0)
+    y64 = oracle.forward(x, th)
+    rf = assert_forward(out["y"], y64, x, 4096)
+    rq = assert_quant(out, y64, 4, 128, 0)
+    print("act n=4096 bf16 int4:", rf, rq)
+    # deterministic, independent of the prepared/unprepared path and of the
+    # batch a row is computed in
+    again = run_quant(x, th, 4, 128, 0, coeffs=True)
+    for k in out:
+        assert np.array_equal(out[k], again[k]), k
+    part = run_quant(x[:37], th, 4, 128, 0)
+    for k in out:
+        assert np.array_equal(out[k][:37], part[k]), k
+
+
+def test_weight_int2_workload_full():
+    """W Q^T for 4096x4096 and 11008x4096 bf16 weights, asym INT2 g128."""
+    w = inputs.weight_int2()
+    for name in ("w1", "w2"):
+        x = w[name]
+        out = run_quant(x, w["theta"], 2, 128, 1)
+        y64 = oracle.forward(x, w["theta"])
+        rf = assert_forward(out["y"], y64, x, 4096)
+        rq = assert_quant(out, y64, 2, 128, 1)
+        print("weight", name, rf, rq)
+        codes_only = run_quant(x, w["theta"], 2, 128, 1, with_y=False)
+        for k in ("codes", "scales", "zeros"):
+            assert np.array_equal(out[k], codes_only[k]), k
+
+
+def test_computational_invariance_on_gpu():
+    """(W Q^T)(Q x) = W x with both rotations computed by the library (fp32)."""
+    rng = np.random.default_rng(5)
+    n = 1024
+    th = rand_theta(rng, n)
+    w = rng.standard_normal((96, n)).astype(np.float32)
+    x = rng.standard_normal((33, n)).astype(np.float32)
+    wq = empty(w.shape, torch.float32)
+    qx = empty(x.shape, torch.float32)
+    B.bfly_forward(dev(w), wq, theta=dev(th))
+    B.bfly_forward(dev(x), qx, theta=dev(th))
+    lhs = host(qx).astype(np.float64) @ host(wq).astype(np.float64).T
+    rhs = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(lhs - rhs).max() <= 1e-5 * math.log2(n) * np.abs(rhs).max()
+
+
+# ---------------------------------------------------------------------------
+# Kronecker composite
+# ---------------------------------------------------------------------------
+
+def run_kron(x, th, mix, quant=True, bits=4, group=128, mode=0):
+    rows, n = x.shape
+    y = empty((rows, n), torch.bfloat16)
+    args = {}
+    if quant:
+        args = dict(codes=torch.zeros((rows, n * bits // 8), dtype=torch.uint8, device="cuda"),
+                    scales=torch.zeros((rows, n // group), dtype=torch.float16, device="cuda"),
+                    zeros=torch.zeros((rows, n // group), dtype=torch.float16, device="cuda")
+                    if mode else None)
+    B.bfly_kron_forward(dev(x), y, dev(mix), theta_b=dev(th), bits=bits, group=group, mode=mode,
+                        **args)
+    out = {"y": host(y)}
+    if quant:
+        out["codes"] = host(args["codes"])
+        out["scales"] = host(args["scales"])
+        if mode:
+            out["zeros"] = host(args["zeros"])
+    return out
+
+
+def test_kron_workload_full():
+    """n=5120 = O5 (x) B1024, 8192 bf16 rows with outliers, sym INT4 g128."""
+    w = inputs.kron_int4()
+    x = w["x"]
+    out = run_kron(x, w["theta_b"], w["mix"])
+    y64 = oracle.kron_forward(x, w["theta_b"], w["mix"])
+    rf = assert_forward(out["y"], y64, x, 5120)
+    rq = assert_quant(out, y64, 4, 128, 0)
+    print("kron n=5120:", rf, rq)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("nb", [256, 1024])
+def test_kron_shapes(m, nb):
+    rng = np.random.default_rng(100 * m + nb)
+    th = rand_theta(rng, nb)
+    mix = inputs.mixing_factor(rng, m)
+    rows = 45
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((rows, m * nb)).astype(np.float32))
+    for quant, mode in ((False, 0), (True, 0), (True, 1)):
+        out = run_kron(x, th, mix, quant=quant, bits=4, group=64, mode=mode)
+        y64 = oracle.kron_forward(x, th, mix)
+        assert_forward(out["y"], y64, x, m * nb)
+        if quant:
+            assert_quant(out, y64, 4, 64, mode)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def test_rows_zero_is_noop():
+    y = torch.full((4, 256), 7.0, device="cuda")
+    x = torch.zeros((0, 256), device="cuda")
+    B.bfly_forward(x, y[:0], theta=dev(np.zeros((8, 128), np.float32)))
+    assert (host(y) == 7.0).all()
+
+
+def test_in_place():
+    rng = np.random.default_rng(3)
+    th = rand_theta(rng, 1024)
+    x = rng.standard_normal((50, 1024)).astype(np.float32)
+    xd = dev(x)
+    B.bfly_forward(xd, xd, theta=dev(th))
+    assert_forward(host(xd), oracle.forward(x, th), x, 1024)
+
+
+def test_zero_angles_identity_bit_exact():
+    rng = np.random.default_rng(4)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((20, 512)).astype(np.float32))
+    y = empty((20, 512), torch.bfloat16)
+    B.bfly_forward(dev(x), y, theta=dev(np.zeros((9, 256), np.float32)))
+    assert np.array_equal(host(y), x)
+
+
+def test_quarter_pi_is_hadamard():
+    n = 256
+    th = np.full((8, 128), math.pi / 4, dtype=np.float32)
+    h = np.array([[1.0]])
+    for _ in range(8):
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    h /= math.sqrt(n)
+    d = np.array([(-1.0) ** bin(i).count("1") for i in range(n)])
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((16, n)).astype(np.float32)
+    y = empty(x.shape, torch.float32)
+    B.bfly_forward(dev(x), y, theta=dev(th))
+    want = (x.astype(np.float64) * d) @ h.T
+    assert np.abs(host(y) - want).max() < 1e-5
+
+
+def test_degenerate_groups():
+    """All-zero rows (scale 0 -> codes 0), constant rows in asym mode, and
+    values so large that the fp16 scale saturates."""
+    n = 256
+    th = np.zeros((8, 128), np.float32)  # identity: groups keep their shape
+    x = np.zeros((3, n), np.float32)
+    x[1] = 3.0
+    x[2, ::2] = 1e9
+    x[2, 1::2] = -1e9
+    for bits, mode in ((4, 0), (2, 1)):
+        out = run_quant(x, th, bits, 32, mode, y_dtype=torch.float32)
+        y64 = oracle.forward(x, th)
+        assert_quant(out, y64, bits, 32, mode)
+        assert not out["codes"][0].any() and not out["scales"][0].any()
+        assert (out["scales"][2] == 0x7BFF).all()
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def run_backward(x, g, th, with_y=True, coeffs=False):
+    rows, n = x.shape
+    ws = torch.empty(B.bfly_backward_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+    y = empty((rows, n), torch.float32) if with_y else None
+    dx = empty((rows, n), torch.float32)
+    dth = torch.full(th.shape, float("nan"), device="cuda")
+    if coeffs:
+        tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+        B.bfly_prepare(dev(th), n, tab)
+        B.bfly_backward(dev(x), dev(g), y, dx, dth, ws, coeffs=tab)
+    else:
+        B.bfly_backward(dev(x), dev(g), y, dx, dth, ws, theta=dev(th))
+    return {"y": host(y) if with_y else None, "dx": host(dx), "dtheta": host(dth)}
+
+
+@pytest.mark.parametrize("n", [64, 256, 1024, 4096])
+def test_backward_small(n):
+    rng = np.random.default_rng(50 + n)
+    th = rand_theta(rng, n)
+    for rows in (1, 29, 515):
+        x = (rng.standard_normal((rows, n)) * 2).astype(np.float32)
+        g = rng.standard_normal((rows, n)).astype(np.float32)
+        out = run_backward(x, g, th)
+        ref = oracle.backward(x, g, th)
+        assert check_f32(out["y"], ref["y"], np.abs(x).max(1), n)["ok"]
+        assert check_f32(out["dx"], ref["dx"], np.abs(g).max(1), n)["ok"]
+        r = check_dtheta(out["dtheta"], ref["dtheta"], ref["dabs"], n)
+        assert r["ok"], r
+    again = run_backward(x, g, th, with_y=False, coeffs=True)
+    assert np.array_equal(again["dtheta"], out["dtheta"])
+    assert np.array_equal(again["dx"], out["dx"])
+
+
+def test_backward_rows_zero_zeroes_dtheta():
+    n = 256
+    out = run_backward(np.zeros((0, n), np.float32), np.zeros((0, n), np.float32),
+                       np.ones((8, 128), np.float32))
+    assert (out["dtheta"] == 0).all()
+
+
+def test_backward_invariant_g_equals_y():
+    """G = Y: the loss does not depend on theta, so dtheta ~ 0 relative to the
+    term magnitudes, and dX = X."""
+    rng = np.random.default_rng(11)
+    n = 1024
+    th = rand_theta(rng, n)
+    x = rng.standard_normal((200, n)).astype(np.float32)
+    g = oracle.forward(x, th).astype(np.float32)
+    out = run_backward(x, g, th)
+    ref = oracle.backward(x, g, th)
+    assert np.abs(out["dtheta"]).max() <= 1e-5 * math.log2(n) * ref["dabs"].max()
+    assert np.abs(out["dx"] - x).max() <= 1e-5 * math.log2(n) * np.abs(x).max()
+
+
+@pytest.mark.timeout(900)
+def test_calibration_workload_full():
+    """262144 x 4096 fp32 forward + backward; dtheta over all rows against the
+    oracle (streamed by blocks), Y and dX on sampled blocks."""
+    c = inputs.CalibFP32()
+    n = c.n
+    X = torch.empty((c.rows, n), dtype=torch.float32, device="cuda")
+    G = torch.empty((c.rows, n), dtype=torch.float32, device="cuda")
+    d64 = np.zeros(c.theta.shape)
+    dabs = np.zeros(c.theta.shape)
+    sampled = {0, c.nblocks // 2, c.nblocks - 1}
+    keep = {}
+    for r0, x, g in c.blocks(threads=8):
+        X[r0:r0 + x.shape[0]].copy_(torch.from_numpy(x))
+        G[r0:r0 + x.shape[0]].copy_(torch.from_numpy(g))
+        k = r0 // c.BLOCK
+        want = k in sampled
+        ref = oracle.backward(x, g, c.theta, want_y=want, want_dx=want)
+        d64 += ref["dtheta"]
+        dabs += ref["dabs"]
+        if want:
+            keep[k] = (r0, x, g, ref["y"], ref["dx"])
+    ws = torch.empty(B.bfly_backward_workspace_bytes(c.rows, n), dtype=torch.uint8, device="cuda")
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    dth = torch.empty(c.theta.shape, dtype=torch.float32, device="cuda")
+    B.bfly_backward(X, G, Y, dX, dth, ws, theta=dev(c.theta))
+    r = check_dtheta(host(dth), d64, dabs, n)
+    print("calib dtheta:", r)
+    assert r["ok"], r
+    for k, (r0, x, g, y64, dx64) in keep.items():
+        m = x.shape[0]
+        assert check_f32(host(Y[r0:r0 + m]), y64, np.abs(x).max(1), n)["ok"]
+        assert check_f32(host(dX[r0:r0 + m]), dx64, np.abs(g).max(1), n)["ok"]

@@ -415,10 +415,13 @@ def test_generators_are_prefix_stable_and_seeded():
     assert np.array_equal(a["theta"], b["theta"])
     assert a["theta"].shape == (12, 2048) and a["theta"].dtype == np.float32
     assert len(a["outliers"]) == 4
-    c = inputs.CalibFP32()
-    x1 = np.concatenate([xc for _, xc, _ in c.chunks(7, limit_rows=20)])
-    x2 = np.concatenate([xc for _, xc, _ in c.chunks(20, limit_rows=20)])
-    assert np.array_equal(x1, x2)
+    c = inputs.CalibFP32(rows=3 * inputs.CalibFP32.BLOCK + 5)
+    blocks = list(c.blocks(threads=2))
+    assert [b[0] for b in blocks] == [0, 4096, 8192, 12288]
+    assert blocks[-1][1].shape == (5, 4096)
+    r0, x1, g1 = c.block(2)
+    assert np.array_equal(x1, blocks[2][1]) and np.array_equal(g1, blocks[2][2])
+    assert np.abs(x1[:, c.outliers]).mean() > 20 * np.abs(g1).mean()
     k = inputs.kron_int4(rows=4)
     assert np.abs(k["mix"].astype(np.float64) @ k["mix"].T - np.eye(5)).max() < 1e-6
     assert k["theta_b"].shape == (10, 512)
