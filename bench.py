@@ -1,0 +1,307 @@
+"""Benchmark: fused butterfly rotation + INT4 quantization on one MI355X.
+
+Workload (the headline one): n = 4096, 8192 bf16 token rows with 0.1 % x50
+outlier channels (LLaMA-2-7B hidden width), 12 Givens stages with 24576
+angles, bf16 Q x out, symmetric absmax INT4 codes per group of 128 with fp16
+scales.  One step = bfly_prepare (angles -> coefficient table) +
+bfly_forward_quant over all 8192 rows.  Inputs are resident in HBM before the
+timed region; the step cycles through 5 separate input/output buffer sets
+(722 MiB) so that no step finds its rows in the 256 MB last-level cache.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+
+Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step:
+18 496 B per row (8192 in + 8192 out + 2048 codes + 64 scale bytes) plus the
+96 KiB of angles, divided by the mean step time.  `roofline` prices the
+fused kernel alone (HIP events around it, on its stream) against the
+8 TB/s HBM peak; `traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters recorded for the current kernel sources (null if they changed).
+`cpu_baseline` times the fp64 oracle on the machine's host cores.
+
+--workload picks one of the other parity workloads for a secondary line
+(tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
+calib_n4096_fp32_fwd_bwd); --copy-probe runs a plain device copy of known
+size (for calibrating the byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "butterfly+quant GB/s (% of HBM roofline), n=4096, 8192 rows bf16"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bfly_fwd_quant_n4096_bf16_int4_traffic.txt")
+NSETS = 5
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "learnable_butterfly_rotation_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None if it is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256_16") != kernel_sources_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_act(w, bytes_per_row, passes=3):
+    import oracle
+    x, th = w["x"], w["theta"]
+    times = []
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        y64 = oracle.forward(x, th)
+        oracle.round_bf16(y64)
+        oracle.quantize(y64, 4, 128, oracle.SYM)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    rows = x.shape[0]
+    return {"value": rows * bytes_per_row / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "all %d rows of the workload (fp64 forward, bf16 rounding, INT4 quantization),"
+                      " median of %d passes: %.3f s per pass, %.0f rows/s" % (rows, passes, t, rows / t)}
+
+
+# ---------------------------------------------------------------------------
+# the headline workload
+# ---------------------------------------------------------------------------
+
+def bench_act(args, torch, B, inputs):
+    w = inputs.act_int4()
+    x, th = w["x"], w["theta"]
+    rows, n = x.shape
+    group, bits = 128, 4
+    bytes_per_row = 2 * n + 2 * n + n * bits // 8 + 2 * (n // group)     # 18 496
+    step_bytes = rows * bytes_per_row + th.nbytes
+    kernel_bytes = rows * bytes_per_row
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    theta = to_dev(th, torch)
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    sets = []
+    xd = to_dev(x, torch)
+    for k in range(NSETS):
+        sets.append({
+            "x": xd if k == 0 else xd.clone(),
+            "y": torch.empty((rows, n), dtype=torch.bfloat16, device="cuda"),
+            "codes": torch.empty((rows, n * bits // 8), dtype=torch.uint8, device="cuda"),
+            "scales": torch.empty((rows, n // group), dtype=torch.float16, device="cuda"),
+        })
+    lib = B.lib()
+    ptrs = [(s["x"].data_ptr(), s["y"].data_ptr(), s["codes"].data_ptr(), s["scales"].data_ptr())
+            for s in sets]
+    th_p, tab_p, tab_n = theta.data_ptr(), tab.data_ptr(), tab.numel()
+
+    def step(i, ev=None):
+        px, py, pc, ps = ptrs[i % NSETS]
+        st = lib.bfly_prepare(th_p, n, tab_p, tab_n, sh)
+        if ev is not None:
+            ev[0].record(stream)
+        st |= lib.bfly_forward_quant(px, B.BFLY_BF16, py, B.BFLY_BF16, pc, ps, None, rows, n,
+                                     None, tab_p, bits, group, B.BFLY_SYM_ABSMAX, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        if st:
+            raise RuntimeError("libbfly call failed with status %d" % st)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    achieved = kernel_bytes / kern_avg_s / 1e9
+    traffic = recorded_traffic()
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"] + ": 8192 rows x n=4096, bf16 in, bf16 Q x out, "
+                               "symmetric absmax INT4 codes per group of 128, fp16 scales",
+                   "rows": rows, "n": n, "bits": bits, "group": group,
+                   "bytes_per_step": step_bytes, "rows_per_s": round(rows / (ms_step / 1e3)),
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "buffer_sets": NSETS},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "fwd_kernel<12,1,bf16> (bfly_forward_quant)",
+                     "kernel_avg_us": round(kern_avg_s * 1e6, 3),
+                     "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                     "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
+                     "algorithmic_bytes_per_launch": kernel_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_act(w, bytes_per_row)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# secondary workloads (reported on one line each, not the headline)
+# ---------------------------------------------------------------------------
+
+def time_loop(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_secondary(args, torch, B, inputs):
+    name = args.workload
+    res = {"workload": name}
+    if name == "tiny_n256_fp32":
+        w = inputs.tiny_fp32()
+        x, y, th = to_dev(w["x"], torch), torch.empty((64, 256), device="cuda"), to_dev(w["theta"], torch)
+        t = time_loop(torch, lambda i: B.bfly_forward(x, y, theta=th), args.steps, args.warmup)
+        res.update(us_per_step=t * 1e6, bytes=64 * 256 * 8)
+    elif name == "weight_n4096_bf16_int2":
+        w = inputs.weight_int2()
+        th = to_dev(w["theta"], torch)
+        tab = torch.empty(B.bfly_coeff_bytes(4096), dtype=torch.uint8, device="cuda")
+        mats = []
+        for k in ("w1", "w2"):
+            xw = to_dev(w[k], torch)
+            r = xw.shape[0]
+            mats.append((xw, torch.empty_like(xw), torch.empty((r, 1024), dtype=torch.uint8, device="cuda"),
+                         torch.empty((r, 32), dtype=torch.float16, device="cuda"),
+                         torch.empty((r, 32), dtype=torch.float16, device="cuda")))
+
+        def fn(i):
+            B.bfly_prepare(th, 4096, tab)
+            for xw, yw, c, s, z in mats:
+                B.bfly_forward_quant(xw, yw, c, s, z, coeffs=tab, bits=2, group=128, mode=1)
+        t = time_loop(torch, fn, args.steps, args.warmup)
+        rows = 4096 + 11008
+        b = rows * (8192 + 8192 + 1024 + 128)
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t)
+    elif name == "kron_n5120_bf16_int4":
+        w = inputs.kron_int4()
+        x, th, mix = to_dev(w["x"], torch), to_dev(w["theta_b"], torch), to_dev(w["mix"], torch)
+        rows = x.shape[0]
+        y = torch.empty_like(x)
+        c = torch.empty((rows, 2560), dtype=torch.uint8, device="cuda")
+        s = torch.empty((rows, 40), dtype=torch.float16, device="cuda")
+        tab = torch.empty(B.bfly_coeff_bytes(1024), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            B.bfly_prepare(th, 1024, tab)
+            B.bfly_kron_forward(x, y, mix, c, s, coeffs_b=tab, bits=4, group=128)
+        t = time_loop(torch, fn, args.steps, args.warmup)
+        b = rows * (10240 + 10240 + 2560 + 80)
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t)
+    elif name == "calib_n4096_fp32_fwd_bwd":
+        c = inputs.CalibFP32()
+        X = torch.empty((c.rows, c.n), device="cuda")
+        G = torch.empty((c.rows, c.n), device="cuda")
+        for r0, xb, gb in c.blocks(threads=16):
+            X[r0:r0 + xb.shape[0]].copy_(torch.from_numpy(xb))
+            G[r0:r0 + gb.shape[0]].copy_(torch.from_numpy(gb))
+        Y, dX = torch.empty_like(X), torch.empty_like(X)
+        dth = torch.empty((12, 2048), device="cuda")
+        th = to_dev(c.theta, torch)
+        ws = torch.empty(B.bfly_backward_workspace_bytes(c.rows, c.n), dtype=torch.uint8, device="cuda")
+        t = time_loop(torch, lambda i: B.bfly_backward(X, G, Y, dX, dth, ws, theta=th),
+                      args.steps, args.warmup)
+        b = c.rows * c.n * 16
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=c.rows / t)
+    else:
+        raise SystemExit("unknown workload %s" % name)
+    if "GBs" in res:
+        res["pct_of_hbm_peak"] = 100 * res["GBs"] / HBM_PEAK_GBS
+    return res
+
+
+def copy_probe(torch, steps):
+    """A plain device-to-device copy of 256 MiB, for calibrating counters."""
+    a = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copy_probe_bytes_written": a.numel() * 4,
+                      "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="act_n4096_bf16_int4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the rotation is row-parallel and this build "
+              "runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import learnable_butterfly_rotation_amd as B
+    from learnable_butterfly_rotation_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    if args.copy_probe:
+        copy_probe(torch, args.steps)
+        return
+    if args.workload == "act_n4096_bf16_int4":
+        print(json.dumps(bench_act(args, torch, B, inputs)))
+    else:
+        print(json.dumps(bench_secondary(args, torch, B, inputs)))
+
+
+if __name__ == "__main__":
+    main()

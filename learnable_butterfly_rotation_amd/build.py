@@ -17,13 +17,17 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbfly.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["bfly_api.hip", "bfly_bwd.hip", "bfly_fwd_plain.hip", "bfly_fwd_kron_a.hip",
-           "bfly_fwd_kron_b.hip"]
+# (source, object, extra flags): the Kronecker unit is compiled once per m
+SOURCES = [("bfly_api.hip", "bfly_api.o", []), ("bfly_bwd.hip", "bfly_bwd.o", []),
+           ("bfly_fwd_plain.hip", "bfly_fwd_plain.o", [])] + \
+          [("bfly_fwd_kron.hip", "bfly_fwd_kron_m%d.o" % m, ["-DKRON_M=%d" % m]) for m in range(2, 9)]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # no packed fp32 (v_pk_*_f32) code generation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # NaN inputs give unspecified results; min/max then need no NaN quieting
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 
@@ -32,9 +36,9 @@ def build(verbose: bool = False, extra=None) -> str:
     os.makedirs(OBJ, exist_ok=True)
     t0 = time.time()
     procs = []
-    for src in SOURCES:
-        obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+    for src, objname, defs in SOURCES:
+        obj = os.path.join(OBJ, objname)
+        cmd = [HIPCC, *FLAGS, *defs, *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.STDOUT, text=True)))
     objs, failed = [], []

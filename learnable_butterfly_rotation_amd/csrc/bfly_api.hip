@@ -10,8 +10,13 @@
 
 namespace bfly {
 hipError_t launch_forward_plain(const FwdParams& p, hipStream_t s);
-hipError_t launch_forward_kron_a(const FwdParams& p, hipStream_t s);
-hipError_t launch_forward_kron_b(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m2(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m3(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m4(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m5(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m6(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m7(const FwdParams& p, hipStream_t s);
+hipError_t launch_forward_kron_m8(const FwdParams& p, hipStream_t s);
 
 bool forward_supported(int lognb, int m) {
   if (m == 1) return lognb >= 6 && lognb <= 12;
@@ -20,9 +25,17 @@ bool forward_supported(int lognb, int m) {
 }
 
 hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
-  if (p.m == 1) return launch_forward_plain(p, s);
-  if (p.m <= 4) return launch_forward_kron_a(p, s);
-  return launch_forward_kron_b(p, s);
+  switch (p.m) {
+    case 1: return launch_forward_plain(p, s);
+    case 2: return launch_forward_kron_m2(p, s);
+    case 3: return launch_forward_kron_m3(p, s);
+    case 4: return launch_forward_kron_m4(p, s);
+    case 5: return launch_forward_kron_m5(p, s);
+    case 6: return launch_forward_kron_m6(p, s);
+    case 7: return launch_forward_kron_m7(p, s);
+    case 8: return launch_forward_kron_m8(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 }  // namespace bfly
 
@@ -56,7 +69,7 @@ bfly_status check_n(int64_t n, int max_log, int* logn) {
 
 bool dtype_ok(int d) { return d == BFLY_F32 || d == BFLY_BF16; }
 
-size_t coeff_bytes_l(int logn) { return (size_t)logn * ((size_t)1 << (logn - 1)) * 8; }
+size_t coeff_bytes_l(int logn) { return bfly::table_bytes(logn); }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -90,15 +103,14 @@ bfly_status check_quant(const uint8_t* codes, const uint16_t* scales, const uint
 template <class F>
 bfly_status with_table(const float* theta, const void* coeffs, int logn, hipStream_t s, F launch) {
   if (coeffs) {
-    const hipError_t e = launch(static_cast<const float2*>(coeffs));
+    const hipError_t e = launch(coeffs);
     return e == hipSuccess ? BFLY_OK : hip_fail(e);
   }
   void* tab = nullptr;
   hipError_t e = hipMallocAsync(&tab, coeff_bytes_l(logn), s);
   if (e != hipSuccess) return hip_fail(e);
-  const int64_t count = (int64_t)logn << (logn - 1);
-  e = bfly::launch_prepare(theta, static_cast<float2*>(tab), count, s);
-  if (e == hipSuccess) e = launch(static_cast<const float2*>(tab));
+  e = bfly::launch_prepare(theta, tab, logn, s);
+  if (e == hipSuccess) e = launch(tab);
   const hipError_t ef = hipFreeAsync(tab, s);
   if (e != hipSuccess) return hip_fail(e);
   if (ef != hipSuccess) return hip_fail(ef);
@@ -123,8 +135,7 @@ bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coe
   if (st != BFLY_OK) return st;
   if (coeff_bytes < coeff_bytes_l(l)) return BFLY_ERR_WORKSPACE;
   if (!aligned(coeffs, 16) || !aligned(theta, 4)) return BFLY_ERR_ALIGN;
-  const hipError_t e = bfly::launch_prepare(theta, static_cast<float2*>(coeffs),
-                                            (int64_t)l << (l - 1), (hipStream_t)hip_stream);
+  const hipError_t e = bfly::launch_prepare(theta, coeffs, l, (hipStream_t)hip_stream);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
@@ -171,8 +182,8 @@ static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_
   p.group = quant ? group : 0;
   p.asym = quant && mode == BFLY_ASYM_MINMAX;
   const hipStream_t s = (hipStream_t)hip_stream;
-  return with_table(theta, coeffs, lognb, s, [&](const float2* cs) {
-    p.cs = cs;
+  return with_table(theta, coeffs, lognb, s, [&](const void* tab) {
+    p.tab = bfly::table_at(tab, lognb);
     return bfly::launch_forward(p, s);
   });
 }
@@ -209,7 +220,7 @@ size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n) {
   int l = 0;
   if (rows < 0 || check_n(n, 12, &l) != BFLY_OK) return 0;
   const size_t slots = (size_t)bfly::backward_blocks(rows, l) * bwd_rows_per_block(l);
-  return align_up(coeff_bytes_l(l), 256) + slots * coeff_bytes_l(l) / 2;
+  return align_up(coeff_bytes_l(l), 256) + slots * ((size_t)l << (l - 1)) * sizeof(float);
 }
 
 bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, float* dtheta,
@@ -228,12 +239,11 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
     return BFLY_ERR_ALIGN;
   const hipStream_t s = (hipStream_t)hip_stream;
   char* ws = static_cast<char*>(workspace);
-  const float2* cs = static_cast<const float2*>(coeffs);
-  if (!cs) {
-    const hipError_t e = bfly::launch_prepare(theta, reinterpret_cast<float2*>(ws),
-                                              (int64_t)l << (l - 1), s);
+  const void* tab = coeffs;
+  if (!tab) {
+    const hipError_t e = bfly::launch_prepare(theta, ws, l, s);
     if (e != hipSuccess) return hip_fail(e);
-    cs = reinterpret_cast<const float2*>(ws);
+    tab = ws;
   }
   bfly::BwdParams p;
   memset(&p, 0, sizeof(p));
@@ -242,7 +252,7 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   p.y = y;
   p.dx = dx;
   p.partials = reinterpret_cast<float*>(ws + align_up(coeff_bytes_l(l), 256));
-  p.cs = cs;
+  p.cs = bfly::table_at(tab, l).cs;
   p.rows = rows;
   p.logn = l;
   p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);

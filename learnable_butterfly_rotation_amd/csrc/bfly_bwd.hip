@@ -231,18 +231,57 @@ __global__ void reduce_partials_kernel(const float* __restrict__ partials, float
   dtheta[k] = (float)sum;
 }
 
-__global__ void prepare_kernel(const float* __restrict__ theta, float2* __restrict__ cs, int64_t count) {
+// One thread per (stage s, pair p).  Besides (cos t, sin t) it writes the
+// three-shear coefficients of stages 0..L-2 and the last stage's 4
+// coefficients.  The sign an element carries before stage s is the parity
+// of the stages s' < s whose angle on that element's pair exceeds pi/2 in
+// magnitude (each such stage negates both of its elements), so every entry
+// is computed independently from the angles.
+__global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
+  const int half = 1 << (logn - 1);
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= count) return;
+  if (k >= (int64_t)logn * half) return;
+  const int s = (int)(k / half), p = (int)(k % half);
+  const int i = ((p >> s) << (s + 1)) | (p & ((1 << s) - 1));  // lower element of the pair
+  const int j = i | (1 << s);
+  const double halfpi = 1.5707963267948966;
+  const double t = (double)theta[k];
   double sn, cn;
-  sincos((double)theta[k], &sn, &cn);
+  sincos(t, &sn, &cn);
+  float2* cs = reinterpret_cast<float2*>(table);
+  float2* lift = reinterpret_cast<float2*>(table + (size_t)half * 8 * logn);
+  float4* last = reinterpret_cast<float4*>(table + (size_t)half * 8 * (2 * logn - 1));
   cs[k] = make_float2((float)cn, (float)sn);
+  // all the angle loads are independent: unrolled, they are in flight together
+  int par_i = 0, par_j = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < 13; ++s2) {
+    if (s2 < s) {
+      // the same predicate (in fp64) as the flip decision below
+      par_i ^= fabs((double)theta[(int64_t)s2 * half + pair_rank(i, s2)]) > halfpi;
+      par_j ^= fabs((double)theta[(int64_t)s2 * half + pair_rank(j, s2)]) > halfpi;
+    }
+  }
+  if (s < logn - 1) {
+    // phi = t or t -+ pi (|phi| <= pi/2): sin and cos of phi are +-sin t and
+    // +-cos t, and tan(phi/2) = sin(phi) / (1 + cos(phi)), whose denominator
+    // lies in [1, 2] -- one fp64 sincos serves every coefficient.
+    const bool flip = fabs(t) > halfpi;
+    const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
+    const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
+    lift[k] = make_float2((float)(-eps * (sp / (1.0 + cp))), (float)(eps * sp));
+  } else {
+    const double si = par_i ? -1.0 : 1.0, sj = par_j ? -1.0 : 1.0;
+    last[p] = make_float4((float)(cn * si), (float)(-sn * sj), (float)(sn * si), (float)(cn * sj));
+  }
 }
 
-hipError_t launch_prepare(const float* theta, float2* cs, int64_t count, hipStream_t s) {
-  const int threads = 256;
+hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s) {
+  const int threads = 64;  // small blocks spread the angles over every CU
+  const int64_t count = (int64_t)logn << (logn - 1);
   const int64_t blocks = (count + threads - 1) / threads;
-  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, theta, cs, count);
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, theta,
+                     static_cast<char*>(table), logn);
   return hipGetLastError();
 }
 

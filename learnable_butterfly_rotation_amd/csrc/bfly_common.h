@@ -38,11 +38,12 @@ __host__ __device__ constexpr int lds_words(int nb) { return nb + 4 * (nb >> 5) 
 // bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two values in one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Rank of the pair (i, i + 2^s) among the stage-s pairs ordered by i.

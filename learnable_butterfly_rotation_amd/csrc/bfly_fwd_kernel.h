@@ -20,26 +20,64 @@
 
 namespace bfly {
 
-template <int LOGNB, int M>
+// Whether the transpose from register layout b0 to b1 keeps every element
+// inside its wavefront.  Thread bit j carries index bit j (j < b) or j + LOGE
+// (j >= b); when each wave-index bit (thread bits 6 .. logt-1) carries the
+// same index bit in both layouts, no data crosses a wave and a wave-level
+// ordering suffices instead of a workgroup barrier.
+__host__ __device__ constexpr bool wave_local(int b0, int b1, int logt) {
+  for (int j = 6; j < logt; ++j)
+    if ((j < b0) != (j < b1)) return false;
+  return true;
+}
+
+__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
+// RPT rows per thread: the same (cos, sin) registers serve RPT rows at once,
+// halving the barriers and coefficient traffic per row and doubling the
+// independent work between barriers.
+template <int LOGNB, int M, int RPT>
 struct FwdShape {
   static constexpr int LOGE = 3;
   static constexpr int NB = 1 << LOGNB;
   static constexpr int E = 1 << LOGE;
-  static constexpr int T = NB >> LOGE;             // threads per row
+  static constexpr int T = NB >> LOGE;             // threads per row team
+  static constexpr int LOGT = ilog2c(T);
   static constexpr int N = M * NB;                 // row length
-  static constexpr int R_THREADS = (256 / T) > 0 ? (256 / T) : 1;
-  static constexpr int SEGW = lds_words(NB);     // padded LDS words per segment
-  static constexpr int R_LDS = (8192 / N) > 0 ? (8192 / N) : 1;
-  static constexpr int R = R_THREADS < R_LDS ? R_THREADS : R_LDS;  // rows per pass
-  static constexpr int NT = T * R;                 // threads per workgroup
+  static constexpr int SEGS = RPT * M;             // segments a thread carries
+  static constexpr int SEGW = lds_words(NB);       // padded LDS words per segment
   static constexpr int L = LOGNB;
   static constexpr int NPH = (L + LOGE - 1) / LOGE;  // register phases
-  static constexpr size_t LDS_BYTES = 2ull * R * M * SEGW * sizeof(float);
+  static constexpr int R_THREADS = (256 / T) > 0 ? (256 / T) : 1;
+  static constexpr int R_LDS = (8192 / (SEGS * NB)) > 0 ? (8192 / (SEGS * NB)) : 1;
+  static constexpr int R = R_THREADS < R_LDS ? R_THREADS : R_LDS;  // teams per workgroup
+  static constexpr int NT = T * R;                 // threads per workgroup
+  static constexpr int ROWS_PER_PASS = R * RPT;
+  static constexpr int BUFW = R * SEGS * SEGW;     // words per LDS buffer
+  static constexpr bool local_transpose(int k) {   // transpose into phase k (k = NPH: back to 0)
+    return wave_local(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0, LOGT);
+  }
+  static constexpr bool any_global() {
+    for (int k = 1; k <= NPH; ++k)
+      if (!local_transpose(k)) return true;
+    return false;
+  }
+  // one buffer for wave-local transposes, two alternating ones for the rest
+  static constexpr size_t LDS_BYTES = (any_global() ? 3ull : 1ull) * BUFW * sizeof(float);
 };
 
-__device__ __forceinline__ void givens(float& a, float& b, float c, float s) {
-  const float na = fmaf(c, a, -(s * b));
-  const float nb = fmaf(s, a, c * b);
+// Givens rotation of (a, b) by phi, |phi| <= pi/2, as three shears:
+// p = -tan(phi/2), u = sin(phi).  Three in-place FMAs, no temporaries.
+__device__ __forceinline__ void shear3(float& a, float& b, float p, float u) {
+  a = fmaf(p, b, a);
+  b = fmaf(u, a, b);
+  a = fmaf(p, b, a);
+}
+
+// The last stage: (a, b) <- (k.x a + k.y b, k.z a + k.w b).
+__device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
+  const float na = fmaf(k.x, a, k.y * b);
+  const float nb = fmaf(k.z, a, k.w * b);
   a = na;
   b = nb;
 }
@@ -85,49 +123,75 @@ __device__ __forceinline__ void lds_get(const float* buf, float (&v)[M][1 << LOG
   }
 }
 
-// Quantize the E consecutive values of one thread (part of a group spread
-// over group/E consecutive lanes) and store codes, scale and zero point.
-// Every lane of the wave executes the reductions; only `store` lanes write.
-template <int E>
-__device__ __forceinline__ void quantize_store(const float (&v)[E], const FwdParams& P,
-                                               int64_t row, int64_t n, int col, bool store) {
-  const int gt = P.group / E;  // lanes per group (power of two, <= 64)
-  const bool asym = P.asym != 0;
-  const int bits = P.bits;
+// Cross-lane max/min over the `gt` consecutive lanes of a quantization group
+// (gt a power of two <= 64).  Within a 16-lane DPP row: xor-1 and xor-2 quad
+// permutes, then the half-row mirror (lane l <-> 7 - l) joins the two quads
+// of a half-row and the row mirror (l <-> 15 - l) the two halves; wider
+// groups use bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+__device__ __forceinline__ float group_max(float v, int gt) {
+  if (gt >= 2) v = fmaxf(v, dpp<DPP_XOR1>(v));
+  if (gt >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
+  if (gt >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  if (gt >= 16) v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  if (gt >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (gt >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group_min(float v, int gt) {
+  if (gt >= 2) v = fminf(v, dpp<DPP_XOR1>(v));
+  if (gt >= 4) v = fminf(v, dpp<DPP_XOR2>(v));
+  if (gt >= 8) v = fminf(v, dpp<DPP_HALF_MIRROR>(v));
+  if (gt >= 16) v = fminf(v, dpp<DPP_MIRROR>(v));
+  if (gt >= 32) v = fminf(v, __shfl_xor(v, 16));
+  if (gt >= 64) v = fminf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Quantize the E = 8 consecutive values one thread holds (part of a group
+// spread over gt = group/8 consecutive lanes).  Returns the packed codes and,
+// in `sz`, the fp16 scale bits (low half) and zero-point bits (high half).
+//
+// Scale: s16 = fp16(absmax / qmax) or fp16((max - min) / levels), the
+// quotient taken as a product with the fp32 reciprocal of the constant (it
+// can differ from the correctly rounded quotient only within 2 fp32 ulps of
+// an fp16 rounding midpoint).  Codes: q = rne(y * r) with r = 1/s16 (one
+// Newton step on the hardware reciprocal), computed as
+// fma(y, r, 1.5*2^23 + bias): the exact product is rounded once, to an
+// integer, ties to even, and the low bits of the result's encoding are
+// q + bias.  Clamping y to [qlo*s16, qhi*s16] (products exact in fp32) is the
+// same as clamping q afterwards.
+__device__ __forceinline__ uint32_t quantize8(const float (&v)[8], int bits, int gt, bool asym,
+                                              float inv_top, float top, uint32_t& sz) {
   float lo, hi;
   if (asym) {
-    lo = v[0];
-    hi = v[0];
-#pragma unroll
-    for (int e = 1; e < E; ++e) {
-      lo = fminf(lo, v[e]);
-      hi = fmaxf(hi, v[e]);
-    }
-    for (int msk = 1; msk < gt; msk <<= 1) {
-      lo = fminf(lo, __shfl_xor(lo, msk));
-      hi = fmaxf(hi, __shfl_xor(hi, msk));
-    }
+    lo = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])), fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
+    hi = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    lo = group_min(lo, gt);
+    hi = group_max(hi, gt);
   } else {
-    hi = fabsf(v[0]);
-#pragma unroll
-    for (int e = 1; e < E; ++e) hi = fmaxf(hi, fabsf(v[e]));
-    for (int msk = 1; msk < gt; msk <<= 1) hi = fmaxf(hi, __shfl_xor(hi, msk));
+    hi = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+               fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    hi = group_max(hi, gt);
     lo = 0.f;
   }
-  const float top = asym ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
-  float s_pre = asym ? (hi - lo) / top : hi / top;
-  s_pre = fminf(s_pre, 65504.f);
+  const float s_pre = fminf((hi - lo) * inv_top, 65504.f);  // saturate to the largest finite fp16
   const _Float16 s16 = (_Float16)s_pre;
   const float sc = (float)s16;
-  // codes: q = rne(clamp(y, qlo*sc, qhi*sc) * (1/sc)) (+ zero).  qlo*sc and
-  // qhi*sc are exact in fp32, and clamping y first is the same as clamping
-  // q afterwards.  fma(y, r, 1.5*2^23) rounds the exact product y*r once,
-  // to an integer, ties to even; its low mantissa bits are q.
   float r = 0.f, clo = 0.f, chi = 0.f, z = 0.f;
   if (sc != 0.f) {
-    r = 1.0f / sc;
+    r = __builtin_amdgcn_rcpf(sc);
+    r = fmaf(fmaf(-sc, r, 1.0f), r, r);
     if (asym) {
-      z = fminf(fmaxf(rintf(-lo / sc), 0.f), top);
+      z = __builtin_amdgcn_fmed3f(rintf(-lo * r), 0.f, top);
       clo = -z * sc;
       chi = (top - z) * sc;
     } else {
@@ -135,124 +199,241 @@ __device__ __forceinline__ void quantize_store(const float (&v)[E], const FwdPar
       chi = top * sc;
     }
   }
-  const uint32_t zi = (uint32_t)z;
-  const uint32_t mask = (1u << bits) - 1u;
-  uint64_t packed = 0;
+  sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z) << 16);
+  uint32_t packed;
+  if (!asym && bits == 4) {
+    // biased nibbles q + 8 in 1..15, two per byte, then two's complement by ^8
+    uint32_t f[8];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float yc = fminf(fmaxf(v[e], clo), chi);
-    const float f = fmaf(yc, r, 12582912.0f);
-    const uint32_t q = (__float_as_uint(f) - 0x4B400000u + zi) & mask;
-    packed |= (uint64_t)q << (bits * e);
-  }
-  if (store) {
-    const int64_t rowbytes = n * bits / 8;
-    uint8_t* cp = P.codes + row * rowbytes + (int64_t)col * bits / 8;
-    const int nbytes = E * bits / 8;  // 2, 4 or 8
-    if (nbytes == 8) *reinterpret_cast<uint2*>(cp) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
-    else if (nbytes == 4) *reinterpret_cast<uint32_t*>(cp) = (uint32_t)packed;
-    else *reinterpret_cast<uint16_t*>(cp) = (uint16_t)packed;
-    if (((col / E) & (gt - 1)) == 0) {
-      const int64_t gi = row * (n / P.group) + col / P.group;
-      P.scales[gi] = __builtin_bit_cast(uint16_t, s16);
-      if (asym) P.zeros[gi] = __builtin_bit_cast(uint16_t, (_Float16)z);
+    for (int e = 0; e < 8; ++e)
+      f[e] = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f(v[e], clo, chi), r, 12582920.0f));
+    const uint32_t p0 = (f[1] << 4) | f[0], p1 = (f[3] << 4) | f[2];
+    const uint32_t p2 = (f[5] << 4) | f[4], p3 = (f[7] << 4) | f[6];
+    const uint32_t w01 = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
+    const uint32_t w23 = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
+    packed = (w01 | w23) ^ 0x88888888u;
+  } else {
+    const uint32_t off = (uint32_t)z - 0x4B400000u;
+    const uint32_t mask = (1u << bits) - 1u;
+    packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = fmaf(__builtin_amdgcn_fmed3f(v[e], clo, chi), r, 12582912.0f);
+      packed |= ((__float_as_uint(f) + off) & mask) << (bits * e);
     }
   }
+  return packed;
 }
 
-template <int LOGNB, int M, bool XBF16>
-__global__ void __launch_bounds__((FwdShape<LOGNB, M>::NT))
-fwd_kernel(FwdParams P) {
-  using S = FwdShape<LOGNB, M>;
-  constexpr int LOGE = S::LOGE, E = S::E, T = S::T, NB = S::NB, N = S::N, R = S::R;
-  constexpr int SEGW = S::SEGW;
+// Orders this wave's LDS writes before its later LDS reads (the LDS executes
+// one wave's instructions in order; this keeps the compiler from moving
+// them across each other).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Output / quantizer variants of the row loop, fixed at compile time so the
+// loop carries no mode branches.
+enum QMode : int { Q_NONE = 0, Q_SYM4 = 1, Q_ANY = 2 };
+
+// Number of workgroup-wide (non wave-local) transposes in one row.
+template <class S>
+__host__ __device__ constexpr int global_transposes() {
+  int g = 0;
+  for (int k = 1; k <= S::NPH; ++k) g += S::local_transpose(k) ? 0 : 1;
+  return g;
+}
+
+template <class S>
+struct Coeffs {
+  float p[S::L - 1][S::E / 2];
+  float u[S::L - 1][S::E / 2];
+  float4 last[S::E / 2];
+};
+
+// The persistent row loop for one (input, output, quantizer) variant.
+template <class S, bool XBF16, int YK, int QM>
+__device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int team, int t,
+                                         const Coeffs<S>& C) {
+  constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, R = S::R, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
+  constexpr int RPT = S::ROWS_PER_PASS / S::R;
+  constexpr int SEGS = S::SEGS, SEGW = S::SEGW, BUFW = S::BUFW, RPP = S::ROWS_PER_PASS;
   constexpr int L = S::L, NPH = S::NPH;
   constexpr int RAW = XBF16 ? E / 8 : E / 4;  // 16-byte vectors per segment
-  extern __shared__ float4 lds_raw[];
-  float* lds = reinterpret_cast<float*>(lds_raw);
+  constexpr int ESZ = XBF16 ? 2 : 4;
+  constexpr bool QUANT = QM != Q_NONE;
+  static_assert(global_transposes<S>() % 2 == 0, "buffer alternation assumes an even count");
 
-  const int tid = threadIdx.x;
-  const int team = tid / T;
-  const int t = tid - team * T;
-
-  // (cos, sin) of every pair this thread rotates, resident for all rows.
-  float cc[L][E / 2], ss[L][E / 2];
-#pragma unroll
-  for (int s = 0; s < L; ++s) {
-    const int b = phase_base(s / LOGE, L, LOGE);
-#pragma unroll
-    for (int j = 0; j < E / 2; ++j) {
-      const int ilo = lay<LOGE>(t, pair_lo(j, s - b), b);
-      const float2 c = P.cs[s * (NB / 2) + pair_rank(ilo, s)];
-      cc[s][j] = c.x;
-      ss[s][j] = c.y;
-    }
-  }
+  float* const lbuf = lds + team * (SEGS * SEGW);          // wave-local transposes
+  float* const gbuf0 = lds + BUFW + team * (SEGS * SEGW);  // workgroup transposes
+  float* const gbuf1 = lds + 2 * BUFW + team * (SEGS * SEGW);
 
   const int64_t rows = P.rows;
-  const int64_t ngrp = (rows + R - 1) / R;
+  const int64_t ngrp = (rows + RPP - 1) / RPP;
   const char* xb = reinterpret_cast<const char*>(P.x);
-  constexpr int ESZ = XBF16 ? 2 : 4;
+  const int bits = QM == Q_SYM4 ? 4 : P.bits;
+  const bool asym = QM == Q_ANY && P.asym != 0;
+  const int gt = QUANT ? P.group / E : 1;
+  const int lg_group = QUANT ? 31 - __builtin_clz(P.group) : 0;
+  const float top = asym ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
+  const float inv_top = 1.0f / top;
+  const int64_t code_row_bytes = (int64_t)N * bits / 8;
+  const int ngroups_row = QUANT ? N >> lg_group : 0;
 
-  // Input registers of the current row group; refilled with the next
-  // group's row as soon as they have been unpacked (zeros past the end).
-  uint4 cur[M][RAW];
-  auto load = [&](int64_t grp, uint4 (&dst)[M][RAW]) {
-    const int64_t row = grp * R + team;
-    const bool ok = row < rows;
+  // Addresses: a row group's base is uniform across the workgroup (scalar
+  // registers); each thread adds a fixed 32-bit offset.  Only the last,
+  // partial group takes the per-row path.
+  constexpr int64_t GRP_ELEMS = (int64_t)RPP * N;
+  const int thr_elem = team * RPT * N + t * E;  // element offset of (team, t) in a group
+  auto group_full = [&](int64_t grp) { return grp * RPP + RPP <= rows; };
+
+  // Input registers of the current row group, refilled with the next
+  // group's rows as soon as they have been unpacked.  In a partial group the
+  // rows past the end read the last row instead (their results are never
+  // stored).
+  uint4 cur[SEGS][RAW];
+  auto load = [&](int64_t grp) {
+    if (group_full(grp)) {
+      const char* base = xb + grp * GRP_ELEMS * ESZ;
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+        for (int a = 0; a < M; ++a) {
+          const uint4* src = reinterpret_cast<const uint4*>(base + (thr_elem + rr * N + a * NB) * ESZ);
+#pragma unroll
+          for (int c = 0; c < RAW; ++c) cur[rr * M + a][c] = src[c];
+        }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        int64_t row = (grp * R + team) * RPT + rr;
+        row = row < rows ? row : rows - 1;
+#pragma unroll
+        for (int a = 0; a < M; ++a) {
+          const uint4* src =
+              reinterpret_cast<const uint4*>(xb + ((row * N + a * NB + (int64_t)t * E) * ESZ));
+#pragma unroll
+          for (int c = 0; c < RAW; ++c) cur[rr * M + a][c] = src[c];
+        }
+      }
+    }
+  };
+
+  // bf16 rows, codes and scales of the previous row group, stored only once
+  // the next group's input has arrived: the wait for that input then never
+  // has to wait for freshly issued stores as well.
+  uint32_t held_y[SEGS][E / 2], held_c[SEGS], held_sz[SEGS];
+  float vq[SEGS][E];  // the previous group's rotated rows, awaiting quantization
+#pragma unroll
+  for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+    for (int e = 0; e < E; ++e) vq[sg][e] = 0.f;
+  int64_t held_grp = -1;
+  const bool scale_lane = QUANT && (t & (gt - 1)) == 0;
+  auto store_one = [&](int64_t grp, int rr) {
+    const int64_t row = (grp * R + team) * RPT + rr;
 #pragma unroll
     for (int a = 0; a < M; ++a) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          xb + (((ok ? row : 0) * N + a * NB + (int64_t)t * E) * ESZ));
+      const int sg = rr * M + a;
+      const int col = a * NB + t * E;
+      if (YK == Y_BF16) {
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(P.y) + grp * GRP_ELEMS +
+                                              (thr_elem + rr * N + a * NB));
 #pragma unroll
-      for (int c = 0; c < RAW; ++c) dst[a][c] = ok ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+        for (int c = 0; c < E / 8; ++c)
+          dst[c] = make_uint4(held_y[sg][4 * c], held_y[sg][4 * c + 1], held_y[sg][4 * c + 2],
+                              held_y[sg][4 * c + 3]);
+      }
+      if (QUANT) {
+        uint8_t* cp = P.codes + grp * (GRP_ELEMS * bits / 8) +
+                      (int)((thr_elem + rr * N + a * NB) * bits / 8);
+        if (bits == 4) *reinterpret_cast<uint32_t*>(cp) = held_c[sg];
+        else *reinterpret_cast<uint16_t*>(cp) = (uint16_t)held_c[sg];
+        if (scale_lane) {
+          const int64_t gi = row * ngroups_row + (col >> lg_group);
+          P.scales[gi] = (uint16_t)held_sz[sg];
+          if (asym) P.zeros[gi] = (uint16_t)(held_sz[sg] >> 16);
+        }
+      }
+    }
+  };
+  auto flush = [&]() {
+    if (YK != Y_BF16 && !QUANT) return;
+    if (held_grp < 0) return;
+    if (group_full(held_grp)) {
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) store_one(held_grp, rr);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr)
+        if ((held_grp * R + team) * RPT + rr < rows) store_one(held_grp, rr);
     }
   };
 
   int64_t grp = blockIdx.x;
-  if (grp < ngrp) load(grp, cur);
-  int bufsel = 0;
+  if (grp < ngrp) load(grp);
   for (; grp < ngrp; grp += gridDim.x) {
-    const int64_t gnext = grp + gridDim.x;
-    const int64_t row = grp * R + team;
-    const bool valid = row < rows;
+    const int64_t row0 = (grp * R + team) * RPT;
 
-    float v[M][E];
+    float v[SEGS][E];
 #pragma unroll
-    for (int a = 0; a < M; ++a) {
+    for (int sg = 0; sg < SEGS; ++sg) {
       if (XBF16) {
 #pragma unroll
         for (int c = 0; c < RAW; ++c) {
-          const uint32_t w[4] = {cur[a][c].x, cur[a][c].y, cur[a][c].z, cur[a][c].w};
+          const uint32_t w[4] = {cur[sg][c].x, cur[sg][c].y, cur[sg][c].z, cur[sg][c].w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            v[a][8 * c + 2 * k] = bf16_lo(w[k]);
-            v[a][8 * c + 2 * k + 1] = bf16_hi(w[k]);
+            v[sg][8 * c + 2 * k] = bf16_lo(w[k]);
+            v[sg][8 * c + 2 * k + 1] = bf16_hi(w[k]);
           }
         }
       } else {
 #pragma unroll
         for (int c = 0; c < RAW; ++c) {
-          v[a][4 * c] = __uint_as_float(cur[a][c].x);
-          v[a][4 * c + 1] = __uint_as_float(cur[a][c].y);
-          v[a][4 * c + 2] = __uint_as_float(cur[a][c].z);
-          v[a][4 * c + 3] = __uint_as_float(cur[a][c].w);
+          v[sg][4 * c] = __uint_as_float(cur[sg][c].x);
+          v[sg][4 * c + 1] = __uint_as_float(cur[sg][c].y);
+          v[sg][4 * c + 2] = __uint_as_float(cur[sg][c].z);
+          v[sg][4 * c + 3] = __uint_as_float(cur[sg][c].w);
         }
       }
     }
+    if (grp + gridDim.x < ngrp) load(grp + gridDim.x);
 
-    if (gnext < ngrp) load(gnext, cur);
-
+    // The previous group's quantization runs here, interleaved with this
+    // group's first register phase: the two dependency chains are
+    // independent, so each fills the other's latency.  (On the first pass it
+    // quantizes zeros and nothing is stored.)
+    if (QUANT) {
 #pragma unroll
-    for (int k = 0; k < NPH; ++k) {
-      const int b = phase_base(k, L, LOGE);
-      if (k > 0) {
-        float* buf = lds + (size_t)(bufsel * R + team) * (M * SEGW);
-        lds_put<LOGE, M, SEGW>(buf, v, t, phase_base(k - 1, L, LOGE));
-        __syncthreads();
-        lds_get<LOGE, M, SEGW>(buf, v, t, b);
-        bufsel ^= 1;
+      for (int sg = 0; sg < SEGS; ++sg)
+        held_c[sg] = quantize8(vq[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
+    }
+    int gidx = 0;  // workgroup transposes so far in this row (compile-time after unrolling)
+#pragma unroll
+    for (int k = 0; k <= NPH; ++k) {
+      if (k == 1) flush();  // the previous group's outputs, now complete
+      if (k > 0) {  // transpose from phase k-1 into phase k (k == NPH: back to layout 0)
+        const int bp = phase_base(k - 1, L, LOGE);
+        const int b = k < NPH ? phase_base(k, L, LOGE) : 0;
+        if (S::local_transpose(k)) {
+          lds_put<LOGE, SEGS, SEGW>(lbuf, v, t, bp);
+          wave_lds_sync();
+          lds_get<LOGE, SEGS, SEGW>(lbuf, v, t, b);
+          wave_lds_sync();
+        } else {
+          float* buf = (gidx & 1) ? gbuf1 : gbuf0;
+          lds_put<LOGE, SEGS, SEGW>(buf, v, t, bp);
+          __syncthreads();
+          lds_get<LOGE, SEGS, SEGW>(buf, v, t, b);
+          ++gidx;
+        }
       }
+      if (k == NPH) break;
+      const int b = phase_base(k, L, LOGE);
       const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
 #pragma unroll
       for (int s = k * LOGE; s < s_end; ++s) {
@@ -261,66 +442,118 @@ fwd_kernel(FwdParams P) {
         for (int j = 0; j < E / 2; ++j) {
           const int lo = pair_lo(j, q), hi = lo | (1 << q);
 #pragma unroll
-          for (int a = 0; a < M; ++a) givens(v[a][lo], v[a][hi], cc[s][j], ss[s][j]);
+          for (int sg = 0; sg < SEGS; ++sg) {
+            if (s < L - 1) shear3(v[sg][lo], v[sg][hi], C.p[s][j], C.u[s][j]);
+            else last2x2(v[sg][lo], v[sg][hi], C.last[j]);
+          }
         }
       }
     }
-    {  // back to the load/store layout
-      float* buf = lds + (size_t)(bufsel * R + team) * (M * SEGW);
-      lds_put<LOGE, M, SEGW>(buf, v, t, phase_base(NPH - 1, L, LOGE));
-      __syncthreads();
-      lds_get<LOGE, M, SEGW>(buf, v, t, 0);
-      bufsel ^= 1;
+
+    if (M > 1 || P.mix != nullptr) {  // Kronecker mix across a row's segments, column by column
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float w[M];
+#pragma unroll
+          for (int a = 0; a < M; ++a) {
+            float acc = P.mix[a * M] * v[rr * M][e];
+#pragma unroll
+            for (int a2 = 1; a2 < M; ++a2) acc = fmaf(P.mix[a * M + a2], v[rr * M + a2][e], acc);
+            w[a] = acc;
+          }
+#pragma unroll
+          for (int a = 0; a < M; ++a) v[rr * M + a][e] = w[a];
+        }
     }
 
-    if (M > 1 || P.mix != nullptr) {  // Kronecker mix across segments, column by column
+    if (YK == Y_F32) {  // fp32 rows are stored right away
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float w[M];
+      for (int rr = 0; rr < RPT; ++rr) {
+        const int64_t row = row0 + rr;
+        if (row >= rows) continue;
 #pragma unroll
         for (int a = 0; a < M; ++a) {
-          float acc = P.mix[a * M] * v[0][e];
-#pragma unroll
-          for (int a2 = 1; a2 < M; ++a2) acc = fmaf(P.mix[a * M + a2], v[a2][e], acc);
-          w[a] = acc;
-        }
-#pragma unroll
-        for (int a = 0; a < M; ++a) v[a][e] = w[a];
-      }
-    }
-
-    if (valid && P.y_kind != Y_NONE) {
-#pragma unroll
-      for (int a = 0; a < M; ++a) {
-        const int64_t off = row * N + a * NB + (int64_t)t * E;
-        if (P.y_kind == Y_BF16) {
-          uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(P.y) + off);
-#pragma unroll
-          for (int c = 0; c < E / 8; ++c)
-            dst[c] = make_uint4(pack_bf16(v[a][8 * c], v[a][8 * c + 1]),
-                                pack_bf16(v[a][8 * c + 2], v[a][8 * c + 3]),
-                                pack_bf16(v[a][8 * c + 4], v[a][8 * c + 5]),
-                                pack_bf16(v[a][8 * c + 6], v[a][8 * c + 7]));
-        } else {
-          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(P.y) + off);
+          float4* dst = reinterpret_cast<float4*>(P.y) + (row * N + a * NB + (int64_t)t * E) / 4;
+          const int sg = rr * M + a;
 #pragma unroll
           for (int c = 0; c < E / 4; ++c)
-            dst[c] = make_float4(v[a][4 * c], v[a][4 * c + 1], v[a][4 * c + 2], v[a][4 * c + 3]);
+            dst[c] = make_float4(v[sg][4 * c], v[sg][4 * c + 1], v[sg][4 * c + 2], v[sg][4 * c + 3]);
         }
       }
-    }
-    if (P.codes != nullptr) {
+    } else if (YK == Y_BF16) {
 #pragma unroll
-      for (int a = 0; a < M; ++a) quantize_store<E>(v[a], P, row, N, a * NB + t * E, valid);
+      for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+        for (int k = 0; k < E / 2; ++k) held_y[sg][k] = pack_bf16(v[sg][2 * k], v[sg][2 * k + 1]);
     }
+    if (QUANT) {
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+        for (int e = 0; e < E; ++e) vq[sg][e] = v[sg][e];
+    }
+    held_grp = grp;
+  }
+  if (QUANT) {
+#pragma unroll
+    for (int sg = 0; sg < SEGS; ++sg)
+      held_c[sg] = quantize8(vq[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
+  }
+  flush();
+}
+
+template <int LOGNB, int M, int RPT, bool XBF16>
+__global__ void __launch_bounds__((FwdShape<LOGNB, M, RPT>::NT))
+fwd_kernel(FwdParams P) {
+  using S = FwdShape<LOGNB, M, RPT>;
+  constexpr int LOGE = S::LOGE, E = S::E, T = S::T, NB = S::NB, L = S::L;
+  extern __shared__ float4 lds_raw[];
+  float* const lds = reinterpret_cast<float*>(lds_raw);
+  const int tid = threadIdx.x;
+  const int team = tid / T;
+  const int t = tid - team * T;
+
+  // Coefficients of every pair this thread rotates, resident for all rows:
+  // stages 0..L-2 as three shears (p, u), the last stage as a 2x2 matrix.
+  Coeffs<S> C;
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const int b = phase_base(s / LOGE, L, LOGE);
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int rank = pair_rank(lay<LOGE>(t, pair_lo(j, s - b), b), s);
+      if (s < L - 1) {
+        const float2 c = P.tab.lift[s * (NB / 2) + rank];
+        C.p[s][j] = c.x;
+        C.u[s][j] = c.y;
+      } else {
+        C.last[j] = P.tab.last[rank];
+      }
+    }
+  }
+
+  const bool quant = P.codes != nullptr;
+  const bool sym4 = quant && P.bits == 4 && P.asym == 0;
+  if (P.y_kind == Y_BF16) {
+    if (!quant) row_loop<S, XBF16, Y_BF16, Q_NONE>(P, lds, team, t, C);
+    else if (sym4) row_loop<S, XBF16, Y_BF16, Q_SYM4>(P, lds, team, t, C);
+    else row_loop<S, XBF16, Y_BF16, Q_ANY>(P, lds, team, t, C);
+  } else if (P.y_kind == Y_NONE) {
+    if (sym4) row_loop<S, XBF16, Y_NONE, Q_SYM4>(P, lds, team, t, C);
+    else row_loop<S, XBF16, Y_NONE, Q_ANY>(P, lds, team, t, C);
+  } else {
+    if (!quant) row_loop<S, XBF16, Y_F32, Q_NONE>(P, lds, team, t, C);
+    else row_loop<S, XBF16, Y_F32, Q_ANY>(P, lds, team, t, C);
   }
 }
 
 // Host-side launch of one instantiation.
-template <int LOGNB, int M, bool XBF16>
+template <int LOGNB, int M, int RPT, bool XBF16>
 hipError_t launch_fwd_inst(const FwdParams& p, hipStream_t stream) {
-  using S = FwdShape<LOGNB, M>;
-  auto kern = fwd_kernel<LOGNB, M, XBF16>;
+  using S = FwdShape<LOGNB, M, RPT>;
+  auto kern = fwd_kernel<LOGNB, M, RPT, XBF16>;
   static int blocks_per_cu = -1;
   static int num_cu = 0;
   if (blocks_per_cu < 0) {
@@ -336,7 +569,7 @@ hipError_t launch_fwd_inst(const FwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     blocks_per_cu = bpc > 0 ? bpc : 1;
   }
-  const int64_t ngrp = (p.rows + S::R - 1) / S::R;
+  const int64_t ngrp = (p.rows + S::ROWS_PER_PASS - 1) / S::ROWS_PER_PASS;
   const int64_t cap = (int64_t)blocks_per_cu * num_cu;
   const int grid = (int)(ngrp < cap ? ngrp : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, p);

@@ -3,9 +3,10 @@
 
 namespace bfly {
 
+// One row per thread: measured faster than two in lockstep at n = 4096.
 template <int LOGNB>
 static hipError_t plain(const FwdParams& p, hipStream_t s) {
-  return p.x_bf16 ? launch_fwd_inst<LOGNB, 1, true>(p, s) : launch_fwd_inst<LOGNB, 1, false>(p, s);
+  return p.x_bf16 ? launch_fwd_inst<LOGNB, 1, 1, true>(p, s) : launch_fwd_inst<LOGNB, 1, 1, false>(p, s);
 }
 
 hipError_t launch_forward_plain(const FwdParams& p, hipStream_t s) {

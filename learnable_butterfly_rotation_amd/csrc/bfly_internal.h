@@ -11,15 +11,49 @@ namespace bfly {
 // Output selector for the rotated rows.
 enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 
-// Everything one forward launch needs.  cs is the prepared (cos, sin) table
-// [log2 nb][nb/2]; mix is the m x m Kronecker factor (nullptr when m == 1).
+// The prepared coefficient table of a butterfly of length n = 2^L, in one
+// device allocation (half = n/2 pairs per stage):
+//   cs   float2 [L][half]     (cos t, sin t) of every angle (backward)
+//   lift float2 [L-1][half]   (p, u) of the three-shear form of stages 0..L-2
+//   last float4 [half]        the last stage with the tracked signs folded in
+// Stages 0..L-2 are applied as x += p y; y += u x; x += p y, which is the
+// Givens rotation by an angle phi with |phi| <= pi/2 (p = -tan(phi/2),
+// u = sin phi).  A rotation by t with |t| > pi/2 equals minus the rotation
+// by t -+ pi; the minus is not applied but tracked as a sign on both
+// elements, and a rotation of sign-carrying elements is again a rotation
+// (by +-t).  The last stage maps the sign-carrying values straight to the
+// true outputs: (y_i, y_j) = (a w_i + b w_j, c w_i + d w_j).
+struct Table {
+  const float2* cs;
+  const float2* lift;
+  const float4* last;
+};
+
+__host__ __device__ inline size_t table_bytes(int logn) {
+  const size_t half = (size_t)1 << (logn - 1);
+  return half * 8 * (size_t)(2 * logn + 1);
+}
+
+__host__ __device__ inline Table table_at(const void* base, int logn) {
+  const size_t half = (size_t)1 << (logn - 1);
+  const char* b = static_cast<const char*>(base);
+  Table t;
+  t.cs = reinterpret_cast<const float2*>(b);
+  t.lift = reinterpret_cast<const float2*>(b + half * 8 * logn);
+  t.last = reinterpret_cast<const float4*>(b + half * 8 * (2 * logn - 1));
+  return t;
+}
+
+// Everything one forward launch needs.  tab is the prepared table of the
+// butterfly of length nb; mix is the m x m Kronecker factor (nullptr for a
+// plain butterfly).
 struct FwdParams {
   const void* x;
   void* y;
   uint8_t* codes;     // nullptr: no quantization
   uint16_t* scales;
   uint16_t* zeros;    // asymmetric mode only
-  const float2* cs;
+  Table tab;
   const float* mix;
   int64_t rows;
   int32_t m;          // segments per row (1 = plain butterfly)
@@ -44,7 +78,7 @@ struct BwdParams {
 };
 
 // Kernel-launch helpers; each returns the hipError_t of the launch.
-hipError_t launch_prepare(const float* theta, float2* cs, int64_t count, hipStream_t s);
+hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);
 hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s);
 

@@ -50,12 +50,13 @@ def test_status_strings(L):
 
 
 def test_sizes(L):
-    assert B.bfly_coeff_bytes(4096) == 12 * 2048 * 8
-    assert B.bfly_coeff_bytes(256) == 8 * 128 * 8
+    # (cos, sin) [L][n/2] + three-shear (p, u) [L-1][n/2] + last stage 4 x [n/2], fp32
+    assert B.bfly_coeff_bytes(4096) == (12 * 2 + (12 - 1) * 2 + 4) * 2048 * 4
+    assert B.bfly_coeff_bytes(256) == (8 * 2 + 7 * 2 + 4) * 128 * 4
     assert B.bfly_coeff_bytes(100) == 0
     assert B.bfly_coeff_bytes(32) == 0
     ws = B.bfly_backward_workspace_bytes(262144, 4096)
-    assert ws >= 12 * 2048 * 8 + 12 * 2048 * 4  # table + at least one partial slot
+    assert ws >= B.bfly_coeff_bytes(4096) + 12 * 2048 * 4  # table + at least one partial slot
     assert B.bfly_backward_workspace_bytes(10, 4096) < ws
     assert B.bfly_backward_workspace_bytes(-1, 4096) == 0
     assert B.bfly_backward_workspace_bytes(100, 8192) == 0
