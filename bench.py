@@ -103,6 +103,21 @@ def cpu_baseline_act(w, bytes_per_row, passes=3):
 # the headline workload
 # ---------------------------------------------------------------------------
 
+def warm_up(torch, fn, steps, min_seconds=0.3):
+    """Run `steps` untimed steps, then keep going until `min_seconds` have
+    passed, so the timed steps start at steady clocks.  Returns the seconds
+    spent."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < steps or time.perf_counter() - t0 < min_seconds:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def bench_act(args, torch, B, inputs):
     w = inputs.act_int4()
     x, th = w["x"], w["theta"]
@@ -142,8 +157,7 @@ def bench_act(args, torch, B, inputs):
         if st:
             raise RuntimeError("libbfly call failed with status %d" % st)
 
-    for i in range(args.warmup):
-        step(i)
+    warm_s = warm_up(torch, step, args.warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -168,7 +182,7 @@ def bench_act(args, torch, B, inputs):
                    "rows": rows, "n": n, "bits": bits, "group": group,
                    "bytes_per_step": step_bytes, "rows_per_s": round(rows / (ms_step / 1e3)),
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "buffer_sets": NSETS},
+                   "buffer_sets": NSETS, "warmup_s": round(warm_s, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -188,9 +202,7 @@ def bench_act(args, torch, B, inputs):
 # ---------------------------------------------------------------------------
 
 def time_loop(torch, fn, steps, warmup):
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    warm_up(torch, fn, warmup)
     t0 = time.perf_counter()
     for i in range(steps):
         fn(i)

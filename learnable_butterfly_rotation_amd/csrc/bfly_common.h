@@ -57,6 +57,31 @@ __device__ __forceinline__ int pair_lo(int j, int q) {
   return ((j >> q) << (q + 1)) | (j & ((1 << q) - 1));
 }
 
+// Buffer resources: a raw buffer over [base, base + bytes).  Accesses outside
+// the range read zeros and drop writes in hardware, so row tails, row groups
+// past the end and masked lanes need no branches around memory operations.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // an offset beyond any range below
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= (int64_t)kOutOfRange ? kOutOfRange : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+}
+
 // Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has
 // 160 KiB per CU); fails if the device cannot provide `bytes`.
 inline hipError_t allow_lds(const void* kernel, size_t bytes) {

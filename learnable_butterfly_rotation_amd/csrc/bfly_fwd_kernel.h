@@ -53,6 +53,11 @@ struct FwdShape {
   static constexpr int R = R_THREADS < R_LDS ? R_THREADS : R_LDS;  // teams per workgroup
   static constexpr int NT = T * R;                 // threads per workgroup
   static constexpr int ROWS_PER_PASS = R * RPT;
+  // Row groups whose input is in flight ahead of the one being computed
+  // (each slot holds SEGS segments of the input in registers).  Measured at
+  // n = 4096: two slots of one segment beat one (the load of the next group
+  // is issued a full group earlier) and three (more registers, no gain).
+  static constexpr int PD = SEGS == 1 ? 2 : 1;
   static constexpr int BUFW = R * SEGS * SEGW;     // words per LDS buffer
   static constexpr bool local_transpose(int k) {   // transpose into phase k (k = NPH: back to 0)
     return wave_local(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0, LOGT);
@@ -82,34 +87,38 @@ __device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
   b = nb;
 }
 
-// Write registers in layout b to an LDS row buffer.
-template <int LOGE, int M, int SEGW>
-__device__ __forceinline__ void lds_put(float* buf, const float (&v)[M][1 << LOGE], int t, int b) {
+// Write / read registers in layout b to / from an LDS row buffer.  lds_addr
+// is additive over disjoint index bits, so the address of register e is the
+// thread's base for the layout plus a compile-time offset for e.
+template <int LOGE, int NSEG, int SEGW>
+__device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b) {
   constexpr int E = 1 << LOGE;
+  float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
   if (b == 0) {
 #pragma unroll
-    for (int a = 0; a < M; ++a)
+    for (int a = 0; a < NSEG; ++a)
 #pragma unroll
       for (int c = 0; c < E / 4; ++c)
-        *reinterpret_cast<float4*>(buf + a * SEGW + lds_addr(t * E + 4 * c)) =
+        *reinterpret_cast<float4*>(base + a * SEGW + lds_addr(4 * c)) =
             make_float4(v[a][4 * c], v[a][4 * c + 1], v[a][4 * c + 2], v[a][4 * c + 3]);
   } else {
 #pragma unroll
-    for (int a = 0; a < M; ++a)
+    for (int a = 0; a < NSEG; ++a)
 #pragma unroll
-      for (int e = 0; e < E; ++e) buf[a * SEGW + lds_addr(lay<LOGE>(t, e, b))] = v[a][e];
+      for (int e = 0; e < E; ++e) base[a * SEGW + lds_addr(e << b)] = v[a][e];
   }
 }
 
-template <int LOGE, int M, int SEGW>
-__device__ __forceinline__ void lds_get(const float* buf, float (&v)[M][1 << LOGE], int t, int b) {
+template <int LOGE, int NSEG, int SEGW>
+__device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b) {
   constexpr int E = 1 << LOGE;
+  const float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
   if (b == 0) {
 #pragma unroll
-    for (int a = 0; a < M; ++a)
+    for (int a = 0; a < NSEG; ++a)
 #pragma unroll
       for (int c = 0; c < E / 4; ++c) {
-        const float4 q = *reinterpret_cast<const float4*>(buf + a * SEGW + lds_addr(t * E + 4 * c));
+        const float4 q = *reinterpret_cast<const float4*>(base + a * SEGW + lds_addr(4 * c));
         v[a][4 * c] = q.x;
         v[a][4 * c + 1] = q.y;
         v[a][4 * c + 2] = q.z;
@@ -117,10 +126,19 @@ __device__ __forceinline__ void lds_get(const float* buf, float (&v)[M][1 << LOG
       }
   } else {
 #pragma unroll
-    for (int a = 0; a < M; ++a)
+    for (int a = 0; a < NSEG; ++a)
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[a][e] = buf[a * SEGW + lds_addr(lay<LOGE>(t, e, b))];
+      for (int e = 0; e < E; ++e) v[a][e] = base[a * SEGW + lds_addr(e << b)];
   }
+}
+
+template <int LOGE, int SEGW>
+__device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b) {
+  lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b);
+}
+template <int LOGE, int SEGW>
+__device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b) {
+  lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b);
 }
 
 // Cross-lane max/min over the `gt` consecutive lanes of a quantization group
@@ -226,18 +244,22 @@ __device__ __forceinline__ uint32_t quantize8(const float (&v)[8], int bits, int
   return packed;
 }
 
-// Orders this wave's LDS writes before its later LDS reads (the LDS executes
-// one wave's instructions in order; this keeps the compiler from moving
-// them across each other).
+// Orders this wave's LDS writes before its later LDS reads.  The LDS
+// executes one wave's instructions in issue order, so a read issued after a
+// write sees it without waiting for the write to complete; only the
+// compiler must be kept from moving the accesses across each other.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
 }
 
 // Output / quantizer variants of the row loop, fixed at compile time so the
 // loop carries no mode branches.
-enum QMode : int { Q_NONE = 0, Q_SYM4 = 1, Q_ANY = 2 };
+// Q_S4G128 and Q_A2G128 fix the two common formats (symmetric INT4 and
+// asymmetric INT2, groups of 128) at compile time, so the group reductions
+// are straight-line code the scheduler can interleave with the rotations;
+// Q_ANY reads bits, group and mode at run time.
+enum QMode : int { Q_NONE = 0, Q_S4G128 = 1, Q_A2G128 = 2, Q_ANY = 3 };
 
 // Number of workgroup-wide (non wave-local) transposes in one row.
 template <class S>
@@ -258,7 +280,7 @@ struct Coeffs {
 template <class S, bool XBF16, int YK, int QM>
 __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int team, int t,
                                          const Coeffs<S>& C) {
-  constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, R = S::R, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
+  constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
   constexpr int RPT = S::ROWS_PER_PASS / S::R;
   constexpr int SEGS = S::SEGS, SEGW = S::SEGW, BUFW = S::BUFW, RPP = S::ROWS_PER_PASS;
   constexpr int L = S::L, NPH = S::NPH;
@@ -274,52 +296,40 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
   const int64_t rows = P.rows;
   const int64_t ngrp = (rows + RPP - 1) / RPP;
   const char* xb = reinterpret_cast<const char*>(P.x);
-  const int bits = QM == Q_SYM4 ? 4 : P.bits;
-  const bool asym = QM == Q_ANY && P.asym != 0;
-  const int gt = QUANT ? P.group / E : 1;
-  const int lg_group = QUANT ? 31 - __builtin_clz(P.group) : 0;
+  constexpr bool FIXED = QM == Q_S4G128 || QM == Q_A2G128;
+  const int bits = QM == Q_S4G128 ? 4 : (QM == Q_A2G128 ? 2 : P.bits);
+  const bool asym = QM == Q_A2G128 || (QM == Q_ANY && P.asym != 0);
+  const int group = FIXED ? 128 : P.group;
+  const int gt = QUANT ? group / E : 1;
+  const int lg_group = QUANT ? 31 - __builtin_clz(group) : 0;
   const float top = asym ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
   const float inv_top = 1.0f / top;
-  const int64_t code_row_bytes = (int64_t)N * bits / 8;
   const int ngroups_row = QUANT ? N >> lg_group : 0;
 
-  // Addresses: a row group's base is uniform across the workgroup (scalar
-  // registers); each thread adds a fixed 32-bit offset.  Only the last,
-  // partial group takes the per-row path.
+  // Memory: every row group gets buffer resources covering exactly its valid
+  // rows (bases and sizes uniform across the workgroup, in scalar
+  // registers); each thread adds fixed 32-bit offsets.  Rows past the end,
+  // groups past the end and lanes with nothing to store fall outside the
+  // ranges, so no memory instruction sits under a branch and the compiler
+  // can keep every prefetch in flight.
   constexpr int64_t GRP_ELEMS = (int64_t)RPP * N;
   const int thr_elem = team * RPT * N + t * E;  // element offset of (team, t) in a group
-  auto group_full = [&](int64_t grp) { return grp * RPP + RPP <= rows; };
+  auto valid_rows = [&](int64_t grp) -> int64_t {
+    const int64_t r = rows - grp * RPP;
+    return grp < 0 ? 0 : (r < 0 ? 0 : (r > RPP ? RPP : r));
+  };
 
-  // Input registers of the current row group, refilled with the next
-  // group's rows as soon as they have been unpacked.  In a partial group the
-  // rows past the end read the last row instead (their results are never
-  // stored).
-  uint4 cur[SEGS][RAW];
-  auto load = [&](int64_t grp) {
-    if (group_full(grp)) {
-      const char* base = xb + grp * GRP_ELEMS * ESZ;
+  constexpr int PD = S::PD;
+  uint4 cur[PD][SEGS][RAW];
+  auto load = [&](int64_t grp, int d) {
+    const auto rs = buffer_range(xb + grp * GRP_ELEMS * ESZ, valid_rows(grp) * N * ESZ);
 #pragma unroll
-      for (int rr = 0; rr < RPT; ++rr)
+    for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
-        for (int a = 0; a < M; ++a) {
-          const uint4* src = reinterpret_cast<const uint4*>(base + (thr_elem + rr * N + a * NB) * ESZ);
+      for (int a = 0; a < M; ++a)
 #pragma unroll
-          for (int c = 0; c < RAW; ++c) cur[rr * M + a][c] = src[c];
-        }
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) {
-        int64_t row = (grp * R + team) * RPT + rr;
-        row = row < rows ? row : rows - 1;
-#pragma unroll
-        for (int a = 0; a < M; ++a) {
-          const uint4* src =
-              reinterpret_cast<const uint4*>(xb + ((row * N + a * NB + (int64_t)t * E) * ESZ));
-#pragma unroll
-          for (int c = 0; c < RAW; ++c) cur[rr * M + a][c] = src[c];
-        }
-      }
-    }
+        for (int c = 0; c < RAW; ++c)
+          cur[d][rr * M + a][c] = buf_ld16(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
   };
 
   // bf16 rows, codes and scales of the previous row group, stored only once
@@ -328,63 +338,78 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
   uint32_t held_y[SEGS][E / 2], held_c[SEGS], held_sz[SEGS];
   float vq[SEGS][E];  // the previous group's rotated rows, awaiting quantization
 #pragma unroll
-  for (int sg = 0; sg < SEGS; ++sg)
+  for (int sg = 0; sg < SEGS; ++sg) {
 #pragma unroll
     for (int e = 0; e < E; ++e) vq[sg][e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k) held_y[sg][k] = 0u;
+    held_c[sg] = held_sz[sg] = 0u;
+  }
   int64_t held_grp = -1;
   const bool scale_lane = QUANT && (t & (gt - 1)) == 0;
-  auto store_one = [&](int64_t grp, int rr) {
-    const int64_t row = (grp * R + team) * RPT + rr;
-#pragma unroll
-    for (int a = 0; a < M; ++a) {
-      const int sg = rr * M + a;
-      const int col = a * NB + t * E;
-      if (YK == Y_BF16) {
-        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(P.y) + grp * GRP_ELEMS +
-                                              (thr_elem + rr * N + a * NB));
-#pragma unroll
-        for (int c = 0; c < E / 8; ++c)
-          dst[c] = make_uint4(held_y[sg][4 * c], held_y[sg][4 * c + 1], held_y[sg][4 * c + 2],
-                              held_y[sg][4 * c + 3]);
-      }
-      if (QUANT) {
-        uint8_t* cp = P.codes + grp * (GRP_ELEMS * bits / 8) +
-                      (int)((thr_elem + rr * N + a * NB) * bits / 8);
-        if (bits == 4) *reinterpret_cast<uint32_t*>(cp) = held_c[sg];
-        else *reinterpret_cast<uint16_t*>(cp) = (uint16_t)held_c[sg];
-        if (scale_lane) {
-          const int64_t gi = row * ngroups_row + (col >> lg_group);
-          P.scales[gi] = (uint16_t)held_sz[sg];
-          if (asym) P.zeros[gi] = (uint16_t)(held_sz[sg] >> 16);
-        }
-      }
-    }
-  };
   auto flush = [&]() {
     if (YK != Y_BF16 && !QUANT) return;
-    if (held_grp < 0) return;
-    if (group_full(held_grp)) {
+    const int64_t hg = held_grp;
+    const int64_t vr = valid_rows(hg);
+    const auto ry = buffer_range(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * N * 2);
+    const auto rc = buffer_range(P.codes + hg * (GRP_ELEMS * bits / 8), vr * N * bits / 8);
+    const auto rsc = buffer_range(P.scales + hg * RPP * ngroups_row, vr * ngroups_row * 2);
+    const auto rz = buffer_range(P.zeros + hg * RPP * ngroups_row, vr * ngroups_row * 2);
 #pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) store_one(held_grp, rr);
-    } else {
+    for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < RPT; ++rr)
-        if ((held_grp * R + team) * RPT + rr < rows) store_one(held_grp, rr);
-    }
+      for (int a = 0; a < M; ++a) {
+        const int sg = rr * M + a;
+        const uint32_t el = (uint32_t)(thr_elem + rr * N + a * NB);
+        if (YK == Y_BF16) {
+#pragma unroll
+          for (int c = 0; c < E / 8; ++c)
+            buf_st16(ry, el * 2 + 16 * c,
+                     make_uint4(held_y[sg][4 * c], held_y[sg][4 * c + 1], held_y[sg][4 * c + 2],
+                                held_y[sg][4 * c + 3]));
+        }
+        if (QUANT) {
+          if (bits == 4) buf_st4(rc, el / 2, held_c[sg]);
+          else buf_st2(rc, el / 4, (uint16_t)held_c[sg]);
+          const uint32_t gi = (uint32_t)((team * RPT + rr) * ngroups_row + ((a * NB + t * E) >> lg_group));
+          const uint32_t off = scale_lane ? 2 * gi : kOutOfRange;
+          buf_st2(rsc, off, (uint16_t)held_sz[sg]);
+          if (asym) buf_st2(rz, off, (uint16_t)(held_sz[sg] >> 16));
+        }
+      }
   };
 
-  int64_t grp = blockIdx.x;
-  if (grp < ngrp) load(grp);
-  for (; grp < ngrp; grp += gridDim.x) {
-    const int64_t row0 = (grp * R + team) * RPT;
+  auto store_f32 = [&](int64_t grp, const float (&vv)[SEGS][E]) {
+    const auto ry = buffer_range(reinterpret_cast<const float*>(P.y) + grp * GRP_ELEMS, valid_rows(grp) * N * 4);
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+      for (int a = 0; a < M; ++a) {
+        const int sg = rr * M + a;
+        const uint32_t el = (uint32_t)(thr_elem + rr * N + a * NB);
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c)
+          buf_st16(ry, el * 4 + 16 * c,
+                   make_uint4(__float_as_uint(vv[sg][4 * c]), __float_as_uint(vv[sg][4 * c + 1]),
+                              __float_as_uint(vv[sg][4 * c + 2]), __float_as_uint(vv[sg][4 * c + 3])));
+      }
+  };
 
+  // A 1 x 1 Kronecker factor, read once (no memory operation in the loop
+  // body may sit under a branch).
+  const bool has_mix1 = M == 1 && P.mix != nullptr;
+  const float mix1 = has_mix1 ? P.mix[0] : 1.0f;
+  const int64_t G = gridDim.x;
+  // One row group through the whole path, from prefetch slot d (a
+  // compile-time index once the callers' loops are unrolled).
+  auto slot = [&](const int64_t grp, const int d) __attribute__((always_inline)) {
     float v[SEGS][E];
 #pragma unroll
     for (int sg = 0; sg < SEGS; ++sg) {
       if (XBF16) {
 #pragma unroll
         for (int c = 0; c < RAW; ++c) {
-          const uint32_t w[4] = {cur[sg][c].x, cur[sg][c].y, cur[sg][c].z, cur[sg][c].w};
+          const uint32_t w[4] = {cur[d][sg][c].x, cur[d][sg][c].y, cur[d][sg][c].z, cur[d][sg][c].w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             v[sg][8 * c + 2 * k] = bf16_lo(w[k]);
@@ -394,14 +419,23 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
       } else {
 #pragma unroll
         for (int c = 0; c < RAW; ++c) {
-          v[sg][4 * c] = __uint_as_float(cur[sg][c].x);
-          v[sg][4 * c + 1] = __uint_as_float(cur[sg][c].y);
-          v[sg][4 * c + 2] = __uint_as_float(cur[sg][c].z);
-          v[sg][4 * c + 3] = __uint_as_float(cur[sg][c].w);
+          v[sg][4 * c] = __uint_as_float(cur[d][sg][c].x);
+          v[sg][4 * c + 1] = __uint_as_float(cur[d][sg][c].y);
+          v[sg][4 * c + 2] = __uint_as_float(cur[d][sg][c].z);
+          v[sg][4 * c + 3] = __uint_as_float(cur[d][sg][c].w);
         }
       }
     }
-    if (grp + gridDim.x < ngrp) load(grp + gridDim.x);
+    // Slot d is free once unpacked, and its refill should reuse its
+    // registers.  Pinning the unpacked values here (an empty asm that the
+    // load cannot cross) keeps the refill from being issued while the old
+    // contents are still live, which would cost a register copy, and so a
+    // wait for the refill, at the loop latch.
+#pragma unroll
+    for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+      for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[sg][e])::"memory");
+    load(grp + PD * G, d);  // past the end: an empty range, no traffic
 
     // The previous group's quantization runs here, interleaved with this
     // group's first register phase: the two dependency chains are
@@ -412,45 +446,54 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
       for (int sg = 0; sg < SEGS; ++sg)
         held_c[sg] = quantize8(vq[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
     }
+    // Phase k: [sync for transpose k] -> read every segment -> per segment:
+    // rotate, then write it for transpose k+1.  Segment by segment (kept in
+    // that order by scheduling barriers), the LDS traffic of one segment
+    // overlaps the arithmetic of the next.
     int gidx = 0;  // workgroup transposes so far in this row (compile-time after unrolling)
 #pragma unroll
     for (int k = 0; k <= NPH; ++k) {
-      if (k == 1) flush();  // the previous group's outputs, now complete
-      if (k > 0) {  // transpose from phase k-1 into phase k (k == NPH: back to layout 0)
-        const int bp = phase_base(k - 1, L, LOGE);
+      const bool local_in = k > 0 && S::local_transpose(k);
+      float* const buf_in = local_in ? lbuf : ((gidx & 1) ? gbuf1 : gbuf0);
+      if (k > 0) {
+        if (local_in) wave_lds_sync();
+        else __syncthreads();
         const int b = k < NPH ? phase_base(k, L, LOGE) : 0;
-        if (S::local_transpose(k)) {
-          lds_put<LOGE, SEGS, SEGW>(lbuf, v, t, bp);
-          wave_lds_sync();
-          lds_get<LOGE, SEGS, SEGW>(lbuf, v, t, b);
-          wave_lds_sync();
-        } else {
-          float* buf = (gidx & 1) ? gbuf1 : gbuf0;
-          lds_put<LOGE, SEGS, SEGW>(buf, v, t, bp);
-          __syncthreads();
-          lds_get<LOGE, SEGS, SEGW>(buf, v, t, b);
-          ++gidx;
-        }
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) lds_get1<LOGE, SEGW>(buf_in + sg * SEGW, v[sg], t, b);
+        if (local_in) wave_lds_sync();
+        else ++gidx;
       }
+      if (k == 1) flush();  // the previous group's outputs, now complete
       if (k == NPH) break;
       const int b = phase_base(k, L, LOGE);
       const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
+      const bool local_out = S::local_transpose(k + 1);
+      float* const buf_out = local_out ? lbuf : ((gidx & 1) ? gbuf1 : gbuf0);
 #pragma unroll
-      for (int s = k * LOGE; s < s_end; ++s) {
-        const int q = s - b;
+      for (int sg = 0; sg < SEGS; ++sg) {
 #pragma unroll
-        for (int j = 0; j < E / 2; ++j) {
-          const int lo = pair_lo(j, q), hi = lo | (1 << q);
+        for (int s = k * LOGE; s < s_end; ++s) {
+          const int q = s - b;
 #pragma unroll
-          for (int sg = 0; sg < SEGS; ++sg) {
+          for (int j = 0; j < E / 2; ++j) {
+            const int lo = pair_lo(j, q), hi = lo | (1 << q);
             if (s < L - 1) shear3(v[sg][lo], v[sg][hi], C.p[s][j], C.u[s][j]);
             else last2x2(v[sg][lo], v[sg][hi], C.last[j]);
           }
         }
+        lds_put1<LOGE, SEGW>(buf_out + sg * SEGW, v[sg], t, b);
+        if (SEGS > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    if (M > 1 || P.mix != nullptr) {  // Kronecker mix across a row's segments, column by column
+    if (M == 1 && has_mix1) {  // a 1 x 1 Kronecker factor: a scalar
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[sg][e] *= mix1;
+    }
+    if (M > 1) {  // Kronecker mix across a row's segments, column by column
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
@@ -469,19 +512,7 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
     }
 
     if (YK == Y_F32) {  // fp32 rows are stored right away
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) {
-        const int64_t row = row0 + rr;
-        if (row >= rows) continue;
-#pragma unroll
-        for (int a = 0; a < M; ++a) {
-          float4* dst = reinterpret_cast<float4*>(P.y) + (row * N + a * NB + (int64_t)t * E) / 4;
-          const int sg = rr * M + a;
-#pragma unroll
-          for (int c = 0; c < E / 4; ++c)
-            dst[c] = make_float4(v[sg][4 * c], v[sg][4 * c + 1], v[sg][4 * c + 2], v[sg][4 * c + 3]);
-        }
-      }
+      store_f32(grp, v);
     } else if (YK == Y_BF16) {
 #pragma unroll
       for (int sg = 0; sg < SEGS; ++sg)
@@ -495,7 +526,34 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
         for (int e = 0; e < E; ++e) vq[sg][e] = v[sg][e];
     }
     held_grp = grp;
+  };
+
+  // Row groups g = blockIdx.x + i * gridDim.x, in passes of PD groups so
+  // that prefetch slot d = i mod PD is a compile-time register index.
+  // The prologue issues the same memory operations, in the same order, as a
+  // pass of the main loop (its stores fall in empty ranges and are dropped).
+  // The compiler's wait counts at the loop head merge the prologue with the
+  // latch; with matching sequences, slot d waits for its own load alone.
+#pragma unroll
+  for (int d = 0; d < PD; ++d) {
+    load(blockIdx.x + d * G, d);
+    asm volatile("" ::: "memory");
+    flush();
+    if (YK == Y_F32) store_f32(-1, vq);
+    asm volatile("" ::: "memory");
   }
+  // Main loop: full passes only, so its body has no branch around memory
+  // operations (a conditional slot would make the compiler wait for the
+  // most recent load at every slot).
+  int64_t g0 = blockIdx.x;
+  for (; g0 + (PD - 1) * G < ngrp; g0 += PD * G) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) slot(g0 + d * G, d);
+  }
+  // Tail: the block's last, partial pass.
+#pragma unroll
+  for (int d = 0; d < PD - 1; ++d)
+    if (g0 + d * G < ngrp) slot(g0 + d * G, d);
   if (QUANT) {
 #pragma unroll
     for (int sg = 0; sg < SEGS; ++sg)
@@ -535,13 +593,18 @@ fwd_kernel(FwdParams P) {
   }
 
   const bool quant = P.codes != nullptr;
-  const bool sym4 = quant && P.bits == 4 && P.asym == 0;
+  // The fixed formats need a group of 128 to span whole 16-lane rows.
+  const bool g128 = quant && P.group == 128 && S::T >= 16;
+  const bool s4 = g128 && P.bits == 4 && P.asym == 0;
+  const bool a2 = g128 && P.bits == 2 && P.asym != 0;
   if (P.y_kind == Y_BF16) {
     if (!quant) row_loop<S, XBF16, Y_BF16, Q_NONE>(P, lds, team, t, C);
-    else if (sym4) row_loop<S, XBF16, Y_BF16, Q_SYM4>(P, lds, team, t, C);
+    else if (s4) row_loop<S, XBF16, Y_BF16, Q_S4G128>(P, lds, team, t, C);
+    else if (a2) row_loop<S, XBF16, Y_BF16, Q_A2G128>(P, lds, team, t, C);
     else row_loop<S, XBF16, Y_BF16, Q_ANY>(P, lds, team, t, C);
   } else if (P.y_kind == Y_NONE) {
-    if (sym4) row_loop<S, XBF16, Y_NONE, Q_SYM4>(P, lds, team, t, C);
+    if (s4) row_loop<S, XBF16, Y_NONE, Q_S4G128>(P, lds, team, t, C);
+    else if (a2) row_loop<S, XBF16, Y_NONE, Q_A2G128>(P, lds, team, t, C);
     else row_loop<S, XBF16, Y_NONE, Q_ANY>(P, lds, team, t, C);
   } else {
     if (!quant) row_loop<S, XBF16, Y_F32, Q_NONE>(P, lds, team, t, C);
