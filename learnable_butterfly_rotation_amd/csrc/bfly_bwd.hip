@@ -232,11 +232,12 @@ __global__ void reduce_partials_kernel(const float* __restrict__ partials, float
 }
 
 // One thread per (stage s, pair p).  Besides (cos t, sin t) it writes the
-// three-shear coefficients of stages 0..L-2 and the last stage's 4
-// coefficients.  The sign an element carries before stage s is the parity
-// of the stages s' < s whose angle on that element's pair exceeds pi/2 in
-// magnitude (each such stage negates both of its elements), so every entry
-// is computed independently from the angles.
+// coefficients of both forward forms of its pair.  Everything an element
+// carries into stage s is a function of the angles of its pairs at the
+// stages s' < s: the sign (three-shear form) is the parity of those angles
+// exceeding pi/2 in magnitude (each such stage negates both of its
+// elements), the scale (scaled form) is the product of their cosines.  So
+// every entry is computed independently from the angles.
 __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
   const int half = 1 << (logn - 1);
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -248,18 +249,28 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   const double t = (double)theta[k];
   double sn, cn;
   sincos(t, &sn, &cn);
-  float2* cs = reinterpret_cast<float2*>(table);
-  float2* lift = reinterpret_cast<float2*>(table + (size_t)half * 8 * logn);
-  float4* last = reinterpret_cast<float4*>(table + (size_t)half * 8 * (2 * logn - 1));
+  const Table tab = table_at(table, logn);
+  float2* cs = const_cast<float2*>(tab.cs);
+  float2* fg = const_cast<float2*>(tab.fg);
+  float4* flast = const_cast<float4*>(tab.flast);
+  float2* lift = const_cast<float2*>(tab.lift);
+  float4* last = const_cast<float4*>(tab.last);
   cs[k] = make_float2((float)cn, (float)sn);
-  // all the angle loads are independent: unrolled, they are in flight together
+  // Both elements' histories through stages s2 < s: the sign parity (three-
+  // shear form) and the product of cosines (scaled form).  The angle loads
+  // are independent: unrolled, they are in flight together.
   int par_i = 0, par_j = 0;
+  double sig_i = 1.0, sig_j = 1.0;
 #pragma unroll
   for (int s2 = 0; s2 < 13; ++s2) {
     if (s2 < s) {
+      const double ti = (double)theta[(int64_t)s2 * half + pair_rank(i, s2)];
+      const double tj = (double)theta[(int64_t)s2 * half + pair_rank(j, s2)];
       // the same predicate (in fp64) as the flip decision below
-      par_i ^= fabs((double)theta[(int64_t)s2 * half + pair_rank(i, s2)]) > halfpi;
-      par_j ^= fabs((double)theta[(int64_t)s2 * half + pair_rank(j, s2)]) > halfpi;
+      par_i ^= fabs(ti) > halfpi;
+      par_j ^= fabs(tj) > halfpi;
+      sig_i *= cos(ti);
+      sig_j *= cos(tj);
     }
   }
   if (s < logn - 1) {
@@ -270,9 +281,19 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
     const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
     const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
     lift[k] = make_float2((float)(-eps * (sp / (1.0 + cp))), (float)(eps * sp));
+    // scaled form: usable while every stored value stays within 2^64 of its
+    // true value (|sigma| >= 2^-64 after this stage)
+    const double tn = sn / cn;
+    const double lim = 5.421010862427522e-20;  // 2^-64
+    const bool ok = fabs(cn * sig_i) >= lim && fabs(cn * sig_j) >= lim;
+    const float nan = __uint_as_float(0x7fc00000u);  // a quiet NaN, as bits
+    fg[k] = ok ? make_float2((float)(-tn * (sig_j / sig_i)), (float)(tn * (sig_i / sig_j)))
+               : make_float2(nan, nan);
   } else {
     const double si = par_i ? -1.0 : 1.0, sj = par_j ? -1.0 : 1.0;
     last[p] = make_float4((float)(cn * si), (float)(-sn * sj), (float)(sn * si), (float)(cn * sj));
+    flast[p] = make_float4((float)(cn * sig_i), (float)(-sn * sig_j), (float)(sn * sig_i),
+                           (float)(cn * sig_j));
   }
 }
 

@@ -79,6 +79,20 @@ __device__ __forceinline__ void shear3(float& a, float& b, float p, float u) {
   a = fmaf(p, b, a);
 }
 
+// One of stages 0..L-2 on the pair (a, b): two fused multiply-adds on the
+// stored values in the scaled form (c0 = beta, c1 = gamma), else three
+// shears (c0 = p, c1 = u).
+template <bool FAST>
+__device__ __forceinline__ void rotate(float& a, float& b, float c0, float c1) {
+  if (FAST) {
+    const float a0 = a;
+    a = fmaf(c0, b, a);
+    b = fmaf(c1, a0, b);
+  } else {
+    shear3(a, b, c0, c1);
+  }
+}
+
 // The last stage: (a, b) <- (k.x a + k.y b, k.z a + k.w b).
 __device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
   const float na = fmaf(k.x, a, k.y * b);
@@ -269,17 +283,18 @@ __host__ __device__ constexpr int global_transposes() {
   return g;
 }
 
+// The coefficients of every pair one thread rotates, for either form.
 template <class S>
 struct Coeffs {
-  float p[S::L - 1][S::E / 2];
-  float u[S::L - 1][S::E / 2];
+  float c0[S::L - 1][S::E / 2];
+  float c1[S::L - 1][S::E / 2];
   float4 last[S::E / 2];
 };
 
 // The persistent row loop for one (input, output, quantizer) variant.
-template <class S, bool XBF16, int YK, int QM>
-__device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int team, int t,
-                                         const Coeffs<S>& C) {
+template <class S, bool XBF16, int YK, int QM, bool FAST>
+__device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows, float* lds, int team,
+                                         int t, const Coeffs<S>& C) {
   constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
   constexpr int RPT = S::ROWS_PER_PASS / S::R;
   constexpr int SEGS = S::SEGS, SEGW = S::SEGW, BUFW = S::BUFW, RPP = S::ROWS_PER_PASS;
@@ -293,7 +308,6 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
   float* const gbuf0 = lds + BUFW + team * (SEGS * SEGW);  // workgroup transposes
   float* const gbuf1 = lds + 2 * BUFW + team * (SEGS * SEGW);
 
-  const int64_t rows = P.rows;
   const int64_t ngrp = (rows + RPP - 1) / RPP;
   const char* xb = reinterpret_cast<const char*>(P.x);
   constexpr bool FIXED = QM == Q_S4G128 || QM == Q_A2G128;
@@ -478,7 +492,7 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
 #pragma unroll
           for (int j = 0; j < E / 2; ++j) {
             const int lo = pair_lo(j, q), hi = lo | (1 << q);
-            if (s < L - 1) shear3(v[sg][lo], v[sg][hi], C.p[s][j], C.u[s][j]);
+            if (s < L - 1) rotate<FAST>(v[sg][lo], v[sg][hi], C.c0[s][j], C.c1[s][j]);
             else last2x2(v[sg][lo], v[sg][hi], C.last[j]);
           }
         }
@@ -562,7 +576,10 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, float* lds, int tea
   flush();
 }
 
-template <int LOGNB, int M, int RPT, bool XBF16>
+// One kernel per (input type, output kind, quantizer format): the host picks
+// the variant, so each kernel holds just the two row loops below and the
+// register allocator sees one loop nest at a time.
+template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM>
 __global__ void __launch_bounds__((FwdShape<LOGNB, M, RPT>::NT))
 fwd_kernel(FwdParams P) {
   using S = FwdShape<LOGNB, M, RPT>;
@@ -573,50 +590,52 @@ fwd_kernel(FwdParams P) {
   const int team = tid / T;
   const int t = tid - team * T;
 
-  // Coefficients of every pair this thread rotates, resident for all rows:
-  // stages 0..L-2 as three shears (p, u), the last stage as a 2x2 matrix.
+  // Coefficients of every pair this thread rotates, resident for all rows,
+  // in the scaled form unless the table marks it unusable (a NaN anywhere:
+  // the workgroup covers every pair, so all workgroups decide alike).
   Coeffs<S> C;
+  auto load_coeffs = [&](const float2* st, const float4* lst) {
 #pragma unroll
-  for (int s = 0; s < L; ++s) {
-    const int b = phase_base(s / LOGE, L, LOGE);
+    for (int s = 0; s < L; ++s) {
+      const int b = phase_base(s / LOGE, L, LOGE);
 #pragma unroll
-    for (int j = 0; j < E / 2; ++j) {
-      const int rank = pair_rank(lay<LOGE>(t, pair_lo(j, s - b), b), s);
-      if (s < L - 1) {
-        const float2 c = P.tab.lift[s * (NB / 2) + rank];
-        C.p[s][j] = c.x;
-        C.u[s][j] = c.y;
-      } else {
-        C.last[j] = P.tab.last[rank];
+      for (int j = 0; j < E / 2; ++j) {
+        const int rank = pair_rank(lay<LOGE>(t, pair_lo(j, s - b), b), s);
+        if (s < L - 1) {
+          const float2 c = st[s * (NB / 2) + rank];
+          C.c0[s][j] = c.x;
+          C.c1[s][j] = c.y;
+        } else {
+          C.last[j] = lst[rank];
+        }
       }
     }
-  }
-
-  const bool quant = P.codes != nullptr;
-  // The fixed formats need a group of 128 to span whole 16-lane rows.
-  const bool g128 = quant && P.group == 128 && S::T >= 16;
-  const bool s4 = g128 && P.bits == 4 && P.asym == 0;
-  const bool a2 = g128 && P.bits == 2 && P.asym != 0;
-  if (P.y_kind == Y_BF16) {
-    if (!quant) row_loop<S, XBF16, Y_BF16, Q_NONE>(P, lds, team, t, C);
-    else if (s4) row_loop<S, XBF16, Y_BF16, Q_S4G128>(P, lds, team, t, C);
-    else if (a2) row_loop<S, XBF16, Y_BF16, Q_A2G128>(P, lds, team, t, C);
-    else row_loop<S, XBF16, Y_BF16, Q_ANY>(P, lds, team, t, C);
-  } else if (P.y_kind == Y_NONE) {
-    if (s4) row_loop<S, XBF16, Y_NONE, Q_S4G128>(P, lds, team, t, C);
-    else if (a2) row_loop<S, XBF16, Y_NONE, Q_A2G128>(P, lds, team, t, C);
-    else row_loop<S, XBF16, Y_NONE, Q_ANY>(P, lds, team, t, C);
-  } else {
-    if (!quant) row_loop<S, XBF16, Y_F32, Q_NONE>(P, lds, team, t, C);
-    else row_loop<S, XBF16, Y_F32, Q_ANY>(P, lds, team, t, C);
+  };
+  load_coeffs(P.tab.fg, P.tab.flast);
+  int nan_seen = 0;
+#pragma unroll
+  for (int s = 0; s < L - 1; ++s)
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j)  // bit test: the build assumes no NaN arithmetic
+      nan_seen |= (__float_as_uint(C.c0[s][j]) & 0x7fffffffu) > 0x7f800000u;
+  const bool shear = __builtin_amdgcn_readfirstlane(__syncthreads_or(nan_seen)) != 0;
+  // The two forms run as consecutive loops (the unused one over zero rows),
+  // not as two arms of a branch: the register allocator then never holds
+  // both coefficient sets at once.
+  row_loop<S, XBF16, YK, QM, true>(P, shear ? 0 : P.rows, lds, team, t, C);
+  if (shear) {
+    // Three-shear form, with the general quantizer for every format.
+    load_coeffs(P.tab.lift, P.tab.last);
+    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false>(P, P.rows, lds, team, t, C);
   }
 }
 
-// Host-side launch of one instantiation.
-template <int LOGNB, int M, int RPT, bool XBF16>
-hipError_t launch_fwd_inst(const FwdParams& p, hipStream_t stream) {
+// Host-side launch: pick the variant, size the persistent grid (cached per
+// variant on first use).
+template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM>
+hipError_t launch_fwd_variant(const FwdParams& p, hipStream_t stream) {
   using S = FwdShape<LOGNB, M, RPT>;
-  auto kern = fwd_kernel<LOGNB, M, RPT, XBF16>;
+  auto kern = fwd_kernel<LOGNB, M, RPT, XBF16, YK, QM>;
   static int blocks_per_cu = -1;
   static int num_cu = 0;
   if (blocks_per_cu < 0) {
@@ -637,6 +656,29 @@ hipError_t launch_fwd_inst(const FwdParams& p, hipStream_t stream) {
   const int grid = (int)(ngrp < cap ? ngrp : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, p);
   return hipGetLastError();
+}
+
+template <int LOGNB, int M, int RPT, bool XBF16>
+hipError_t launch_fwd_inst(const FwdParams& p, hipStream_t stream) {
+  using S = FwdShape<LOGNB, M, RPT>;
+  const bool quant = p.codes != nullptr;
+  // The fixed formats need a group of 128 to span whole 16-lane rows.
+  const bool g128 = quant && p.group == 128 && S::T >= 16;
+  const bool s4 = g128 && p.bits == 4 && p.asym == 0;
+  const bool a2 = g128 && p.bits == 2 && p.asym != 0;
+  if (p.y_kind == Y_BF16) {
+    if (!quant) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_BF16, Q_NONE>(p, stream);
+    if (s4) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_BF16, Q_S4G128>(p, stream);
+    if (a2) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_BF16, Q_A2G128>(p, stream);
+    return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_BF16, Q_ANY>(p, stream);
+  }
+  if (p.y_kind == Y_NONE) {
+    if (s4) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_NONE, Q_S4G128>(p, stream);
+    if (a2) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_NONE, Q_A2G128>(p, stream);
+    return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_NONE, Q_ANY>(p, stream);
+  }
+  if (!quant) return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_F32, Q_NONE>(p, stream);
+  return launch_fwd_variant<LOGNB, M, RPT, XBF16, Y_F32, Q_ANY>(p, stream);
 }
 
 }  // namespace bfly

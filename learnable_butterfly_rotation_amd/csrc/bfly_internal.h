@@ -13,25 +13,42 @@ enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 
 // The prepared coefficient table of a butterfly of length n = 2^L, in one
 // device allocation (half = n/2 pairs per stage):
-//   cs   float2 [L][half]     (cos t, sin t) of every angle (backward)
-//   lift float2 [L-1][half]   (p, u) of the three-shear form of stages 0..L-2
-//   last float4 [half]        the last stage with the tracked signs folded in
-// Stages 0..L-2 are applied as x += p y; y += u x; x += p y, which is the
-// Givens rotation by an angle phi with |phi| <= pi/2 (p = -tan(phi/2),
-// u = sin phi).  A rotation by t with |t| > pi/2 equals minus the rotation
-// by t -+ pi; the minus is not applied but tracked as a sign on both
-// elements, and a rotation of sign-carrying elements is again a rotation
-// (by +-t).  The last stage maps the sign-carrying values straight to the
-// true outputs: (y_i, y_j) = (a w_i + b w_j, c w_i + d w_j).
+//   cs    float2 [L][half]    (cos t, sin t) of every angle (backward)
+//   fg    float2 [L-1][half]  (beta, gamma): stages 0..L-2 in scaled form
+//   flast float4 [half]       the last stage with the scales folded in
+//   lift  float2 [L-1][half]  (p, u): stages 0..L-2 as three shears
+//   last  float4 [half]       the last stage with the tracked signs folded in
+//
+// Scaled form (the "fast Givens" rotation): every element carries a scale
+// sigma (1 on input) and the kernel stores w = x / sigma.  A rotation by t of
+// the pair (i, j) becomes two fused multiply-adds on the stored values,
+//   w_i <- w_i + beta w_j,  w_j <- w_j + gamma w_i  (both from the old values)
+// with beta = -tan t * sigma_j / sigma_i, gamma = tan t * sigma_i / sigma_j,
+// after which both scales are multiplied by cos t.  The last stage maps the
+// stored values to the true outputs with the 2x2 matrix
+// (c sigma_i, -s sigma_j, s sigma_i, c sigma_j).  Scales are tracked in fp64
+// when the table is prepared.  Stored magnitudes grow like 1 / |sigma| (for
+// angles drawn uniformly, 1/|sigma| reaches ~2^31 at n = 4096); a pair
+// whose scales would fall below 2^-64 has beta set to NaN, and a forward
+// launch that sees any NaN uses the three-shear form instead.
+//
+// Three-shear form: x += p y; y += u x; x += p y is the Givens rotation by
+// an angle phi with |phi| <= pi/2 (p = -tan(phi/2), u = sin phi).  A
+// rotation by t with |t| > pi/2 equals minus the rotation by t -+ pi; the
+// minus is not applied but tracked as a sign on both elements, and a
+// rotation of sign-carrying elements is again a rotation (by +-t).  The last
+// stage maps the sign-carrying values straight to the true outputs.
 struct Table {
   const float2* cs;
+  const float2* fg;
+  const float4* flast;
   const float2* lift;
   const float4* last;
 };
 
 __host__ __device__ inline size_t table_bytes(int logn) {
   const size_t half = (size_t)1 << (logn - 1);
-  return half * 8 * (size_t)(2 * logn + 1);
+  return half * 8 * (size_t)(3 * logn + 2);
 }
 
 __host__ __device__ inline Table table_at(const void* base, int logn) {
@@ -39,8 +56,10 @@ __host__ __device__ inline Table table_at(const void* base, int logn) {
   const char* b = static_cast<const char*>(base);
   Table t;
   t.cs = reinterpret_cast<const float2*>(b);
-  t.lift = reinterpret_cast<const float2*>(b + half * 8 * logn);
-  t.last = reinterpret_cast<const float4*>(b + half * 8 * (2 * logn - 1));
+  t.fg = reinterpret_cast<const float2*>(b + half * 8 * logn);
+  t.flast = reinterpret_cast<const float4*>(b + half * 8 * (2 * logn - 1));
+  t.lift = reinterpret_cast<const float2*>(b + half * 8 * (2 * logn + 1));
+  t.last = reinterpret_cast<const float4*>(b + half * 8 * (3 * logn));
   return t;
 }
 

@@ -291,6 +291,64 @@ def test_quarter_pi_is_hadamard():
     assert np.abs(host(y) - want).max() < 1e-5
 
 
+def _table_uses_scaled_form(theta, n):
+    """Whether the prepared table keeps the scaled (two-FMA) rotation form.
+    Reads the table's scaled-form coefficient block (after the (cos, sin)
+    block, (log2 n - 1) x n/2 float2) and looks for the NaN marker."""
+    L, half = int(math.log2(n)), n // 2
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare(dev(theta), n, tab)
+    raw = tab.cpu().numpy()
+    fg = raw[half * 8 * L: half * 8 * (2 * L - 1)].view(np.float32)
+    return not np.isnan(fg).any()
+
+
+@pytest.mark.parametrize("n", [256, 4096])
+def test_three_shear_form_for_right_angles(n):
+    """Angles of exactly +-pi/2 (as fp32) on every pair: the scaled form's
+    scales would shrink by ~4e-8 per stage, so the table falls back to the
+    three-shear form; results must still match the oracle."""
+    L = int(math.log2(n))
+    rng = np.random.default_rng(70 + n)
+    th = np.where(rng.random((L, n // 2)) < 0.5, np.float32(math.pi / 2),
+                  np.float32(-math.pi / 2)).astype(np.float32)
+    assert not _table_uses_scaled_form(th, n)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((45, n)).astype(np.float32))
+    out = run_quant(x, th, 4, 128, 0)
+    y64 = oracle.forward(x, th)
+    assert_forward(out["y"], y64, x, n)
+    assert_quant(out, y64, 4, 128, 0)
+    xf = rng.standard_normal((33, n)).astype(np.float32)
+    y = empty(xf.shape, torch.float32)
+    B.bfly_forward(dev(xf), y, theta=dev(th))
+    assert_forward(host(y), oracle.forward(xf, th), xf, n)
+
+
+@pytest.mark.parametrize("n", [256, 4096])
+def test_scaled_form_with_near_right_angles(n):
+    """Two stages of angles 1e-3..3e-3 away from +-pi/2 (scales shrink by
+    ~1e-3 per such stage, still in range): the scaled form stays in use, with
+    coefficients up to ~1e3 times larger; results must match the oracle."""
+    L = int(math.log2(n))
+    rng = np.random.default_rng(80 + n)
+    th = inputs.angles(rng, n)
+    for s in (0, L - 3):
+        off = rng.uniform(1e-3, 3e-3, n // 2) * np.sign(rng.standard_normal(n // 2))
+        th[s] = (np.sign(rng.standard_normal(n // 2)) * (math.pi / 2) + off).astype(np.float32)
+    assert _table_uses_scaled_form(th, n)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((45, n)).astype(np.float32))
+    out = run_quant(x, th, 4, 128, 0)
+    y64 = oracle.forward(x, th)
+    assert_forward(out["y"], y64, x, n)
+    assert_quant(out, y64, 4, 128, 0)
+    out = run_quant(x, th, 2, 128, 1)
+    assert_quant(out, y64, 2, 128, 1)
+    xf = rng.standard_normal((33, n)).astype(np.float32)
+    y = empty(xf.shape, torch.float32)
+    B.bfly_forward(dev(xf), y, theta=dev(th))
+    assert_forward(host(y), oracle.forward(xf, th), xf, n)
+
+
 def test_degenerate_groups():
     """All-zero rows (scale 0 -> codes 0), constant rows in asym mode, and
     values so large that the fp16 scale saturates."""
