@@ -231,6 +231,51 @@ __global__ void reduce_partials_kernel(const float* __restrict__ partials, float
   dtheta[k] = (float)sum;
 }
 
+// sin and cos, in fp64, of an fp32 angle.  Cody and Waite's additive
+// reduction: k = nearest integer to a * 2/pi, r = a - k * pi/2 with pi/2 split
+// as P1 + P2 + P3, where P1 has 30 significant bits, so that k * P1 is exact
+// and (a fp32 argument having at most 24) a - k * P1 is exact too for
+// |k| < 2^20; then the Taylor series of sin and cos on |r| <= pi/4, whose
+// first omitted terms are below 1e-19.  Angles of magnitude 1e6 and beyond
+// (or not finite) take the library routine.
+__device__ __forceinline__ void sincos_of_float(float a, double& sn, double& cn) {
+  const double x = (double)a;
+  if (!(fabs(x) < 1.0e6)) {
+    sincos(x, &sn, &cn);
+    return;
+  }
+  const double P1 = 1.5707963276654482;       // 0x1.921fb548p+0
+  const double P2 = -8.705515695504166e-10;
+  const double P3 = 1.6446256936324258e-26;
+  const double k = rint(x * 0.6366197723675814);  // 2 / pi
+  const double r = ((x - k * P1) - k * P2) - k * P3;
+  const double r2 = r * r;
+  // Horner in r^2 with the coefficients (-1)^m / (2m+1)! and (-1)^m / (2m)!
+  double ps = 2.8114572543455206e-15;                     // 1/17!
+  ps = fma(ps, r2, -7.647163731819816e-13);               // 1/15!
+  ps = fma(ps, r2, 1.6059043836821613e-10);               // 1/13!
+  ps = fma(ps, r2, -2.505210838544172e-08);               // 1/11!
+  ps = fma(ps, r2, 2.7557319223985893e-06);               // 1/9!
+  ps = fma(ps, r2, -0.0001984126984126984);               // 1/7!
+  ps = fma(ps, r2, 0.008333333333333333);                 // 1/5!
+  ps = fma(ps, r2, -0.16666666666666666);                 // 1/3!
+  const double sr = fma(ps * r2, r, r);
+  double pc = -1.5619206968586225e-16;                    // 1/18!
+  pc = fma(pc, r2, 4.779477332387385e-14);                // 1/16!
+  pc = fma(pc, r2, -1.1470745597729725e-11);              // 1/14!
+  pc = fma(pc, r2, 2.08767569878681e-09);                 // 1/12!
+  pc = fma(pc, r2, -2.755731922398589e-07);               // 1/10!
+  pc = fma(pc, r2, 2.48015873015873e-05);                 // 1/8!
+  pc = fma(pc, r2, -0.001388888888888889);                // 1/6!
+  pc = fma(pc, r2, 0.041666666666666664);                 // 1/4!
+  pc = fma(pc, r2, -0.5);                                 // 1/2!
+  const double cr = fma(pc, r2, 1.0);
+  // a = r + k pi/2: rotate (cos r, sin r) by k quarter turns
+  const int q = (int)k & 3;
+  sn = (q == 0) ? sr : (q == 1) ? cr : (q == 2) ? -sr : -cr;
+  cn = (q == 0) ? cr : (q == 1) ? -sr : (q == 2) ? -cr : sr;
+}
+
 // One thread per (stage s, pair p).  Besides (cos t, sin t) it writes the
 // coefficients of both forward forms of its pair.  Everything an element
 // carries into stage s is a function of the angles of its pairs at the
@@ -238,9 +283,18 @@ __global__ void reduce_partials_kernel(const float* __restrict__ partials, float
 // exceeding pi/2 in magnitude (each such stage negates both of its
 // elements), the scale (scaled form) is the product of their cosines.  So
 // every entry is computed independently from the angles.
+//
+// Eight consecutive lanes share one (s, p): lane q takes the earlier stages
+// s2 = q and q + 8, and the partial histories are combined across the eight
+// lanes, which cuts the chain of fp64 sines and cosines per lane to two.
+constexpr int PREP_LANES = 8;
+
 __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
   const int half = 1 << (logn - 1);
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = (int)(gid % PREP_LANES);
+  const int64_t k = gid / PREP_LANES;
+  // a pair's lanes leave together (the reductions below need all of them)
   if (k >= (int64_t)logn * half) return;
   const int s = (int)(k / half), p = (int)(k % half);
   const int i = ((p >> s) << (s + 1)) | (p & ((1 << s) - 1));  // lower element of the pair
@@ -248,35 +302,58 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   const double halfpi = 1.5707963267948966;
   const double t = (double)theta[k];
   double sn, cn;
-  sincos(t, &sn, &cn);
+  sincos_of_float(theta[k], sn, cn);
   const Table tab = table_at(table, logn);
   float2* cs = const_cast<float2*>(tab.cs);
   float2* fg = const_cast<float2*>(tab.fg);
   float4* flast = const_cast<float4*>(tab.flast);
   float2* lift = const_cast<float2*>(tab.lift);
   float4* last = const_cast<float4*>(tab.last);
-  cs[k] = make_float2((float)cn, (float)sn);
   // Both elements' histories through stages s2 < s: the sign parity (three-
-  // shear form) and the product of cosines (scaled form).  The angle loads
-  // are independent: unrolled, they are in flight together.
+  // shear form) and the product of cosines (scaled form), this lane's share
+  // first.  The angle loads are unconditional (a stage not before s reads
+  // the pair's own angle, unused), so all of them are in flight together.
+  constexpr int SMAX = 12;  // stages of the largest butterfly
+  constexpr int PER = (SMAX + PREP_LANES - 1) / PREP_LANES;
+  float ti[PER], tj[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int s2 = q + PREP_LANES * m;
+    ti[m] = theta[s2 < s ? (int64_t)s2 * half + pair_rank(i, s2) : k];
+    tj[m] = theta[s2 < s ? (int64_t)s2 * half + pair_rank(j, s2) : k];
+  }
   int par_i = 0, par_j = 0;
   double sig_i = 1.0, sig_j = 1.0;
 #pragma unroll
-  for (int s2 = 0; s2 < 13; ++s2) {
-    if (s2 < s) {
-      const double ti = (double)theta[(int64_t)s2 * half + pair_rank(i, s2)];
-      const double tj = (double)theta[(int64_t)s2 * half + pair_rank(j, s2)];
+  for (int m = 0; m < PER; ++m) {
+    if (q + PREP_LANES * m < s) {
       // the same predicate (in fp64) as the flip decision below
-      par_i ^= fabs(ti) > halfpi;
-      par_j ^= fabs(tj) > halfpi;
-      sig_i *= cos(ti);
-      sig_j *= cos(tj);
+      par_i ^= fabs((double)ti[m]) > halfpi;
+      par_j ^= fabs((double)tj[m]) > halfpi;
+      double si2, ci2, sj2, cj2;
+      sincos_of_float(ti[m], si2, ci2);
+      sincos_of_float(tj[m], sj2, cj2);
+      sig_i *= ci2;
+      sig_j *= cj2;
     }
   }
+  // combine the lanes (products and parities are order independent up to
+  // rounding; every lane ends with the same values, taken in the same order)
+#pragma unroll
+  for (int d = 1; d < PREP_LANES; d <<= 1) {
+    const double oi = __shfl_xor(sig_i, d, PREP_LANES);
+    const double oj = __shfl_xor(sig_j, d, PREP_LANES);
+    sig_i = (q & d) ? oi * sig_i : sig_i * oi;
+    sig_j = (q & d) ? oj * sig_j : sig_j * oj;
+    par_i ^= __shfl_xor(par_i, d, PREP_LANES);
+    par_j ^= __shfl_xor(par_j, d, PREP_LANES);
+  }
+  if (q != 0) return;  // one lane per pair writes
+  cs[k] = make_float2((float)cn, (float)sn);
   if (s < logn - 1) {
     // phi = t or t -+ pi (|phi| <= pi/2): sin and cos of phi are +-sin t and
     // +-cos t, and tan(phi/2) = sin(phi) / (1 + cos(phi)), whose denominator
-    // lies in [1, 2] -- one fp64 sincos serves every coefficient.
+    // lies in [1, 2] -- one sin and cos serve every coefficient.
     const bool flip = fabs(t) > halfpi;
     const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
     const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
@@ -299,7 +376,7 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
 
 hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s) {
   const int threads = 64;  // small blocks spread the angles over every CU
-  const int64_t count = (int64_t)logn << (logn - 1);
+  const int64_t count = ((int64_t)logn << (logn - 1)) * PREP_LANES;
   const int64_t blocks = (count + threads - 1) / threads;
   hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, theta,
                      static_cast<char*>(table), logn);
