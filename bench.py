@@ -230,17 +230,20 @@ def bench_secondary(args, torch, B, inputs):
         w = inputs.weight_int2()
         th = to_dev(w["theta"], torch)
         tab = torch.empty(B.bfly_coeff_bytes(4096), dtype=torch.uint8, device="cuda")
-        mats = []
-        for k in ("w1", "w2"):
-            xw = to_dev(w[k], torch)
-            r = xw.shape[0]
-            mats.append((xw, torch.empty_like(xw), torch.empty((r, 1024), dtype=torch.uint8, device="cuda"),
-                         torch.empty((r, 32), dtype=torch.float16, device="cuda"),
-                         torch.empty((r, 32), dtype=torch.float16, device="cuda")))
+        sets = []  # 3 sets of both matrices (765 MB): no step finds its rows in cache
+        for _ in range(3):
+            mats = []
+            for k in ("w1", "w2"):
+                xw = to_dev(w[k], torch)
+                r = xw.shape[0]
+                mats.append((xw, torch.empty_like(xw), torch.empty((r, 1024), dtype=torch.uint8, device="cuda"),
+                             torch.empty((r, 32), dtype=torch.float16, device="cuda"),
+                             torch.empty((r, 32), dtype=torch.float16, device="cuda")))
+            sets.append(mats)
 
         def fn(i):
             B.bfly_prepare(th, 4096, tab)
-            for xw, yw, c, s, z in mats:
+            for xw, yw, c, s, z in sets[i % 3]:
                 B.bfly_forward_quant(xw, yw, c, s, z, coeffs=tab, bits=2, group=128, mode=1)
         t = time_loop(torch, fn, args.steps, args.warmup)
         rows = 4096 + 11008
@@ -248,14 +251,17 @@ def bench_secondary(args, torch, B, inputs):
         res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t)
     elif name == "kron_n5120_bf16_int4":
         w = inputs.kron_int4()
-        x, th, mix = to_dev(w["x"], torch), to_dev(w["theta_b"], torch), to_dev(w["mix"], torch)
-        rows = x.shape[0]
-        y = torch.empty_like(x)
-        c = torch.empty((rows, 2560), dtype=torch.uint8, device="cuda")
-        s = torch.empty((rows, 40), dtype=torch.float16, device="cuda")
+        th, mix = to_dev(w["theta_b"], torch), to_dev(w["mix"], torch)
+        rows = w["x"].shape[0]
+        sets = []  # 4 sets (720 MB): no step finds its rows in cache
+        for _ in range(4):
+            x = to_dev(w["x"], torch)
+            sets.append((x, torch.empty_like(x), torch.empty((rows, 2560), dtype=torch.uint8, device="cuda"),
+                         torch.empty((rows, 40), dtype=torch.float16, device="cuda")))
         tab = torch.empty(B.bfly_coeff_bytes(1024), dtype=torch.uint8, device="cuda")
 
         def fn(i):
+            x, y, c, s = sets[i % 4]
             B.bfly_prepare(th, 1024, tab)
             B.bfly_kron_forward(x, y, mix, c, s, coeffs_b=tab, bits=4, group=128)
         t = time_loop(torch, fn, args.steps, args.warmup)

@@ -25,15 +25,31 @@ struct BwdShape {
   static constexpr int E = 1 << LOGE;
   static constexpr int N = 1 << LOGN;
   static constexpr int T = N >> LOGE;
+  static constexpr int LOGT = LOGN - LOGE;
   static constexpr int R = (256 / T) > 0 ? (256 / T) : 1;
   static constexpr int NT = T * R;
   static constexpr int L = LOGN;
   static constexpr int NPH = (L + LOGE - 1) / LOGE;
-  // two buffers (double-buffered) of v and g for each of the R rows
   static constexpr int W = lds_words(N);  // padded LDS words per row
-  static constexpr size_t LDS_BYTES = 2ull * 2 * R * W * sizeof(float);
+  // Transpose into phase k (k >= 1) from phase k - 1, and back.
+  static constexpr bool local_transpose(int k) {
+    return wave_local(phase_base(k - 1, L, LOGE), phase_base(k, L, LOGE), LOGT);
+  }
+  // Buffers per team: v and g for wave-local transposes; v for the forward
+  // workgroup transposes; v and g for the reverse workgroup transposes.
+  // Within a row the forward and the reverse workgroup transposes use
+  // different buffers, so one barrier per transpose orders every reuse.
+  static constexpr int global_transposes() {
+    int c = 0;
+    for (int k = 1; k < NPH; ++k) c += local_transpose(k) ? 0 : 1;
+    return c;
+  }
+  static_assert(global_transposes() <= 1, "one buffer per direction assumes one workgroup transpose");
+  static constexpr int NBUF = 5;
+  static constexpr size_t LDS_BYTES = (size_t)NBUF * R * W * sizeof(float);
 };
 
+// Rotation by t (forward) and by -t (transpose), given (cos t, sin t).
 __device__ __forceinline__ void givens_t(float& a, float& b, float c, float s) {
   const float na = fmaf(c, a, s * b);
   const float nb = fmaf(-s, a, c * b);
@@ -48,38 +64,6 @@ __device__ __forceinline__ void givens_f(float& a, float& b, float c, float s) {
   b = nb;
 }
 
-template <int LOGE>
-__device__ __forceinline__ void put(float* buf, const float (&v)[1 << LOGE], int t, int b) {
-  constexpr int E = 1 << LOGE;
-  if (b == 0) {
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c)
-      *reinterpret_cast<float4*>(buf + lds_addr(t * E + 4 * c)) =
-          make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) buf[lds_addr(lay<LOGE>(t, e, b))] = v[e];
-  }
-}
-
-template <int LOGE>
-__device__ __forceinline__ void get(const float* buf, float (&v)[1 << LOGE], int t, int b) {
-  constexpr int E = 1 << LOGE;
-  if (b == 0) {
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-      const float4 q = *reinterpret_cast<const float4*>(buf + lds_addr(t * E + 4 * c));
-      v[4 * c] = q.x;
-      v[4 * c + 1] = q.y;
-      v[4 * c + 2] = q.z;
-      v[4 * c + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = buf[lds_addr(lay<LOGE>(t, e, b))];
-  }
-}
-
 template <int LOGN>
 __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   using S = BwdShape<LOGN>;
@@ -87,11 +71,16 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   constexpr int NPH = S::NPH, W = S::W;
   constexpr int BL = phase_base(NPH - 1, L, LOGE);  // layout of the last phase
   extern __shared__ float4 lds_raw[];
-  float* lds = reinterpret_cast<float*>(lds_raw);
+  float* const lds = reinterpret_cast<float*>(lds_raw);
 
   const int tid = threadIdx.x;
   const int team = tid / T;
   const int t = tid - team * T;
+  float* const lbuf_v = lds + (0 * R + team) * W;
+  float* const lbuf_g = lds + (1 * R + team) * W;
+  float* const fbuf_v = lds + (2 * R + team) * W;
+  float* const rbuf_v = lds + (3 * R + team) * W;
+  float* const rbuf_g = lds + (4 * R + team) * W;
 
   float cc[L][E / 2], ss[L][E / 2], acc[L][E / 2];
 #pragma unroll
@@ -107,54 +96,66 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
     }
   }
 
+  // Memory through buffer resources whose range is exactly the row (empty
+  // past the last row: loads give zeros, which add nothing to the angle
+  // gradients, and stores are dropped), so no memory operation is under a
+  // branch.  x and dX move in the load layout (16-byte vectors), g and y in
+  // the last phase's layout (4-byte words, 256 contiguous bytes per wave).
   const int64_t rows = P.rows;
   const int64_t ngrp = (rows + R - 1) / R;
-  // Input registers of the current row; refilled with the next row as soon
-  // as they have been copied out (zeros past the end, which contribute
-  // nothing to the angle gradients).
-  float4 xc[E / 4];
-  float gc[E];
-  auto load = [&](int64_t grp, float4 (&xd)[E / 4], float (&gd)[E]) {
+  const uint32_t off0 = (uint32_t)(t * E) * 4;
+  const uint32_t offl = (uint32_t)lay<LOGE>(t, 0, BL) * 4;
+  auto row_bytes = [&](int64_t grp) -> int64_t {
     const int64_t row = grp * R + team;
-    const bool ok = row < rows;
-    const float4* xs = reinterpret_cast<const float4*>(P.x + (ok ? row : 0) * N + (int64_t)t * E);
+    return (grp < ngrp && row < rows) ? (int64_t)N * 4 : 0;
+  };
+  uint4 xc[E / 4];
+  uint32_t gc[E];
+  auto load = [&](int64_t grp) {
+    const int64_t row = grp * R + team;
+    const auto rx = buffer_range(P.x + row * N, row_bytes(grp));
+    const auto rg = buffer_range(P.g + row * N, row_bytes(grp));
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c) xd[c] = ok ? xs[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* gs = P.g + (ok ? row : 0) * N;
+    for (int c = 0; c < E / 4; ++c) xc[c] = buf_ld16(rx, off0 + 16 * c);
 #pragma unroll
-    for (int e = 0; e < E; ++e) gd[e] = ok ? gs[lay<LOGE>(t, e, BL)] : 0.f;
+    for (int e = 0; e < E; ++e) gc[e] = buf_ld4(rg, offl + ((uint32_t)e << BL) * 4);
   };
 
-  int64_t grp = blockIdx.x;
-  if (grp < ngrp) load(grp, xc, gc);
-  int bufsel = 0;
-  for (; grp < ngrp; grp += gridDim.x) {
-    const int64_t gnext = grp + gridDim.x;
+  load(blockIdx.x);
+  for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
     const int64_t row = grp * R + team;
-    const bool valid = row < rows;
-
     float v[E], g[E];
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
-      v[4 * c] = xc[c].x;
-      v[4 * c + 1] = xc[c].y;
-      v[4 * c + 2] = xc[c].z;
-      v[4 * c + 3] = xc[c].w;
+      v[4 * c] = __uint_as_float(xc[c].x);
+      v[4 * c + 1] = __uint_as_float(xc[c].y);
+      v[4 * c + 2] = __uint_as_float(xc[c].z);
+      v[4 * c + 3] = __uint_as_float(xc[c].w);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) g[e] = gc[e];
-    if (gnext < ngrp) load(gnext, xc, gc);
+    for (int e = 0; e < E; ++e) g[e] = __uint_as_float(gc[e]);
+    // the registers are free once copied: pin the copies so the refill is
+    // issued after them and reuses the registers
+#pragma unroll
+    for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[e]), "+v"(g[e])::"memory");
+    load(grp + gridDim.x);
 
-    // forward
+    // forward: v = Q x, ending in the last phase's layout
 #pragma unroll
     for (int k = 0; k < NPH; ++k) {
       const int b = phase_base(k, L, LOGE);
       if (k > 0) {
-        float* buf = lds + (size_t)((bufsel * 2) * R + team) * W;
-        put<LOGE>(buf, v, t, phase_base(k - 1, L, LOGE));
-        __syncthreads();
-        get<LOGE>(buf, v, t, b);
-        bufsel ^= 1;
+        const int bp = phase_base(k - 1, L, LOGE);
+        if (S::local_transpose(k)) {
+          lds_put1<LOGE, W>(lbuf_v, v, t, bp);
+          wave_lds_sync();
+          lds_get1<LOGE, W>(lbuf_v, v, t, b);
+          wave_lds_sync();
+        } else {
+          lds_put1<LOGE, W>(fbuf_v, v, t, bp);
+          __syncthreads();
+          lds_get1<LOGE, W>(fbuf_v, v, t, b);
+        }
       }
       const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
 #pragma unroll
@@ -167,13 +168,14 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
         }
       }
     }
-    if (valid && P.y != nullptr) {
-      float* yr = P.y + row * N;
+    if (P.y != nullptr) {
+      const auto ry = buffer_range(P.y + row * N, row_bytes(grp));
 #pragma unroll
-      for (int e = 0; e < E; ++e) yr[lay<LOGE>(t, e, BL)] = v[e];
+      for (int e = 0; e < E; ++e) buf_st4(ry, offl + ((uint32_t)e << BL) * 4, __float_as_uint(v[e]));
     }
 
-    // reverse sweep
+    // reverse sweep: for each stage from the last, accumulate the angle
+    // gradient, then undo the stage on v and apply its transpose to g
 #pragma unroll
     for (int k = NPH - 1; k >= 0; --k) {
       const int b = phase_base(k, L, LOGE);
@@ -191,23 +193,28 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
         }
       }
       if (k > 0) {
-        float* bv = lds + (size_t)((bufsel * 2) * R + team) * W;
-        float* bg = lds + (size_t)((bufsel * 2 + 1) * R + team) * W;
         const int bp = phase_base(k - 1, L, LOGE);
-        put<LOGE>(bv, v, t, b);
-        put<LOGE>(bg, g, t, b);
-        __syncthreads();
-        get<LOGE>(bv, v, t, bp);
-        get<LOGE>(bg, g, t, bp);
-        bufsel ^= 1;
+        if (S::local_transpose(k)) {
+          lds_put1<LOGE, W>(lbuf_v, v, t, b);
+          lds_put1<LOGE, W>(lbuf_g, g, t, b);
+          wave_lds_sync();
+          lds_get1<LOGE, W>(lbuf_v, v, t, bp);
+          lds_get1<LOGE, W>(lbuf_g, g, t, bp);
+          wave_lds_sync();
+        } else {
+          lds_put1<LOGE, W>(rbuf_v, v, t, b);
+          lds_put1<LOGE, W>(rbuf_g, g, t, b);
+          __syncthreads();
+          lds_get1<LOGE, W>(rbuf_v, v, t, bp);
+          lds_get1<LOGE, W>(rbuf_g, g, t, bp);
+        }
       }
     }
-    if (valid) {
-      float4* dst = reinterpret_cast<float4*>(P.dx + row * N + (int64_t)t * E);
+    const auto rd = buffer_range(P.dx + row * N, row_bytes(grp));
 #pragma unroll
-      for (int c = 0; c < E / 4; ++c)
-        dst[c] = make_float4(g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3]);
-    }
+    for (int c = 0; c < E / 4; ++c)
+      buf_st16(rd, off0 + 16 * c, make_uint4(__float_as_uint(g[4 * c]), __float_as_uint(g[4 * c + 1]),
+                                             __float_as_uint(g[4 * c + 2]), __float_as_uint(g[4 * c + 3])));
   }
 
   float* part = P.partials + ((int64_t)blockIdx.x * R + team) * (L * (N / 2));

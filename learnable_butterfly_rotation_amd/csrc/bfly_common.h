@@ -75,6 +75,9 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
@@ -93,6 +96,82 @@ inline hipError_t allow_lds(const void* kernel, size_t bytes) {
   if (e != hipSuccess) return e;
   if ((size_t)maxb < bytes) return hipErrorInvalidConfiguration;
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Whether the transpose from register layout b0 to b1 keeps every element
+// inside its wavefront.  Thread bit j carries index bit j (j < b) or j + LOGE
+// (j >= b); when each wave-index bit (thread bits 6 .. logt-1) carries the
+// same index bit in both layouts, no data crosses a wave and a wave-level
+// ordering suffices instead of a workgroup barrier.
+__host__ __device__ constexpr bool wave_local(int b0, int b1, int logt) {
+  for (int j = 6; j < logt; ++j)
+    if ((j < b0) != (j < b1)) return false;
+  return true;
+}
+
+__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
+// Write / read registers in layout b to / from an LDS row buffer.  lds_addr
+// is additive over disjoint index bits, so the address of register e is the
+// thread's base for the layout plus a compile-time offset for e.
+template <int LOGE, int NSEG, int SEGW>
+__device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b) {
+  constexpr int E = 1 << LOGE;
+  float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
+  if (b == 0) {
+#pragma unroll
+    for (int a = 0; a < NSEG; ++a)
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c)
+        *reinterpret_cast<float4*>(base + a * SEGW + lds_addr(4 * c)) =
+            make_float4(v[a][4 * c], v[a][4 * c + 1], v[a][4 * c + 2], v[a][4 * c + 3]);
+  } else {
+#pragma unroll
+    for (int a = 0; a < NSEG; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) base[a * SEGW + lds_addr(e << b)] = v[a][e];
+  }
+}
+
+template <int LOGE, int NSEG, int SEGW>
+__device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b) {
+  constexpr int E = 1 << LOGE;
+  const float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
+  if (b == 0) {
+#pragma unroll
+    for (int a = 0; a < NSEG; ++a)
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        const float4 q = *reinterpret_cast<const float4*>(base + a * SEGW + lds_addr(4 * c));
+        v[a][4 * c] = q.x;
+        v[a][4 * c + 1] = q.y;
+        v[a][4 * c + 2] = q.z;
+        v[a][4 * c + 3] = q.w;
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < NSEG; ++a)
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[a][e] = base[a * SEGW + lds_addr(e << b)];
+  }
+}
+
+template <int LOGE, int SEGW>
+__device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b) {
+  lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b);
+}
+template <int LOGE, int SEGW>
+__device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b) {
+  lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b);
+}
+
+// Orders this wave's LDS writes before its later LDS reads.  The LDS
+// executes one wave's instructions in issue order, so a read issued after a
+// write sees it without waiting for the write to complete; only the
+// compiler must be kept from moving the accesses across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace bfly

@@ -20,19 +20,6 @@
 
 namespace bfly {
 
-// Whether the transpose from register layout b0 to b1 keeps every element
-// inside its wavefront.  Thread bit j carries index bit j (j < b) or j + LOGE
-// (j >= b); when each wave-index bit (thread bits 6 .. logt-1) carries the
-// same index bit in both layouts, no data crosses a wave and a wave-level
-// ordering suffices instead of a workgroup barrier.
-__host__ __device__ constexpr bool wave_local(int b0, int b1, int logt) {
-  for (int j = 6; j < logt; ++j)
-    if ((j < b0) != (j < b1)) return false;
-  return true;
-}
-
-__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
-
 // RPT rows per thread: the same (cos, sin) registers serve RPT rows at once,
 // halving the barriers and coefficient traffic per row and doubling the
 // independent work between barriers.
@@ -99,60 +86,6 @@ __device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
   const float nb = fmaf(k.z, a, k.w * b);
   a = na;
   b = nb;
-}
-
-// Write / read registers in layout b to / from an LDS row buffer.  lds_addr
-// is additive over disjoint index bits, so the address of register e is the
-// thread's base for the layout plus a compile-time offset for e.
-template <int LOGE, int NSEG, int SEGW>
-__device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b) {
-  constexpr int E = 1 << LOGE;
-  float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
-  if (b == 0) {
-#pragma unroll
-    for (int a = 0; a < NSEG; ++a)
-#pragma unroll
-      for (int c = 0; c < E / 4; ++c)
-        *reinterpret_cast<float4*>(base + a * SEGW + lds_addr(4 * c)) =
-            make_float4(v[a][4 * c], v[a][4 * c + 1], v[a][4 * c + 2], v[a][4 * c + 3]);
-  } else {
-#pragma unroll
-    for (int a = 0; a < NSEG; ++a)
-#pragma unroll
-      for (int e = 0; e < E; ++e) base[a * SEGW + lds_addr(e << b)] = v[a][e];
-  }
-}
-
-template <int LOGE, int NSEG, int SEGW>
-__device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b) {
-  constexpr int E = 1 << LOGE;
-  const float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
-  if (b == 0) {
-#pragma unroll
-    for (int a = 0; a < NSEG; ++a)
-#pragma unroll
-      for (int c = 0; c < E / 4; ++c) {
-        const float4 q = *reinterpret_cast<const float4*>(base + a * SEGW + lds_addr(4 * c));
-        v[a][4 * c] = q.x;
-        v[a][4 * c + 1] = q.y;
-        v[a][4 * c + 2] = q.z;
-        v[a][4 * c + 3] = q.w;
-      }
-  } else {
-#pragma unroll
-    for (int a = 0; a < NSEG; ++a)
-#pragma unroll
-      for (int e = 0; e < E; ++e) v[a][e] = base[a * SEGW + lds_addr(e << b)];
-  }
-}
-
-template <int LOGE, int SEGW>
-__device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b) {
-  lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b);
-}
-template <int LOGE, int SEGW>
-__device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b) {
-  lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b);
 }
 
 // Cross-lane max/min over the `gt` consecutive lanes of a quantization group
@@ -256,15 +189,6 @@ __device__ __forceinline__ uint32_t quantize8(const float (&v)[8], int bits, int
     }
   }
   return packed;
-}
-
-// Orders this wave's LDS writes before its later LDS reads.  The LDS
-// executes one wave's instructions in issue order, so a read issued after a
-// write sees it without waiting for the write to complete; only the
-// compiler must be kept from moving the accesses across each other.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Output / quantizer variants of the row loop, fixed at compile time so the
