@@ -12,9 +12,10 @@
 //   g = Q^T dL/dY = dL/dX in the load/store layout.  Each thread keeps one
 //   fp32 accumulator per pair it owns across all rows of its workgroup and
 //   writes them to the workgroup's slot of the partials buffer at the end.
-// Pass 2: dtheta[k] = sum over slots of partials[slot][k], slot order fixed,
-// accumulated in fp64 -- the result is bit-identical from run to run and
-// independent of the device (the slot count depends only on rows and n).
+// Pass 2: dtheta[k] = sum over slots of partials[slot][k] in fp64, in an
+// order fixed by the slot count alone -- the result is bit-identical from
+// run to run and independent of the device (the slot count depends only on
+// rows and n).
 #include "bfly_common.h"
 
 namespace bfly {
@@ -229,13 +230,29 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   }
 }
 
-__global__ void reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ dtheta,
-                                       int nslots, int count) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= count) return;
+// Pass 2.  A block covers 32 consecutive angles with 8 lanes each: lane q
+// sums slots q, q + 8, q + 16, ... in that order (fp64), then lane 0 adds
+// the eight sums in order q = 0 .. 7.  The order depends only on the slot
+// count, so the result is bit-identical from run to run.
+constexpr int RED_PARTS = 8, RED_COLS = 32;
+
+__global__ void __launch_bounds__(RED_PARTS * RED_COLS)
+reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ dtheta, int nslots,
+                       int count) {
+  __shared__ double part[RED_PARTS][RED_COLS];
+  const int c = threadIdx.x % RED_COLS, q = threadIdx.x / RED_COLS;
+  const int k = blockIdx.x * RED_COLS + c;
   double sum = 0.0;
-  for (int sl = 0; sl < nslots; ++sl) sum += (double)partials[(int64_t)sl * count + k];
-  dtheta[k] = (float)sum;
+  if (k < count)
+    for (int sl = q; sl < nslots; sl += RED_PARTS) sum += (double)partials[(int64_t)sl * count + k];
+  part[q][c] = sum;
+  __syncthreads();
+  if (q == 0 && k < count) {
+    double tot = part[0][c];
+#pragma unroll
+    for (int r = 1; r < RED_PARTS; ++r) tot += part[r][c];
+    dtheta[k] = (float)tot;
+  }
 }
 
 // sin and cos, in fp64, of an fp32 angle.  Cody and Waite's additive
@@ -394,7 +411,9 @@ int backward_blocks(int64_t rows, int logn) {
   const int T = (1 << logn) >> 3;
   const int R = (256 / T) > 0 ? (256 / T) : 1;
   const int64_t ngrp = (rows + R - 1) / R;
-  const int64_t cap = 1024;
+  // one workgroup per CU at n = 4096 (512 threads), two of 256 threads
+  // below; a constant of the shape, never of the device
+  const int64_t cap = T >= 512 ? 256 : 512;
   return (int)(ngrp < cap ? (ngrp > 0 ? ngrp : 1) : cap);
 }
 
@@ -410,8 +429,8 @@ static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t
   }
   const int count = S::L * (S::N / 2);
   const int nslots = p.nblk * S::R;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((count + 255) / 256), dim3(256), 0, s,
-                     p.partials, dtheta, nslots, count);
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((count + RED_COLS - 1) / RED_COLS),
+                     dim3(RED_PARTS * RED_COLS), 0, s, p.partials, dtheta, nslots, count);
   return hipGetLastError();
 }
 
