@@ -153,9 +153,10 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
           lds_get1<LOGE, W>(lbuf_v, v, t, b);
           wave_lds_sync();
         } else {
-          lds_put1<LOGE, W>(fbuf_v, v, t, bp);
+          const bool id = same_lane_bits(bp, b);
+          lds_put1<LOGE, W>(fbuf_v, v, t, bp, id);
           __syncthreads();
-          lds_get1<LOGE, W>(fbuf_v, v, t, b);
+          lds_get1<LOGE, W>(fbuf_v, v, t, b, id);
         }
       }
       const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
@@ -203,11 +204,12 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
           lds_get1<LOGE, W>(lbuf_g, g, t, bp);
           wave_lds_sync();
         } else {
-          lds_put1<LOGE, W>(rbuf_v, v, t, b);
-          lds_put1<LOGE, W>(rbuf_g, g, t, b);
+          const bool id = same_lane_bits(b, bp);
+          lds_put1<LOGE, W>(rbuf_v, v, t, b, id);
+          lds_put1<LOGE, W>(rbuf_g, g, t, b, id);
           __syncthreads();
-          lds_get1<LOGE, W>(rbuf_v, v, t, bp);
-          lds_get1<LOGE, W>(rbuf_g, g, t, bp);
+          lds_get1<LOGE, W>(rbuf_v, v, t, bp, id);
+          lds_get1<LOGE, W>(rbuf_g, g, t, bp, id);
         }
       }
     }

@@ -114,35 +114,45 @@ __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c
 // Write / read registers in layout b to / from an LDS row buffer.  lds_addr
 // is additive over disjoint index bits, so the address of register e is the
 // thread's base for the layout plus a compile-time offset for e.
+//
+// `id` selects unpadded addressing (word = index), for transposes in which
+// every lane keeps the same low 6 index bits on both sides: each access of
+// one register then covers 64 consecutive words (no bank conflicts), and
+// registers lie multiples of 64 words apart, so the compiler pairs them
+// into ds_read2st64 / ds_write2st64, twice the words per instruction.
+__device__ __forceinline__ int lds_index(int i, bool id) { return id ? i : lds_addr(i); }
+
 template <int LOGE, int NSEG, int SEGW>
-__device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b) {
+__device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b,
+                                        bool id = false) {
   constexpr int E = 1 << LOGE;
-  float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
+  float* const base = buf + lds_index(lay<LOGE>(t, 0, b), id);
   if (b == 0) {
 #pragma unroll
     for (int a = 0; a < NSEG; ++a)
 #pragma unroll
       for (int c = 0; c < E / 4; ++c)
-        *reinterpret_cast<float4*>(base + a * SEGW + lds_addr(4 * c)) =
+        *reinterpret_cast<float4*>(base + a * SEGW + lds_index(4 * c, id)) =
             make_float4(v[a][4 * c], v[a][4 * c + 1], v[a][4 * c + 2], v[a][4 * c + 3]);
   } else {
 #pragma unroll
     for (int a = 0; a < NSEG; ++a)
 #pragma unroll
-      for (int e = 0; e < E; ++e) base[a * SEGW + lds_addr(e << b)] = v[a][e];
+      for (int e = 0; e < E; ++e) base[a * SEGW + lds_index(e << b, id)] = v[a][e];
   }
 }
 
 template <int LOGE, int NSEG, int SEGW>
-__device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b) {
+__device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b,
+                                        bool id = false) {
   constexpr int E = 1 << LOGE;
-  const float* const base = buf + lds_addr(lay<LOGE>(t, 0, b));
+  const float* const base = buf + lds_index(lay<LOGE>(t, 0, b), id);
   if (b == 0) {
 #pragma unroll
     for (int a = 0; a < NSEG; ++a)
 #pragma unroll
       for (int c = 0; c < E / 4; ++c) {
-        const float4 q = *reinterpret_cast<const float4*>(base + a * SEGW + lds_addr(4 * c));
+        const float4 q = *reinterpret_cast<const float4*>(base + a * SEGW + lds_index(4 * c, id));
         v[a][4 * c] = q.x;
         v[a][4 * c + 1] = q.y;
         v[a][4 * c + 2] = q.z;
@@ -152,17 +162,27 @@ __device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << 
 #pragma unroll
     for (int a = 0; a < NSEG; ++a)
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[a][e] = base[a * SEGW + lds_addr(e << b)];
+      for (int e = 0; e < E; ++e) v[a][e] = base[a * SEGW + lds_index(e << b, id)];
   }
 }
 
 template <int LOGE, int SEGW>
-__device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b) {
-  lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b);
+__device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b,
+                                         bool id = false) {
+  lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b, id);
 }
 template <int LOGE, int SEGW>
-__device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b) {
-  lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b);
+__device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b,
+                                         bool id = false) {
+  lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b, id);
+}
+
+// Whether every lane keeps the same low 6 index bits in layouts b0 and b1
+// (thread bit j < 6 carries index bit j when j < b, else j + LOGE).
+__host__ __device__ constexpr bool same_lane_bits(int b0, int b1) {
+  for (int j = 0; j < 6; ++j)
+    if ((j < b0) != (j < b1)) return false;
+  return true;
 }
 
 // Orders this wave's LDS writes before its later LDS reads.  The LDS

@@ -46,6 +46,11 @@ struct FwdShape {
   // is issued a full group earlier) and three (more registers, no gain).
   static constexpr int PD = SEGS == 1 ? 2 : 1;
   static constexpr int BUFW = R * SEGS * SEGW;     // words per LDS buffer
+  // Unpadded addressing for a workgroup transpose that keeps lanes' index bits.
+  static constexpr bool id_transpose(int k) {
+    return !local_transpose(k) &&
+           same_lane_bits(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0);
+  }
   static constexpr bool local_transpose(int k) {   // transpose into phase k (k = NPH: back to 0)
     return wave_local(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0, LOGT);
   }
@@ -398,7 +403,8 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
         else __syncthreads();
         const int b = k < NPH ? phase_base(k, L, LOGE) : 0;
 #pragma unroll
-        for (int sg = 0; sg < SEGS; ++sg) lds_get1<LOGE, SEGW>(buf_in + sg * SEGW, v[sg], t, b);
+        for (int sg = 0; sg < SEGS; ++sg)
+          lds_get1<LOGE, SEGW>(buf_in + sg * SEGW, v[sg], t, b, S::id_transpose(k));
         if (local_in) wave_lds_sync();
         else ++gidx;
       }
@@ -420,7 +426,7 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
             else last2x2(v[sg][lo], v[sg][hi], C.last[j]);
           }
         }
-        lds_put1<LOGE, SEGW>(buf_out + sg * SEGW, v[sg], t, b);
+        lds_put1<LOGE, SEGW>(buf_out + sg * SEGW, v[sg], t, b, S::id_transpose(k + 1));
         if (SEGS > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
