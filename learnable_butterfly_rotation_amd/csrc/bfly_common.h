@@ -115,16 +115,29 @@ __host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c
 // is additive over disjoint index bits, so the address of register e is the
 // thread's base for the layout plus a compile-time offset for e.
 //
-// `id` selects unpadded addressing (word = index), for transposes in which
-// every lane keeps the same low 6 index bits on both sides: each access of
-// one register then covers 64 consecutive words (no bank conflicts), and
-// registers lie multiples of 64 words apart, so the compiler pairs them
-// into ds_read2st64 / ds_write2st64, twice the words per instruction.
-__device__ __forceinline__ int lds_index(int i, bool id) { return id ? i : lds_addr(i); }
+// Other addressings (`mode`), each additive over index bits as well:
+//   LDS_ID    word = index, for transposes in which every lane keeps the same
+//             low 6 index bits on both sides: each access of one register
+//             covers 64 consecutive words (no bank conflicts), and registers
+//             lie multiples of 64 words apart, so the compiler pairs them
+//             into ds_read2st64 / ds_write2st64, twice the words per
+//             instruction;
+//   LDS_P512  4 pad words after every 32 within each block of 512, blocks
+//             576 words apart, for the transpose from registers 512 elements
+//             apart (n = 4096) back to 8 consecutive elements: the strided
+//             side pairs into ds_write2st64 (576 = 9 * 64), the 16-byte side
+//             stays conflict-free (8 lanes of a 16-byte access land on
+//             distinct banks).
+enum LdsMode : int { LDS_PAD = 0, LDS_ID = 1, LDS_P512 = 2 };
+__host__ __device__ constexpr int lds_index(int i, int mode) {
+  return mode == LDS_ID     ? i
+         : mode == LDS_P512 ? (i >> 9) * 576 + (i & 511) + 4 * ((i >> 5) & 15)
+                            : lds_addr(i);
+}
 
 template <int LOGE, int NSEG, int SEGW>
 __device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << LOGE], int t, int b,
-                                        bool id = false) {
+                                        int id = LDS_PAD) {
   constexpr int E = 1 << LOGE;
   float* const base = buf + lds_index(lay<LOGE>(t, 0, b), id);
   if (b == 0) {
@@ -144,7 +157,7 @@ __device__ __forceinline__ void lds_put(float* buf, const float (&v)[NSEG][1 << 
 
 template <int LOGE, int NSEG, int SEGW>
 __device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << LOGE], int t, int b,
-                                        bool id = false) {
+                                        int id = LDS_PAD) {
   constexpr int E = 1 << LOGE;
   const float* const base = buf + lds_index(lay<LOGE>(t, 0, b), id);
   if (b == 0) {
@@ -168,12 +181,12 @@ __device__ __forceinline__ void lds_get(const float* buf, float (&v)[NSEG][1 << 
 
 template <int LOGE, int SEGW>
 __device__ __forceinline__ void lds_put1(float* buf, const float (&v)[1 << LOGE], int t, int b,
-                                         bool id = false) {
+                                         int id = LDS_PAD) {
   lds_put<LOGE, 1, SEGW>(buf, reinterpret_cast<const float (&)[1][1 << LOGE]>(v), t, b, id);
 }
 template <int LOGE, int SEGW>
 __device__ __forceinline__ void lds_get1(const float* buf, float (&v)[1 << LOGE], int t, int b,
-                                         bool id = false) {
+                                         int id = LDS_PAD) {
   lds_get<LOGE, 1, SEGW>(buf, reinterpret_cast<float (&)[1][1 << LOGE]>(v), t, b, id);
 }
 

@@ -46,11 +46,15 @@ struct FwdShape {
   // is issued a full group earlier) and three (more registers, no gain).
   static constexpr int PD = SEGS == 1 ? 2 : 1;
   static constexpr int BUFW = R * SEGS * SEGW;     // words per LDS buffer
-  // Unpadded addressing for a workgroup transpose that keeps lanes' index bits.
-  static constexpr bool id_transpose(int k) {
-    return !local_transpose(k) &&
-           same_lane_bits(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0);
+  // LDS addressing of the transpose into phase k (see LdsMode).
+  static constexpr int id_transpose(int k) {
+    return local_transpose(k) ? LDS_PAD
+           : same_lane_bits(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0) ? LDS_ID
+           : (k == NPH && phase_base(k - 1, L, LOGE) >= 9) ? LDS_P512
+           : LDS_PAD;
   }
+  static_assert(lds_index(NB - 1, LDS_P512) < SEGW && lds_index(NB - 1, LDS_ID) < SEGW,
+                "every addressing stays inside a segment's words");
   static constexpr bool local_transpose(int k) {   // transpose into phase k (k = NPH: back to 0)
     return wave_local(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0, LOGT);
   }
