@@ -252,7 +252,7 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   p.y = y;
   p.dx = dx;
   p.partials = reinterpret_cast<float*>(ws + align_up(coeff_bytes_l(l), 256));
-  p.cs = bfly::table_at(tab, l).cs;
+  p.tab = bfly::table_at(tab, l);
   p.rows = rows;
   p.logn = l;
   p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);

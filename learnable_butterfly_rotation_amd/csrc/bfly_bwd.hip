@@ -1,8 +1,8 @@
 // Backward of the butterfly for learning the angles, fp32, plus the angle
 // preparation kernel.
 //
-// Pass 1, per row (team of T threads, E elements each, (cos, sin) resident
-// in VGPRs as in the forward):
+// Pass 1, per row (team of T threads, E elements each, the three-shear
+// coefficients resident in VGPRs as in the forward):
 //   v <- x (load/store layout), forward phases -> v = Q x in the last
 //   phase's layout, y stored from there; g <- dL/dY loaded directly in that
 //   layout; then the stages in reverse: for each pair (lo, hi) of stage s
@@ -12,6 +12,14 @@
 //   g = Q^T dL/dY = dL/dX in the load/store layout.  Each thread keeps one
 //   fp32 accumulator per pair it owns across all rows of its workgroup and
 //   writes them to the workgroup's slot of the partials buffer at the end.
+//   Stages 0..L-2 run as three shears on sign-carrying values (the forward
+//   table's three-shear form); their inverse, which is also their transpose,
+//   is the same three shears with negated coefficients, for v and for g
+//   alike, since g carries the same signs as v.  The accumulated term then
+//   carries the product of the pair's two signs, which the table records
+//   and which multiplies the accumulator when it is written.  The last stage
+//   is the 2x2 matrix that maps signed values to true ones; its inverse is
+//   its transpose.
 // Pass 2: dtheta[k] = sum over slots of partials[slot][k] in fp64, in an
 // order fixed by the slot count alone -- the result is bit-identical from
 // run to run and independent of the device (the slot count depends only on
@@ -50,21 +58,6 @@ struct BwdShape {
   static constexpr size_t LDS_BYTES = (size_t)NBUF * R * W * sizeof(float);
 };
 
-// Rotation by t (forward) and by -t (transpose), given (cos t, sin t).
-__device__ __forceinline__ void givens_t(float& a, float& b, float c, float s) {
-  const float na = fmaf(c, a, s * b);
-  const float nb = fmaf(-s, a, c * b);
-  a = na;
-  b = nb;
-}
-
-__device__ __forceinline__ void givens_f(float& a, float& b, float c, float s) {
-  const float na = fmaf(c, a, -(s * b));
-  const float nb = fmaf(s, a, c * b);
-  a = na;
-  b = nb;
-}
-
 template <int LOGN>
 __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   using S = BwdShape<LOGN>;
@@ -83,16 +76,21 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   float* const rbuf_v = lds + (3 * R + team) * W;
   float* const rbuf_g = lds + (4 * R + team) * W;
 
-  float cc[L][E / 2], ss[L][E / 2], acc[L][E / 2];
+  float pp[L - 1][E / 2], uu[L - 1][E / 2], acc[L][E / 2];
+  float4 lastc[E / 2];
 #pragma unroll
   for (int s = 0; s < L; ++s) {
     const int b = phase_base(s / LOGE, L, LOGE);
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
-      const int ilo = lay<LOGE>(t, pair_lo(j, s - b), b);
-      const float2 c = P.cs[s * (N / 2) + pair_rank(ilo, s)];
-      cc[s][j] = c.x;
-      ss[s][j] = c.y;
+      const int rank = pair_rank(lay<LOGE>(t, pair_lo(j, s - b), b), s);
+      if (s < L - 1) {
+        const float2 c = P.tab.lift[s * (N / 2) + rank];
+        pp[s][j] = c.x;
+        uu[s][j] = c.y;
+      } else {
+        lastc[j] = P.tab.last[rank];
+      }
       acc[s][j] = 0.f;
     }
   }
@@ -166,7 +164,8 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
 #pragma unroll
         for (int j = 0; j < E / 2; ++j) {
           const int lo = pair_lo(j, q), hi = lo | (1 << q);
-          givens_f(v[lo], v[hi], cc[s][j], ss[s][j]);
+          if (s < L - 1) shear3(v[lo], v[hi], pp[s][j], uu[s][j]);
+          else last2x2(v[lo], v[hi], lastc[j]);
         }
       }
     }
@@ -190,8 +189,15 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
           const int lo = pair_lo(j, q), hi = lo | (1 << q);
           acc[s][j] = fmaf(g[hi], v[lo], acc[s][j]);
           acc[s][j] = fmaf(-g[lo], v[hi], acc[s][j]);
-          givens_t(v[lo], v[hi], cc[s][j], ss[s][j]);
-          givens_t(g[lo], g[hi], cc[s][j], ss[s][j]);
+          if (s < L - 1) {
+            shear3(v[lo], v[hi], -pp[s][j], -uu[s][j]);
+            shear3(g[lo], g[hi], -pp[s][j], -uu[s][j]);
+          } else {
+            const float4 m = lastc[j];  // transpose of the last stage's matrix
+            const float4 mt = make_float4(m.x, m.z, m.y, m.w);
+            last2x2(v[lo], v[hi], mt);
+            last2x2(g[lo], g[hi], mt);
+          }
         }
       }
       if (k > 0) {
@@ -226,8 +232,8 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
     const int b = phase_base(s / LOGE, L, LOGE);
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
-      const int ilo = lay<LOGE>(t, pair_lo(j, s - b), b);
-      part[s * (N / 2) + pair_rank(ilo, s)] = acc[s][j];
+      const int k = s * (N / 2) + pair_rank(lay<LOGE>(t, pair_lo(j, s - b), b), s);
+      part[k] = s < L - 1 ? P.tab.eps[k] * acc[s][j] : acc[s][j];
     }
   }
 }
@@ -384,6 +390,7 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
     const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
     const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
     lift[k] = make_float2((float)(-eps * (sp / (1.0 + cp))), (float)(eps * sp));
+    const_cast<float*>(tab.eps)[k] = (float)eps;
     // scaled form: usable while every stored value stays within 2^64 of its
     // true value (|sigma| >= 2^-64 after this stage)
     const double tn = sn / cn;

@@ -207,4 +207,20 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Givens rotation of (a, b) by phi, |phi| <= pi/2, as three shears:
+// p = -tan(phi/2), u = sin(phi).  Three in-place FMAs, no temporaries.
+__device__ __forceinline__ void shear3(float& a, float& b, float p, float u) {
+  a = fmaf(p, b, a);
+  b = fmaf(u, a, b);
+  a = fmaf(p, b, a);
+}
+
+// The last stage: (a, b) <- (k.x a + k.y b, k.z a + k.w b).
+__device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
+  const float na = fmaf(k.x, a, k.y * b);
+  const float nb = fmaf(k.z, a, k.w * b);
+  a = na;
+  b = nb;
+}
+
 }  // namespace bfly

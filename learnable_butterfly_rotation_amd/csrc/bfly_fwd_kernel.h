@@ -67,14 +67,6 @@ struct FwdShape {
   static constexpr size_t LDS_BYTES = (any_global() ? 3ull : 1ull) * BUFW * sizeof(float);
 };
 
-// Givens rotation of (a, b) by phi, |phi| <= pi/2, as three shears:
-// p = -tan(phi/2), u = sin(phi).  Three in-place FMAs, no temporaries.
-__device__ __forceinline__ void shear3(float& a, float& b, float p, float u) {
-  a = fmaf(p, b, a);
-  b = fmaf(u, a, b);
-  a = fmaf(p, b, a);
-}
-
 // One of stages 0..L-2 on the pair (a, b): two fused multiply-adds on the
 // stored values in the scaled form (c0 = beta, c1 = gamma), else three
 // shears (c0 = p, c1 = u).
@@ -89,13 +81,6 @@ __device__ __forceinline__ void rotate(float& a, float& b, float c0, float c1) {
   }
 }
 
-// The last stage: (a, b) <- (k.x a + k.y b, k.z a + k.w b).
-__device__ __forceinline__ void last2x2(float& a, float& b, float4 k) {
-  const float na = fmaf(k.x, a, k.y * b);
-  const float nb = fmaf(k.z, a, k.w * b);
-  a = na;
-  b = nb;
-}
 
 // Cross-lane max/min over the `gt` consecutive lanes of a quantization group
 // (gt a power of two <= 64).  Within a 16-lane DPP row: xor-1 and xor-2 quad

@@ -38,17 +38,22 @@ enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 // minus is not applied but tracked as a sign on both elements, and a
 // rotation of sign-carrying elements is again a rotation (by +-t).  The last
 // stage maps the sign-carrying values straight to the true outputs.
+//   eps   float [L-1][half]   the product of the signs the pair's two
+//                             elements carry in the three-shear form (the
+//                             backward's angle gradients are accumulated on
+//                             signed values and multiplied by it at the end)
 struct Table {
   const float2* cs;
   const float2* fg;
   const float4* flast;
   const float2* lift;
   const float4* last;
+  const float* eps;
 };
 
 __host__ __device__ inline size_t table_bytes(int logn) {
   const size_t half = (size_t)1 << (logn - 1);
-  return half * 8 * (size_t)(3 * logn + 2);
+  return half * 8 * (size_t)(3 * logn + 2) + half * 4 * (size_t)(logn - 1);
 }
 
 __host__ __device__ inline Table table_at(const void* base, int logn) {
@@ -60,6 +65,7 @@ __host__ __device__ inline Table table_at(const void* base, int logn) {
   t.flast = reinterpret_cast<const float4*>(b + half * 8 * (2 * logn - 1));
   t.lift = reinterpret_cast<const float2*>(b + half * 8 * (2 * logn + 1));
   t.last = reinterpret_cast<const float4*>(b + half * 8 * (3 * logn));
+  t.eps = reinterpret_cast<const float*>(b + half * 8 * (3 * logn + 2));
   return t;
 }
 
@@ -90,7 +96,7 @@ struct BwdParams {
   float* y;           // optional
   float* dx;
   float* partials;    // [nblk][log2 n][n/2]
-  const float2* cs;
+  Table tab;
   int64_t rows;
   int32_t logn;
   int32_t nblk;       // number of partial slots = grid size

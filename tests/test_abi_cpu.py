@@ -52,9 +52,10 @@ def test_status_strings(L):
 def test_sizes(L):
     # (cos, sin) [L][n/2] + three-shear (p, u) [L-1][n/2] + last stage 4 x [n/2], fp32
     # per pair: (cos, sin) for every stage, two coefficient pairs (scaled and
-    # three-shear form) for stages 0..L-2, two 4-coefficient last stages
-    assert B.bfly_coeff_bytes(4096) == (12 * 2 + 2 * (12 - 1) * 2 + 2 * 4) * 2048 * 4
-    assert B.bfly_coeff_bytes(256) == (8 * 2 + 2 * 7 * 2 + 2 * 4) * 128 * 4
+    # three-shear form) and a sign product for stages 0..L-2, two
+    # 4-coefficient last stages
+    assert B.bfly_coeff_bytes(4096) == (12 * 2 + 2 * (12 - 1) * 2 + (12 - 1) + 2 * 4) * 2048 * 4
+    assert B.bfly_coeff_bytes(256) == (8 * 2 + 2 * 7 * 2 + 7 + 2 * 4) * 128 * 4
     assert B.bfly_coeff_bytes(100) == 0
     assert B.bfly_coeff_bytes(32) == 0
     ws = B.bfly_backward_workspace_bytes(262144, 4096)
