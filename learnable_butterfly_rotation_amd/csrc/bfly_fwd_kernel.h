@@ -58,6 +58,12 @@ struct FwdShape {
   static constexpr bool local_transpose(int k) {   // transpose into phase k (k = NPH: back to 0)
     return wave_local(phase_base(k - 1, L, LOGE), k < NPH ? phase_base(k, L, LOGE) : 0, LOGT);
   }
+  // Workgroup transposes before the last one (its buffer parity).
+  static constexpr int final_gidx() {
+    int g = 0;
+    for (int k = 1; k < NPH; ++k) g += local_transpose(k) ? 0 : 1;
+    return g;
+  }
   static constexpr bool any_global() {
     for (int k = 1; k <= NPH; ++k)
       if (!local_transpose(k)) return true;
@@ -264,26 +270,25 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
           cur[d][rr * M + a][c] = buf_ld16(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
   };
 
-  // bf16 rows, codes and scales of the previous row group, stored only once
-  // the next group's input has arrived: the wait for that input then never
-  // has to wait for freshly issued stores as well.
+  // The previous row group's outputs: bf16 rows, codes and scales (and, for
+  // fp32 output, its rows), stored only once the next group's input has
+  // arrived, so the wait for that input never has to wait for freshly issued
+  // stores as well.
   uint32_t held_y[SEGS][E / 2], held_c[SEGS], held_sz[SEGS];
-  float vq[SEGS][E];  // the previous group's rotated rows, awaiting quantization
 #pragma unroll
   for (int sg = 0; sg < SEGS; ++sg) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) vq[sg][e] = 0.f;
 #pragma unroll
     for (int k = 0; k < E / 2; ++k) held_y[sg][k] = 0u;
     held_c[sg] = held_sz[sg] = 0u;
   }
   int64_t held_grp = -1;
   const bool scale_lane = QUANT && (t & (gt - 1)) == 0;
-  auto flush = [&]() {
-    if (YK != Y_BF16 && !QUANT) return;
+  auto flush = [&](const float (&w)[SEGS][E]) {
+    if (YK == Y_NONE && !QUANT) return;
     const int64_t hg = held_grp;
     const int64_t vr = valid_rows(hg);
     const auto ry = buffer_range(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * N * 2);
+    const auto ry4 = buffer_range(reinterpret_cast<const float*>(P.y) + hg * GRP_ELEMS, vr * N * 4);
     const auto rc = buffer_range(P.codes + hg * (GRP_ELEMS * bits / 8), vr * N * bits / 8);
     const auto rsc = buffer_range(P.scales + hg * RPP * ngroups_row, vr * ngroups_row * 2);
     const auto rz = buffer_range(P.zeros + hg * RPP * ngroups_row, vr * ngroups_row * 2);
@@ -299,6 +304,12 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
             buf_st16(ry, el * 2 + 16 * c,
                      make_uint4(held_y[sg][4 * c], held_y[sg][4 * c + 1], held_y[sg][4 * c + 2],
                                 held_y[sg][4 * c + 3]));
+        } else if (YK == Y_F32) {
+#pragma unroll
+          for (int c = 0; c < E / 4; ++c)
+            buf_st16(ry4, el * 4 + 16 * c,
+                     make_uint4(__float_as_uint(w[sg][4 * c]), __float_as_uint(w[sg][4 * c + 1]),
+                                __float_as_uint(w[sg][4 * c + 2]), __float_as_uint(w[sg][4 * c + 3])));
         }
         if (QUANT) {
           if (bits == 4) buf_st4(rc, el / 2, held_c[sg]);
@@ -311,41 +322,81 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
       }
   };
 
-  auto store_f32 = [&](int64_t grp, const float (&vv)[SEGS][E]) {
-    const auto ry = buffer_range(reinterpret_cast<const float*>(P.y) + grp * GRP_ELEMS, valid_rows(grp) * N * 4);
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr)
-#pragma unroll
-      for (int a = 0; a < M; ++a) {
-        const int sg = rr * M + a;
-        const uint32_t el = (uint32_t)(thr_elem + rr * N + a * NB);
-#pragma unroll
-        for (int c = 0; c < E / 4; ++c)
-          buf_st16(ry, el * 4 + 16 * c,
-                   make_uint4(__float_as_uint(vv[sg][4 * c]), __float_as_uint(vv[sg][4 * c + 1]),
-                              __float_as_uint(vv[sg][4 * c + 2]), __float_as_uint(vv[sg][4 * c + 3])));
-      }
-  };
-
   // A 1 x 1 Kronecker factor, read once (no memory operation in the loop
   // body may sit under a branch).
   const bool has_mix1 = M == 1 && P.mix != nullptr;
   const float mix1 = has_mix1 ? P.mix[0] : 1.0f;
   const int64_t G = gridDim.x;
+
+  // The last transpose of a row group leaves its rows in layout 0 in this
+  // buffer; the next slot (or the epilogue) reads them there.
+  float* const fin_buf = S::local_transpose(NPH) ? lbuf : ((S::final_gidx() & 1) ? gbuf1 : gbuf0);
+  auto read_final = [&](float (&w)[SEGS][E]) {
+#pragma unroll
+    for (int sg = 0; sg < SEGS; ++sg)
+      lds_get1<LOGE, SEGW>(fin_buf + sg * SEGW, w[sg], t, 0, S::id_transpose(NPH));
+    if (S::local_transpose(NPH)) wave_lds_sync();
+  };
+  // Everything the previous group still needs before its stores: the
+  // Kronecker mix, bf16 packing and quantization.
+  auto finish = [&](float (&w)[SEGS][E]) {
+    if (M == 1 && has_mix1) {  // a 1 x 1 Kronecker factor: a scalar
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[sg][e] *= mix1;
+    }
+    if (M > 1) {  // Kronecker mix across a row's segments, column by column
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float mw[M];
+#pragma unroll
+          for (int a = 0; a < M; ++a) {
+            float acc = P.mix[a * M] * w[rr * M][e];
+#pragma unroll
+            for (int a2 = 1; a2 < M; ++a2) acc = fmaf(P.mix[a * M + a2], w[rr * M + a2][e], acc);
+            mw[a] = acc;
+          }
+#pragma unroll
+          for (int a = 0; a < M; ++a) w[rr * M + a][e] = mw[a];
+        }
+    }
+    if (YK == Y_BF16) {
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+        for (int k = 0; k < E / 2; ++k) held_y[sg][k] = pack_bf16(w[sg][2 * k], w[sg][2 * k + 1]);
+    }
+    if (QUANT) {
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg)
+        held_c[sg] = quantize8(w[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
+    }
+  };
+
   // One row group through the whole path, from prefetch slot d (a
   // compile-time index once the callers' loops are unrolled).
   auto slot = [&](const int64_t grp, const int d) __attribute__((always_inline)) {
+    // The previous group's rows come out of LDS first: their read latency is
+    // covered by this group's unpacking and first register phase, and their
+    // finishing work (quantization above all) interleaves with that phase.
+    // (On the first pass this reads whatever the buffer holds; its stores
+    // fall in empty ranges.)
+    float w[SEGS][E];
+    read_final(w);
     float v[SEGS][E];
 #pragma unroll
     for (int sg = 0; sg < SEGS; ++sg) {
       if (XBF16) {
 #pragma unroll
         for (int c = 0; c < RAW; ++c) {
-          const uint32_t w[4] = {cur[d][sg][c].x, cur[d][sg][c].y, cur[d][sg][c].z, cur[d][sg][c].w};
+          const uint32_t u[4] = {cur[d][sg][c].x, cur[d][sg][c].y, cur[d][sg][c].z, cur[d][sg][c].w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            v[sg][8 * c + 2 * k] = bf16_lo(w[k]);
-            v[sg][8 * c + 2 * k + 1] = bf16_hi(w[k]);
+            v[sg][8 * c + 2 * k] = bf16_lo(u[k]);
+            v[sg][8 * c + 2 * k + 1] = bf16_hi(u[k]);
           }
         }
       } else {
@@ -368,20 +419,12 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
 #pragma unroll
       for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[sg][e])::"memory");
     load(grp + PD * G, d);  // past the end: an empty range, no traffic
-
-    // The previous group's quantization runs here, interleaved with this
-    // group's first register phase: the two dependency chains are
-    // independent, so each fills the other's latency.  (On the first pass it
-    // quantizes zeros and nothing is stored.)
-    if (QUANT) {
-#pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-        held_c[sg] = quantize8(vq[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
-    }
+    finish(w);
     // Phase k: [sync for transpose k] -> read every segment -> per segment:
     // rotate, then write it for transpose k+1.  Segment by segment (kept in
     // that order by scheduling barriers), the LDS traffic of one segment
-    // overlaps the arithmetic of the next.
+    // overlaps the arithmetic of the next.  The read after the last
+    // transpose is the next slot's.
     int gidx = 0;  // workgroup transposes so far in this row (compile-time after unrolling)
 #pragma unroll
     for (int k = 0; k <= NPH; ++k) {
@@ -390,15 +433,15 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
       if (k > 0) {
         if (local_in) wave_lds_sync();
         else __syncthreads();
-        const int b = k < NPH ? phase_base(k, L, LOGE) : 0;
+        if (k == NPH) break;
+        const int b = phase_base(k, L, LOGE);
 #pragma unroll
         for (int sg = 0; sg < SEGS; ++sg)
           lds_get1<LOGE, SEGW>(buf_in + sg * SEGW, v[sg], t, b, S::id_transpose(k));
         if (local_in) wave_lds_sync();
         else ++gidx;
       }
-      if (k == 1) flush();  // the previous group's outputs, now complete
-      if (k == NPH) break;
+      if (k == 1) flush(w);  // the previous group's outputs, now complete
       const int b = phase_base(k, L, LOGE);
       const int s_end = ((k + 1) * LOGE < L) ? (k + 1) * LOGE : L;
       const bool local_out = S::local_transpose(k + 1);
@@ -419,45 +462,6 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
         if (SEGS > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    if (M == 1 && has_mix1) {  // a 1 x 1 Kronecker factor: a scalar
-#pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[sg][e] *= mix1;
-    }
-    if (M > 1) {  // Kronecker mix across a row's segments, column by column
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float w[M];
-#pragma unroll
-          for (int a = 0; a < M; ++a) {
-            float acc = P.mix[a * M] * v[rr * M][e];
-#pragma unroll
-            for (int a2 = 1; a2 < M; ++a2) acc = fmaf(P.mix[a * M + a2], v[rr * M + a2][e], acc);
-            w[a] = acc;
-          }
-#pragma unroll
-          for (int a = 0; a < M; ++a) v[rr * M + a][e] = w[a];
-        }
-    }
-
-    if (YK == Y_F32) {  // fp32 rows are stored right away
-      store_f32(grp, v);
-    } else if (YK == Y_BF16) {
-#pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-#pragma unroll
-        for (int k = 0; k < E / 2; ++k) held_y[sg][k] = pack_bf16(v[sg][2 * k], v[sg][2 * k + 1]);
-    }
-    if (QUANT) {
-#pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-#pragma unroll
-        for (int e = 0; e < E; ++e) vq[sg][e] = v[sg][e];
-    }
     held_grp = grp;
   };
 
@@ -467,12 +471,16 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
   // pass of the main loop (its stores fall in empty ranges and are dropped).
   // The compiler's wait counts at the loop head merge the prologue with the
   // latch; with matching sequences, slot d waits for its own load alone.
+  float zero[SEGS][E];
+#pragma unroll
+  for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+    for (int e = 0; e < E; ++e) zero[sg][e] = 0.f;
 #pragma unroll
   for (int d = 0; d < PD; ++d) {
     load(blockIdx.x + d * G, d);
     asm volatile("" ::: "memory");
-    flush();
-    if (YK == Y_F32) store_f32(-1, vq);
+    flush(zero);
     asm volatile("" ::: "memory");
   }
   // Main loop: full passes only, so its body has no branch around memory
@@ -487,12 +495,11 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
 #pragma unroll
   for (int d = 0; d < PD - 1; ++d)
     if (g0 + d * G < ngrp) slot(g0 + d * G, d);
-  if (QUANT) {
-#pragma unroll
-    for (int sg = 0; sg < SEGS; ++sg)
-      held_c[sg] = quantize8(vq[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
-  }
-  flush();
+  // Epilogue: the last group's outputs.
+  float w[SEGS][E];
+  read_final(w);
+  finish(w);
+  flush(w);
 }
 
 // One kernel per (input type, output kind, quantizer format): the host picks
