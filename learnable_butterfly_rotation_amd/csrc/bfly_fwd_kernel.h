@@ -216,15 +216,46 @@ struct Coeffs {
 };
 
 // The persistent row loop for one (input, output, quantizer) variant.
-template <class S, bool XBF16, int YK, int QM, bool FAST>
+// Input registers of one row group: SEGS segments of 16-byte vectors.
+template <class S, bool XBF16>
+struct InRegs {
+  static constexpr int RAW = XBF16 ? S::E / 8 : S::E / 4;  // 16-byte vectors per segment
+  uint4 r[S::PD][S::SEGS][RAW];
+};
+
+// Issue the loads of row group grp into prefetch slot d, through a buffer
+// resource covering exactly the group's valid rows (none past the end).
+template <class S, bool XBF16>
+__device__ __forceinline__ void load_group(const FwdParams& P, const int64_t rows, const int64_t grp,
+                                           InRegs<S, XBF16>& in, const int d, const int team,
+                                           const int t) {
+  constexpr int N = S::N, NB = S::NB, E = S::E, RPP = S::ROWS_PER_PASS;
+  constexpr int RPT = S::ROWS_PER_PASS / S::R, M = S::SEGS / RPT;
+  constexpr int RAW = InRegs<S, XBF16>::RAW, ESZ = XBF16 ? 2 : 4;
+  const int64_t r = rows - grp * RPP;
+  const int64_t valid = grp < 0 ? 0 : (r < 0 ? 0 : (r > RPP ? RPP : r));
+  const auto rs = buffer_range(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * N) * ESZ,
+                               valid * N * ESZ);
+  const int thr_elem = team * RPT * N + t * E;
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+    for (int a = 0; a < M; ++a)
+#pragma unroll
+      for (int c = 0; c < RAW; ++c)
+        in.r[d][rr * M + a][c] = buf_ld16(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
+}
+
+// PRE: the caller has already issued the prologue's loads (slot d holds row
+// group blockIdx.x + d * gridDim.x), before its own set-up work.
+template <class S, bool XBF16, int YK, int QM, bool FAST, bool PRE>
 __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows, float* lds, int team,
-                                         int t, const Coeffs<S>& C) {
+                                         int t, const Coeffs<S>& C, InRegs<S, XBF16>& in) {
   constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
   constexpr int RPT = S::ROWS_PER_PASS / S::R;
   constexpr int SEGS = S::SEGS, SEGW = S::SEGW, BUFW = S::BUFW, RPP = S::ROWS_PER_PASS;
   constexpr int L = S::L, NPH = S::NPH;
   constexpr int RAW = XBF16 ? E / 8 : E / 4;  // 16-byte vectors per segment
-  constexpr int ESZ = XBF16 ? 2 : 4;
   constexpr bool QUANT = QM != Q_NONE;
   static_assert(global_transposes<S>() % 2 == 0, "buffer alternation assumes an even count");
 
@@ -233,7 +264,6 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
   float* const gbuf1 = lds + 2 * BUFW + team * (SEGS * SEGW);
 
   const int64_t ngrp = (rows + RPP - 1) / RPP;
-  const char* xb = reinterpret_cast<const char*>(P.x);
   constexpr bool FIXED = QM == Q_S4G128 || QM == Q_A2G128;
   const int bits = QM == Q_S4G128 ? 4 : (QM == Q_A2G128 ? 2 : P.bits);
   const bool asym = QM == Q_A2G128 || (QM == Q_ANY && P.asym != 0);
@@ -258,17 +288,8 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
   };
 
   constexpr int PD = S::PD;
-  uint4 cur[PD][SEGS][RAW];
-  auto load = [&](int64_t grp, int d) {
-    const auto rs = buffer_range(xb + grp * GRP_ELEMS * ESZ, valid_rows(grp) * N * ESZ);
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr)
-#pragma unroll
-      for (int a = 0; a < M; ++a)
-#pragma unroll
-        for (int c = 0; c < RAW; ++c)
-          cur[d][rr * M + a][c] = buf_ld16(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
-  };
+  auto& cur = in.r;
+  auto load = [&](int64_t grp, int d) { load_group<S, XBF16>(P, rows, grp, in, d, team, t); };
 
   // The previous row group's outputs: bf16 rows, codes and scales (and, for
   // fp32 output, its rows), stored only once the next group's input has
@@ -478,7 +499,7 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
     for (int e = 0; e < E; ++e) zero[sg][e] = 0.f;
 #pragma unroll
   for (int d = 0; d < PD; ++d) {
-    load(blockIdx.x + d * G, d);
+    if (!PRE) load(blockIdx.x + d * G, d);
     asm volatile("" ::: "memory");
     flush(zero);
     asm volatile("" ::: "memory");
@@ -537,6 +558,12 @@ fwd_kernel(FwdParams P) {
       }
     }
   };
+  // The first row groups' input is requested before anything else, so its
+  // latency overlaps the coefficient loads and the form check.
+  InRegs<S, XBF16> in;
+#pragma unroll
+  for (int d = 0; d < S::PD; ++d)
+    load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team, t);
   load_coeffs(P.tab.fg, P.tab.flast);
   int nan_seen = 0;
 #pragma unroll
@@ -548,11 +575,11 @@ fwd_kernel(FwdParams P) {
   // The two forms run as consecutive loops (the unused one over zero rows),
   // not as two arms of a branch: the register allocator then never holds
   // both coefficient sets at once.
-  row_loop<S, XBF16, YK, QM, true>(P, shear ? 0 : P.rows, lds, team, t, C);
+  row_loop<S, XBF16, YK, QM, true, true>(P, shear ? 0 : P.rows, lds, team, t, C, in);
   if (shear) {
     // Three-shear form, with the general quantizer for every format.
     load_coeffs(P.tab.lift, P.tab.last);
-    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false>(P, P.rows, lds, team, t, C);
+    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false>(P, P.rows, lds, team, t, C, in);
   }
 }
 
