@@ -558,13 +558,35 @@ fwd_kernel(FwdParams P) {
       }
     }
   };
+  // The scaled form's table is in thread order: 16-byte loads, each wave's
+  // one contiguous run.
+  auto load_fast = [&](const float4* tab) {
+    const auto rt = buffer_range(tab, (size_t)2 * (L + 1) * T * sizeof(float4));
+#pragma unroll
+    for (int s = 0; s < L - 1; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 q = buf_ld16(rt, (uint32_t)(((2 * s + h) * T + t) * 16));
+        C.c0[s][2 * h] = __uint_as_float(q.x);
+        C.c1[s][2 * h] = __uint_as_float(q.y);
+        C.c0[s][2 * h + 1] = __uint_as_float(q.z);
+        C.c1[s][2 * h + 1] = __uint_as_float(q.w);
+      }
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const uint4 q = buf_ld16(rt, (uint32_t)(((2 * (L - 1) + j) * T + t) * 16));
+      C.last[j] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+                              __uint_as_float(q.w));
+    }
+  };
+  static_assert(E == 8, "the thread-ordered table holds four pairs per stage and thread");
   // The first row groups' input is requested before anything else, so its
   // latency overlaps the coefficient loads and the form check.
   InRegs<S, XBF16> in;
 #pragma unroll
   for (int d = 0; d < S::PD; ++d)
     load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team, t);
-  load_coeffs(P.tab.fg, P.tab.flast);
+  load_fast(P.tab.fgt);
   int nan_seen = 0;
 #pragma unroll
   for (int s = 0; s < L - 1; ++s)

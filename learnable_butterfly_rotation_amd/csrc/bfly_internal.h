@@ -14,8 +14,17 @@ enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 // The prepared coefficient table of a butterfly of length n = 2^L, in one
 // device allocation (half = n/2 pairs per stage):
 //   cs    float2 [L][half]    (cos t, sin t) of every angle (backward)
-//   fg    float2 [L-1][half]  (beta, gamma): stages 0..L-2 in scaled form
-//   flast float4 [half]       the last stage with the scales folded in
+//   fgt   float4 [2(L+1)][n/8] the scaled form, in forward-thread order:
+//                             row q of thread t holds what the forward
+//                             kernel's thread t loads q-th, so that every
+//                             load of a wave is one contiguous 1 KiB run.
+//                             Rows 2s and 2s+1 (s < L-1): (beta, gamma) of
+//                             the thread's pairs 0,1 and 2,3 of stage s;
+//                             rows 2(L-1)+j: the last stage of its pair j
+//                             with the scales folded in.  (Thread t of a
+//                             forward phase with base bit b holds the eight
+//                             elements whose bits b..b+2 vary; fwd_pair_slot
+//                             gives the place of each pair.)
 //   lift  float2 [L-1][half]  (p, u): stages 0..L-2 as three shears
 //   last  float4 [half]       the last stage with the tracked signs folded in
 //
@@ -44,8 +53,7 @@ enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 //                             signed values and multiplied by it at the end)
 struct Table {
   const float2* cs;
-  const float2* fg;
-  const float4* flast;
+  const float4* fgt;
   const float2* lift;
   const float4* last;
   const float* eps;
@@ -61,12 +69,30 @@ __host__ __device__ inline Table table_at(const void* base, int logn) {
   const char* b = static_cast<const char*>(base);
   Table t;
   t.cs = reinterpret_cast<const float2*>(b);
-  t.fg = reinterpret_cast<const float2*>(b + half * 8 * logn);
-  t.flast = reinterpret_cast<const float4*>(b + half * 8 * (2 * logn - 1));
+  t.fgt = reinterpret_cast<const float4*>(b + half * 8 * logn);
   t.lift = reinterpret_cast<const float2*>(b + half * 8 * (2 * logn + 1));
   t.last = reinterpret_cast<const float4*>(b + half * 8 * (3 * logn));
   t.eps = reinterpret_cast<const float*>(b + half * 8 * (3 * logn + 2));
   return t;
+}
+
+// Place of pair (s, p) in fgt: the forward kernel gives stage s to phase
+// s / 3, whose base bit is b = min(3 (s / 3), L - 3); thread t holds the
+// elements with t's bits below b, e at bits b..b+2 and t's other bits above,
+// and its pair slot j is e without the pair bit s - b.  Returns the float4
+// row (2s + j/2 for s < L-1, 2(L-1) + j for the last stage) times n/8 plus
+// t, and sets j.
+__host__ __device__ inline int64_t fwd_pair_slot(int s, int p, int logn, int& j) {
+  const int i = ((p >> s) << (s + 1)) | (p & ((1 << s) - 1));  // lower element
+  const int k = s / 3;
+  const int b = (3 * k < logn - 3) ? 3 * k : logn - 3;
+  const int e = (i >> b) & 7;
+  const int t = (i & ((1 << b) - 1)) | ((i >> (b + 3)) << b);
+  const int q = s - b;
+  j = ((e >> (q + 1)) << q) | (e & ((1 << q) - 1));
+  const int64_t T = (int64_t)1 << (logn - 3);
+  const int row = s < logn - 1 ? 2 * s + (j >> 1) : 2 * (logn - 1) + j;
+  return row * T + t;
 }
 
 // Everything one forward launch needs.  tab is the prepared table of the

@@ -293,8 +293,9 @@ def test_quarter_pi_is_hadamard():
 
 def _table_uses_scaled_form(theta, n):
     """Whether the prepared table keeps the scaled (two-FMA) rotation form.
-    Reads the table's scaled-form coefficient block (after the (cos, sin)
-    block, (log2 n - 1) x n/2 float2) and looks for the NaN marker."""
+    Reads the (beta, gamma) part of the table's scaled-form block (after the
+    (cos, sin) block; (log2 n - 1) x n/2 float2, in the forward kernel's
+    thread order) and looks for the NaN marker."""
     L, half = int(math.log2(n)), n // 2
     tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
     B.bfly_prepare(dev(theta), n, tab)
