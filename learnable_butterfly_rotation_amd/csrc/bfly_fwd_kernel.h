@@ -248,8 +248,16 @@ __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t row
 
 // PRE: the caller has already issued the prologue's loads (slot d holds row
 // group blockIdx.x + d * gridDim.x), before its own set-up work.
-template <class S, bool XBF16, int YK, int QM, bool FAST, bool PRE>
-__device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows, float* lds, int team,
+// CHECK: the coefficients are still arriving.  The block's first row group
+// runs before anything waits for all of them (each phase waits for its own
+// stages' loads only); then the coefficients are checked for the NaN marker
+// of an unusable scaled form.  If any workgroup thread saw one, the loop
+// stops after that group (whose stored outputs are garbage) and returns
+// false, and the caller must redo every row.  The early stop only shortens
+// the loop: a separate exit path would put the two forms' loops on two arms
+// of a branch, where the register allocator does far worse.
+template <class S, bool XBF16, int YK, int QM, bool FAST, bool PRE, bool CHECK>
+__device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows, float* lds, int team,
                                          int t, const Coeffs<S>& C, InRegs<S, XBF16>& in) {
   constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
   constexpr int RPT = S::ROWS_PER_PASS / S::R;
@@ -508,19 +516,44 @@ __device__ __forceinline__ void row_loop(const FwdParams& P, const int64_t rows,
   // operations (a conditional slot would make the compiler wait for the
   // most recent load at every slot).
   int64_t g0 = blockIdx.x;
-  for (; g0 + (PD - 1) * G < ngrp; g0 += PD * G) {
+  constexpr int D0 = CHECK ? 1 % PD : 0;  // prefetch slot of the loop's first group
+  bool usable = true;
+  if (CHECK) {
+    // The grid never exceeds the number of groups: every block has this one.
+    slot(g0, 0);
+    g0 += G;
+    bool nan_seen = false;
 #pragma unroll
-    for (int d = 0; d < PD; ++d) slot(g0 + d * G, d);
+    for (int s = 0; s < L - 1; ++s)
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j)  // bit test: the build assumes no NaN arithmetic
+        nan_seen |= (__float_as_uint(C.c0[s][j]) & 0x7fffffffu) > 0x7f800000u;
+    // One word per wave, one barrier.
+    constexpr int NW = (S::NT + 63) / 64;
+    __shared__ int nan_wave[NW];
+    const int any = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
+    if ((threadIdx.x & 63) == 0) nan_wave[threadIdx.x >> 6] = any;
+    __syncthreads();
+    int seen = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) seen |= nan_wave[w];
+    usable = __builtin_amdgcn_readfirstlane(seen) == 0;
+  }
+  const int64_t nrun = usable ? ngrp : 0;
+  for (; g0 + (PD - 1) * G < nrun; g0 += PD * G) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) slot(g0 + d * G, (D0 + d) % PD);
   }
   // Tail: the block's last, partial pass.
 #pragma unroll
   for (int d = 0; d < PD - 1; ++d)
-    if (g0 + d * G < ngrp) slot(g0 + d * G, d);
+    if (g0 + d * G < nrun) slot(g0 + d * G, (D0 + d) % PD);
   // Epilogue: the last group's outputs.
   float w[SEGS][E];
   read_final(w);
   finish(w);
   flush(w);
+  return usable;
 }
 
 // One kernel per (input type, output kind, quantizer format): the host picks
@@ -559,14 +592,15 @@ fwd_kernel(FwdParams P) {
     }
   };
   // The scaled form's table is in thread order: 16-byte loads, each wave's
-  // one contiguous run.
+  // one contiguous run, issued in stage order.
   auto load_fast = [&](const float4* tab) {
     const auto rt = buffer_range(tab, (size_t)2 * (L + 1) * T * sizeof(float4));
 #pragma unroll
     for (int s = 0; s < L - 1; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 q = buf_ld16(rt, (uint32_t)(((2 * s + h) * T + t) * 16));
+        const uint4 q = buf_ld16s(rt, (uint32_t)(t * 16), (uint32_t)((2 * s + h) * T * 16));
+        __builtin_amdgcn_sched_barrier(0);  // issue in stage order: phases wait for their own
         C.c0[s][2 * h] = __uint_as_float(q.x);
         C.c1[s][2 * h] = __uint_as_float(q.y);
         C.c0[s][2 * h + 1] = __uint_as_float(q.z);
@@ -574,7 +608,7 @@ fwd_kernel(FwdParams P) {
       }
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
-      const uint4 q = buf_ld16(rt, (uint32_t)(((2 * (L - 1) + j) * T + t) * 16));
+      const uint4 q = buf_ld16s(rt, (uint32_t)(t * 16), (uint32_t)((2 * (L - 1) + j) * T * 16));
       C.last[j] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
                               __uint_as_float(q.w));
     }
@@ -587,21 +621,14 @@ fwd_kernel(FwdParams P) {
   for (int d = 0; d < S::PD; ++d)
     load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team, t);
   load_fast(P.tab.fgt);
-  int nan_seen = 0;
-#pragma unroll
-  for (int s = 0; s < L - 1; ++s)
-#pragma unroll
-    for (int j = 0; j < E / 2; ++j)  // bit test: the build assumes no NaN arithmetic
-      nan_seen |= (__float_as_uint(C.c0[s][j]) & 0x7fffffffu) > 0x7f800000u;
-  const bool shear = __builtin_amdgcn_readfirstlane(__syncthreads_or(nan_seen)) != 0;
-  // The two forms run as consecutive loops (the unused one over zero rows),
-  // not as two arms of a branch: the register allocator then never holds
-  // both coefficient sets at once.
-  row_loop<S, XBF16, YK, QM, true, true>(P, shear ? 0 : P.rows, lds, team, t, C, in);
-  if (shear) {
+  __builtin_amdgcn_sched_barrier(0);
+  // The two forms run as consecutive loops, not as two arms of a branch:
+  // the register allocator then never holds both coefficient sets at once.
+  const bool usable = row_loop<S, XBF16, YK, QM, true, true, true>(P, P.rows, lds, team, t, C, in);
+  if (!usable) {
     // Three-shear form, with the general quantizer for every format.
     load_coeffs(P.tab.lift, P.tab.last);
-    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false>(P, P.rows, lds, team, t, C, in);
+    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false, false>(P, P.rows, lds, team, t, C, in);
   }
 }
 
