@@ -67,6 +67,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base,
   const uint32_t n = bytes <= 0 ? 0u : (bytes >= (int64_t)kOutOfRange ? kOutOfRange : (uint32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
+// The same for a size known to fit 32 bits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range32(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Rows of row group grp (groups of cap rows) that lie below rows; 0 for a
+// negative group.  Written as 32-bit tests on the halves of the 64-bit
+// values, which keeps uniform arguments on the scalar unit (it has no
+// signed 64-bit compare).
+__device__ __forceinline__ int group_rows(int64_t rows, int64_t grp, int cap) {
+  const int64_t r = rows - grp * cap;
+  const int r_hi = (int)(r >> 32), g_hi = (int)(grp >> 32);
+  const uint32_t r_lo = (uint32_t)r;
+  return (g_hi < 0 || r_hi < 0) ? 0 : (r_hi > 0 || r_lo >= (uint32_t)cap) ? cap : (int)r_lo;
+}
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);

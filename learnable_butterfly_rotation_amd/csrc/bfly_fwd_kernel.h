@@ -121,9 +121,9 @@ __device__ __forceinline__ float group_min(float v, int gt) {
   return v;
 }
 
-// Quantize the E = 8 consecutive values one thread holds (part of a group
-// spread over gt = group/8 consecutive lanes).  Returns the packed codes and,
-// in `sz`, the fp16 scale bits (low half) and zero-point bits (high half).
+// Quantization of the E = 8 consecutive values one thread holds (part of a
+// group spread over gt = group/8 consecutive lanes), in two steps: the
+// group's parameters, then the codes.
 //
 // Scale: s16 = fp16(absmax / qmax) or fp16((max - min) / levels), the
 // quotient taken as a product with the fp32 reciprocal of the constant (it
@@ -133,9 +133,18 @@ __device__ __forceinline__ float group_min(float v, int gt) {
 // fma(y, r, 1.5*2^23 + bias): the exact product is rounded once, to an
 // integer, ties to even, and the low bits of the result's encoding are
 // q + bias.  Clamping y to [qlo*s16, qhi*s16] (products exact in fp32) is the
-// same as clamping q afterwards.
-__device__ __forceinline__ uint32_t quantize8(const float (&v)[8], int bits, int gt, bool asym,
-                                              float inv_top, float top, uint32_t& sz) {
+// same as clamping q afterwards.  The clamp changes a code only when some
+// y * r of the group rounds outside [qlo, qhi], which needs a scale that
+// lost precision (fp16 subnormal, or saturated at 65504): near_edge flags a
+// group within 1/4 of that (room to spare for the fp32 rounding of the
+// extremes' products), and callers may skip the clamp where no group is.
+struct QParams {
+  float r, clo, chi, z;
+  uint32_t sz;  // fp16 scale bits (low half), zero-point bits (high half)
+  bool near_edge;
+};
+__device__ __forceinline__ QParams quant_params(const float (&v)[8], int gt, bool asym, float inv_top,
+                                                float top) {
   float lo, hi;
   if (asym) {
     lo = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])), fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
@@ -151,40 +160,50 @@ __device__ __forceinline__ uint32_t quantize8(const float (&v)[8], int bits, int
   const float s_pre = fminf((hi - lo) * inv_top, 65504.f);  // saturate to the largest finite fp16
   const _Float16 s16 = (_Float16)s_pre;
   const float sc = (float)s16;
-  float r = 0.f, clo = 0.f, chi = 0.f, z = 0.f;
+  QParams q;
+  q.r = q.clo = q.chi = q.z = 0.f;
   if (sc != 0.f) {
-    r = __builtin_amdgcn_rcpf(sc);
-    r = fmaf(fmaf(-sc, r, 1.0f), r, r);
+    q.r = __builtin_amdgcn_rcpf(sc);
+    q.r = fmaf(fmaf(-sc, q.r, 1.0f), q.r, q.r);
     if (asym) {
-      z = __builtin_amdgcn_fmed3f(rintf(-lo * r), 0.f, top);
-      clo = -z * sc;
-      chi = (top - z) * sc;
+      q.z = __builtin_amdgcn_fmed3f(rintf(-lo * q.r), 0.f, top);
+      q.clo = -q.z * sc;
+      q.chi = (top - q.z) * sc;
     } else {
-      clo = -top * sc;
-      chi = top * sc;
+      q.clo = -top * sc;
+      q.chi = top * sc;
     }
   }
-  sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)z) << 16);
+  q.sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q.z) << 16);
+  // z and top are small integers: the bounds are exact.
+  q.near_edge = hi * q.r > (top - q.z) + 0.25f || lo * q.r < -q.z - 0.25f;
+  return q;
+}
+__device__ __forceinline__ void quant_clamp(float (&v)[8], const QParams& q) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __builtin_amdgcn_fmed3f(v[e], q.clo, q.chi);
+}
+// The packed codes of v, already clamped (or known not to need it).
+__device__ __forceinline__ uint32_t quant_pack(const float (&v)[8], const QParams& q, int bits, bool asym) {
   uint32_t packed;
   if (!asym && bits == 4) {
     // biased nibbles q + 8 in 1..15, two per byte, then two's complement by ^8
     uint32_t f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      f[e] = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f(v[e], clo, chi), r, 12582920.0f));
+    for (int e = 0; e < 8; ++e) f[e] = __float_as_uint(fmaf(v[e], q.r, 12582920.0f));
     const uint32_t p0 = (f[1] << 4) | f[0], p1 = (f[3] << 4) | f[2];
     const uint32_t p2 = (f[5] << 4) | f[4], p3 = (f[7] << 4) | f[6];
     const uint32_t w01 = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
     const uint32_t w23 = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
     packed = (w01 | w23) ^ 0x88888888u;
   } else {
-    const uint32_t off = (uint32_t)z - 0x4B400000u;
+    const uint32_t off = (uint32_t)q.z - 0x4B400000u;
     const uint32_t mask = (1u << bits) - 1u;
     packed = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = fmaf(__builtin_amdgcn_fmed3f(v[e], clo, chi), r, 12582912.0f);
+      const float f = fmaf(v[e], q.r, 12582912.0f);
       packed |= ((__float_as_uint(f) + off) & mask) << (bits * e);
     }
   }
@@ -232,10 +251,9 @@ __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t row
   constexpr int N = S::N, NB = S::NB, E = S::E, RPP = S::ROWS_PER_PASS;
   constexpr int RPT = S::ROWS_PER_PASS / S::R, M = S::SEGS / RPT;
   constexpr int RAW = InRegs<S, XBF16>::RAW, ESZ = XBF16 ? 2 : 4;
-  const int64_t r = rows - grp * RPP;
-  const int64_t valid = grp < 0 ? 0 : (r < 0 ? 0 : (r > RPP ? RPP : r));
-  const auto rs = buffer_range(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * N) * ESZ,
-                               valid * N * ESZ);
+  const uint32_t valid = (uint32_t)group_rows(rows, grp, RPP);
+  const auto rs = buffer_range32(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * N) * ESZ,
+                                 valid * (uint32_t)(N * ESZ));
   const int thr_elem = team * RPT * N + t * E;
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr)
@@ -290,10 +308,6 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // can keep every prefetch in flight.
   constexpr int64_t GRP_ELEMS = (int64_t)RPP * N;
   const int thr_elem = team * RPT * N + t * E;  // element offset of (team, t) in a group
-  auto valid_rows = [&](int64_t grp) -> int64_t {
-    const int64_t r = rows - grp * RPP;
-    return grp < 0 ? 0 : (r < 0 ? 0 : (r > RPP ? RPP : r));
-  };
 
   constexpr int PD = S::PD;
   auto& cur = in.r;
@@ -315,12 +329,12 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   auto flush = [&](const float (&w)[SEGS][E]) {
     if (YK == Y_NONE && !QUANT) return;
     const int64_t hg = held_grp;
-    const int64_t vr = valid_rows(hg);
-    const auto ry = buffer_range(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * N * 2);
-    const auto ry4 = buffer_range(reinterpret_cast<const float*>(P.y) + hg * GRP_ELEMS, vr * N * 4);
-    const auto rc = buffer_range(P.codes + hg * (GRP_ELEMS * bits / 8), vr * N * bits / 8);
-    const auto rsc = buffer_range(P.scales + hg * RPP * ngroups_row, vr * ngroups_row * 2);
-    const auto rz = buffer_range(P.zeros + hg * RPP * ngroups_row, vr * ngroups_row * 2);
+    const uint32_t vr = (uint32_t)group_rows(rows, hg, RPP);  // at most RPP rows: 32-bit sizes
+    const auto ry = buffer_range32(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * (N * 2));
+    const auto ry4 = buffer_range32(reinterpret_cast<const float*>(P.y) + hg * GRP_ELEMS, vr * (N * 4));
+    const auto rc = buffer_range32(P.codes + hg * (GRP_ELEMS * bits / 8), vr * (uint32_t)(N * bits / 8));
+    const auto rsc = buffer_range32(P.scales + hg * RPP * ngroups_row, vr * (uint32_t)(ngroups_row * 2));
+    const auto rz = buffer_range32(P.zeros + hg * RPP * ngroups_row, vr * (uint32_t)(ngroups_row * 2));
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
@@ -396,12 +410,38 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
 #pragma unroll
       for (int sg = 0; sg < SEGS; ++sg)
 #pragma unroll
-        for (int k = 0; k < E / 2; ++k) held_y[sg][k] = pack_bf16(w[sg][2 * k], w[sg][2 * k + 1]);
+        for (int k = 0; k < E / 2; ++k) {
+          held_y[sg][k] = pack_bf16(w[sg][2 * k], w[sg][2 * k + 1]);
+          // packed here, so the unclamped values die before the clamp below
+          asm volatile("" : "+v"(held_y[sg][k]));
+        }
     }
     if (QUANT) {
+      QParams qp[SEGS];
+      bool near_edge = false;
 #pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-        held_c[sg] = quantize8(w[sg], bits, gt, asym, inv_top, top, held_sz[sg]);
+      for (int sg = 0; sg < SEGS; ++sg) {
+        qp[sg] = quant_params(w[sg], gt, asym, inv_top, top);
+        near_edge |= qp[sg].near_edge;
+        held_sz[sg] = qp[sg].sz;
+      }
+      if (YK == Y_F32) {  // the rows are stored as they are: clamp copies
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) {
+          float c[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) c[e] = w[sg][e];
+          quant_clamp(c, qp[sg]);
+          held_c[sg] = quant_pack(c, qp[sg], bits, asym);
+        }
+      } else {  // one wave-uniform test for every segment, the clamp in place
+        if (__builtin_amdgcn_ballot_w64(near_edge) != 0) {
+#pragma unroll
+          for (int sg = 0; sg < SEGS; ++sg) quant_clamp(w[sg], qp[sg]);
+        }
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) held_c[sg] = quant_pack(w[sg], qp[sg], bits, asym);
+      }
     }
   };
 

@@ -367,6 +367,37 @@ def test_degenerate_groups():
         assert (out["scales"][2] == 0x7BFF).all()
 
 
+@pytest.mark.parametrize("n", [256, 4096])
+def test_fixed_formats_scale_edges(n):
+    """The fixed formats (sym INT4 and asym INT2, groups of 128, bf16 rows)
+    skip the code clamp in waves where no group's fp16 scale lost precision.
+    Groups here have fp16-subnormal scales (codes that must saturate), a
+    saturated scale, zero, or ordinary values, side by side in some rows;
+    the last two rows hold only ordinary groups."""
+    rng = np.random.default_rng(70 + n)
+    L = int(math.log2(n))
+    th = np.zeros((L, n // 2), np.float32)  # identity: each group keeps its values
+    rows, ng = 6, n // 128
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    tiny = 2.0 ** -24  # fp16's smallest subnormal
+    for r in range(rows - 2):
+        for gi in range(ng):
+            grp = x[r, gi * 128:(gi + 1) * 128]
+            kind = (r + gi) % 4
+            if kind == 1:  # max|y| / 7 between 0.4 and 3 subnormal steps
+                grp *= rng.uniform(3.0, 20.0) * tiny / np.abs(grp).max()
+            elif kind == 2:
+                grp *= 1e9 / np.abs(grp).max()
+            elif kind == 3:
+                grp[:] = 0.0
+    xb = inputs.f32_to_bf16_bits(x)
+    y64 = oracle.forward(xb, th)
+    for bits, mode in ((4, 0), (2, 1)):
+        out = run_quant(xb, th, bits, 128, mode)
+        assert_forward(out["y"], y64, xb, n)
+        assert_quant(out, y64, bits, 128, mode)
+
+
 # ---------------------------------------------------------------------------
 # backward
 # ---------------------------------------------------------------------------
