@@ -337,9 +337,7 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   sincos_of_float(theta[k], sn, cn);
   const Table tab = table_at(table, logn);
   float2* cs = const_cast<float2*>(tab.cs);
-  float4* fgt = const_cast<float4*>(tab.fgt);
-  int slot_j = 0;
-  const int64_t slot = fwd_pair_slot(s, p, logn, slot_j);
+  float* fgt = reinterpret_cast<float*>(const_cast<float4*>(tab.fgt));
   float2* lift = const_cast<float2*>(tab.lift);
   float4* last = const_cast<float4*>(tab.last);
   // Both elements' histories through stages s2 < s: the sign parity (three-
@@ -398,14 +396,19 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
     const double lim = 5.421010862427522e-20;  // 2^-64
     const bool ok = fabs(cn * sig_i) >= lim && fabs(cn * sig_j) >= lim;
     const float nan = __uint_as_float(0x7fc00000u);  // a quiet NaN, as bits
-    reinterpret_cast<float2*>(fgt)[2 * slot + (slot_j & 1)] =
-        ok ? make_float2((float)(-tn * (sig_j / sig_i)), (float)(tn * (sig_i / sig_j)))
-           : make_float2(nan, nan);
+    fgt[fwd_coef_index(s, i, logn)] = ok ? (float)(-tn * (sig_j / sig_i)) : nan;
+    fgt[fwd_coef_index(s, j, logn)] = ok ? (float)(tn * (sig_i / sig_j)) : nan;
   } else {
     const double si = par_i ? -1.0 : 1.0, sj = par_j ? -1.0 : 1.0;
     last[p] = make_float4((float)(cn * si), (float)(-sn * sj), (float)(sn * si), (float)(cn * sj));
-    fgt[slot] = make_float4((float)(cn * sig_i), (float)(-sn * sig_j), (float)(sn * sig_i),
-                           (float)(cn * sig_j));
+    const float ki = (float)(cn * sig_i), kij = (float)(-sn * sig_j);
+    const float kji = (float)(sn * sig_i), kj = (float)(cn * sig_j);
+    if (fwd_plan(logn).SA < logn) {  // a register pair: its 2x2 matrix
+      *reinterpret_cast<float4*>(fgt + fwd_last_index(i, logn)) = make_float4(ki, kij, kji, kj);
+    } else {  // lane-mapped: each element's (own, partner) weights
+      *reinterpret_cast<float2*>(fgt + fwd_last_index(i, logn)) = make_float2(ki, kij);
+      *reinterpret_cast<float2*>(fgt + fwd_last_index(j, logn)) = make_float2(kj, kji);
+    }
   }
 }
 

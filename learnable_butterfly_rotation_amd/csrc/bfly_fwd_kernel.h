@@ -71,7 +71,88 @@ struct FwdShape {
   }
   // one buffer for wave-local transposes, two alternating ones for the rest
   static constexpr size_t LDS_BYTES = (any_global() ? 3ull : 1ull) * BUFW * sizeof(float);
+
+  // The scaled form's two-phase plan (lane-mapped stages through DPP; see
+  // FwdPlan): transposes A -> B and B -> A, wave-local when a team fits in
+  // one wave.  LDS word of element i: i plus PADB pad words per 128, which
+  // spreads phase B's lane-mapped bits (element bits SA.., offsets of 128)
+  // over distinct banks.
+  static constexpr FwdPlan PL = fwd_plan(L);
+  static constexpr bool TWO = PL.SA < L;
+  static constexpr bool LOCAL2 = T <= 64;
+  static constexpr int PADB = PL.DB == 0 ? 0 : (64 >> PL.DB);
+  static constexpr int SEGW2 = NB + PADB * (NB >> 7);
+  static constexpr int BUF2W = R * SEGS * SEGW2;
+  static_assert((TWO ? (LOCAL2 ? 1 : 2) * BUF2W : 0) * sizeof(float) <= LDS_BYTES,
+                "the two-phase buffers fit the allocation of the three-shear form");
 };
+
+// LDS word of element i in the two-phase transposes.
+template <class S>
+__device__ __forceinline__ constexpr int lds2(int i) { return i + S::PADB * (i >> 7); }
+
+// A lane-mapped stage of the scaled form on a thread's 8 registers: each
+// lane adds k_e times its partner lane's register e (the partner reached by
+// the DPP control; every lane reads the old values).  One v_fmac_f32_dpp per
+// element, as in inline assembly: the compiler does not fold a DPP move into
+// a multiply-add.  s_nop 1 first: a DPP operand must not have been written
+// by a VALU instruction in the two issue slots before (within the block each
+// source was last written a full stage earlier).
+#define BFLY_DPP_OP(I, D, S, K, CTRL) \
+  "v_fmac_f32_dpp %" #D ", %" #S ", %" #K " " CTRL " row_mask:0xf bank_mask:0xf\n"
+// In place: register e's own DPP source is register e.
+#define BFLY_LANE_FMA8_IP(CTRL, V, K)                                                            \
+  asm("s_nop 1\n" BFLY_DPP_OP(0, 0, 0, 8, CTRL) BFLY_DPP_OP(1, 1, 1, 9, CTRL)                   \
+          BFLY_DPP_OP(2, 2, 2, 10, CTRL) BFLY_DPP_OP(3, 3, 3, 11, CTRL)                           \
+              BFLY_DPP_OP(4, 4, 4, 12, CTRL) BFLY_DPP_OP(5, 5, 5, 13, CTRL)                       \
+                  BFLY_DPP_OP(6, 6, 6, 14, CTRL) BFLY_DPP_OP(7, 7, 7, 15, CTRL)                   \
+      : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), "+v"(V[6]),     \
+        "+v"(V[7])                                                                                \
+      : "v"(K[0]), "v"(K[1]), "v"(K[2]), "v"(K[3]), "v"(K[4]), "v"(K[5]), "v"(K[6]), "v"(K[7]))
+// Into separate accumulators.
+#define BFLY_LANE_FMA8_ACC(CTRL, ACC, SRC, K)                                                    \
+  asm("s_nop 1\n" BFLY_DPP_OP(0, 0, 8, 16, CTRL) BFLY_DPP_OP(1, 1, 9, 17, CTRL)                 \
+          BFLY_DPP_OP(2, 2, 10, 18, CTRL) BFLY_DPP_OP(3, 3, 11, 19, CTRL)                         \
+              BFLY_DPP_OP(4, 4, 12, 20, CTRL) BFLY_DPP_OP(5, 5, 13, 21, CTRL)                     \
+                  BFLY_DPP_OP(6, 6, 14, 22, CTRL) BFLY_DPP_OP(7, 7, 15, 23, CTRL)                 \
+      : "+v"(ACC[0]), "+v"(ACC[1]), "+v"(ACC[2]), "+v"(ACC[3]), "+v"(ACC[4]), "+v"(ACC[5]),     \
+        "+v"(ACC[6]), "+v"(ACC[7])                                                                \
+      : "v"(SRC[0]), "v"(SRC[1]), "v"(SRC[2]), "v"(SRC[3]), "v"(SRC[4]), "v"(SRC[5]),           \
+        "v"(SRC[6]), "v"(SRC[7]), "v"(K[0]), "v"(K[1]), "v"(K[2]), "v"(K[3]), "v"(K[4]),         \
+        "v"(K[5]), "v"(K[6]), "v"(K[7]))
+// The DPP control of lane-map mask j: j = 0, 1: quad permutes (lane ^ 1,
+// lane ^ 2); j = 2: half-row mirror (lane ^ 7); j = 3: row mirror (lane ^ 15).
+#define BFLY_DPP_SWITCH(J, MACRO, ...)                          \
+  switch (J) {                                                  \
+    case 0: MACRO("quad_perm:[1,0,3,2]", __VA_ARGS__); break;    \
+    case 1: MACRO("quad_perm:[2,3,0,1]", __VA_ARGS__); break;    \
+    case 2: MACRO("row_half_mirror", __VA_ARGS__); break;        \
+    default: MACRO("row_mirror", __VA_ARGS__); break;            \
+  }
+
+// A lane-mapped stage s < L-1, on lane-map bit j.
+__device__ __forceinline__ void lane_stage(int j, float (&v)[8], const float (&c0)[4],
+                                           const float (&c1)[4]) {
+  float k[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) k[e] = (e & 1) ? c1[e >> 1] : c0[e >> 1];
+  BFLY_DPP_SWITCH(j, BFLY_LANE_FMA8_IP, v, k)
+}
+// The last stage on a lane-mapped bit: y_e = a_e w_e + b_e w_partner, with
+// last[h] = (a_2h, b_2h, a_2h+1, b_2h+1).
+__device__ __forceinline__ void lane_last(int j, float (&v)[8], const float4 (&last)[4]) {
+  float acc[8], b[8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    acc[2 * h] = last[h].x * v[2 * h];
+    acc[2 * h + 1] = last[h].z * v[2 * h + 1];
+    b[2 * h] = last[h].y;
+    b[2 * h + 1] = last[h].w;
+  }
+  BFLY_DPP_SWITCH(j, BFLY_LANE_FMA8_ACC, acc, v, b)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = acc[e];
+}
 
 // One of stages 0..L-2 on the pair (a, b): two fused multiply-adds on the
 // stored values in the scaled form (c0 = beta, c1 = gamma), else three
@@ -244,17 +325,18 @@ struct InRegs {
 
 // Issue the loads of row group grp into prefetch slot d, through a buffer
 // resource covering exactly the group's valid rows (none past the end).
+// elem0: the element of the thread's register 0 within its row segment.
 template <class S, bool XBF16>
 __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t rows, const int64_t grp,
                                            InRegs<S, XBF16>& in, const int d, const int team,
-                                           const int t) {
+                                           const int elem0) {
   constexpr int N = S::N, NB = S::NB, E = S::E, RPP = S::ROWS_PER_PASS;
   constexpr int RPT = S::ROWS_PER_PASS / S::R, M = S::SEGS / RPT;
   constexpr int RAW = InRegs<S, XBF16>::RAW, ESZ = XBF16 ? 2 : 4;
   const uint32_t valid = (uint32_t)group_rows(rows, grp, RPP);
   const auto rs = buffer_range32(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * N) * ESZ,
                                  valid * (uint32_t)(N * ESZ));
-  const int thr_elem = team * RPT * N + t * E;
+  const int thr_elem = team * RPT * N + elem0;
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
@@ -307,11 +389,15 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // ranges, so no memory instruction sits under a branch and the compiler
   // can keep every prefetch in flight.
   constexpr int64_t GRP_ELEMS = (int64_t)RPP * N;
-  const int thr_elem = team * RPT * N + t * E;  // element offset of (team, t) in a group
+  // Element of the thread's register 0 within a row segment: the two-phase
+  // plan's layout A for the scaled form, register-contiguous blocks for the
+  // three-shear form.
+  const int elem0 = FAST ? fwd_elem_a(t, 0, S::PL) : t * E;
+  const int thr_elem = team * RPT * N + elem0;  // element offset of (team, t) in a group
 
   constexpr int PD = S::PD;
   auto& cur = in.r;
-  auto load = [&](int64_t grp, int d) { load_group<S, XBF16>(P, rows, grp, in, d, team, t); };
+  auto load = [&](int64_t grp, int d) { load_group<S, XBF16>(P, rows, grp, in, d, team, elem0); };
 
   // The previous row group's outputs: bf16 rows, codes and scales (and, for
   // fp32 output, its rows), stored only once the next group's input has
@@ -357,7 +443,7 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
         if (QUANT) {
           if (bits == 4) buf_st4(rc, el / 2, held_c[sg]);
           else buf_st2(rc, el / 4, (uint16_t)held_c[sg]);
-          const uint32_t gi = (uint32_t)((team * RPT + rr) * ngroups_row + ((a * NB + t * E) >> lg_group));
+          const uint32_t gi = (uint32_t)((team * RPT + rr) * ngroups_row + ((a * NB + elem0) >> lg_group));
           const uint32_t off = scale_lane ? 2 * gi : kOutOfRange;
           buf_st2(rsc, off, (uint16_t)held_sz[sg]);
           if (asym) buf_st2(rz, off, (uint16_t)(held_sz[sg] >> 16));
@@ -374,11 +460,88 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // The last transpose of a row group leaves its rows in layout 0 in this
   // buffer; the next slot (or the epilogue) reads them there.
   float* const fin_buf = S::local_transpose(NPH) ? lbuf : ((S::final_gidx() & 1) ? gbuf1 : gbuf0);
+  // Two-phase plan (scaled form): A -> B through abuf, B -> A through bbuf
+  // (the same buffer when a team is one wave's: its LDS accesses stay in
+  // order).  One-phase rows keep their results in registers (fin).
+  constexpr int SEGW2 = S::SEGW2;
+  float* const abuf = lds + team * (SEGS * SEGW2);
+  float* const bbuf = S::LOCAL2 ? abuf : lds + S::BUF2W + team * (SEGS * SEGW2);
+  const int ea = lds2<S>(elem0);
+  const int eb = lds2<S>(fwd_elem_b(t, 0, S::PL));
+  float fin[SEGS][E];
+#pragma unroll
+  for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+    for (int e = 0; e < E; ++e) fin[sg][e] = 0.f;
+  auto get_a = [&](const float* buf, float (&x)[E]) {
+    const float4 q0 = *reinterpret_cast<const float4*>(buf + ea);
+    const float4 q1 = *reinterpret_cast<const float4*>(buf + ea + 4);
+    x[0] = q0.x; x[1] = q0.y; x[2] = q0.z; x[3] = q0.w;
+    x[4] = q1.x; x[5] = q1.y; x[6] = q1.z; x[7] = q1.w;
+  };
+  auto put_a = [&](float* buf, const float (&x)[E]) {
+    *reinterpret_cast<float4*>(buf + ea) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(buf + ea + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  };
+  auto get_b = [&](const float* buf, float (&x)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = buf[eb + lds2<S>(e << (L - 3))];
+  };
+  auto put_b = [&](float* buf, const float (&x)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) buf[eb + lds2<S>(e << (L - 3))] = x[e];
+  };
+  auto sync2 = [&]() {
+    if (S::LOCAL2) wave_lds_sync();
+    else __syncthreads();
+  };
   auto read_final = [&](float (&w)[SEGS][E]) {
+    if (FAST) {
+      if (S::TWO) {
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) get_a(bbuf + sg * SEGW2, w[sg]);
+        if (S::LOCAL2) wave_lds_sync();
+      } else {
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+          for (int e = 0; e < E; ++e) w[sg][e] = fin[sg][e];
+      }
+      return;
+    }
 #pragma unroll
     for (int sg = 0; sg < SEGS; ++sg)
       lds_get1<LOGE, SEGW>(fin_buf + sg * SEGW, w[sg], t, 0, S::id_transpose(NPH));
     if (S::local_transpose(NPH)) wave_lds_sync();
+  };
+  // Scaled form, two-phase plan: the stages of phase A and of phase B.
+  auto phase_a = [&](float (&x)[E]) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j) {
+        const int lo = pair_lo(j, s), hi = lo | (1 << s);
+        rotate<true>(x[lo], x[hi], C.c0[s][j], C.c1[s][j]);
+      }
+#pragma unroll
+    for (int s = 3; s < S::PL.SA; ++s) {
+      if (s < L - 1) lane_stage(s - 3, x, C.c0[s], C.c1[s]);
+      else lane_last(s - 3, x, C.last);
+    }
+  };
+  auto phase_b = [&](float (&x)[E]) {
+#pragma unroll
+    for (int s = S::PL.SA; s < L - 3; ++s) lane_stage(s - S::PL.SA, x, C.c0[s], C.c1[s]);
+#pragma unroll
+    for (int s = (S::PL.SA > L - 3 ? S::PL.SA : L - 3); s < L; ++s) {
+      const int q = s - (L - 3);
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j) {
+        const int lo = pair_lo(j, q), hi = lo | (1 << q);
+        if (s < L - 1) rotate<true>(x[lo], x[hi], C.c0[s][j], C.c1[s][j]);
+        else last2x2(x[lo], x[hi], C.last[j]);
+      }
+    }
   };
   // Everything the previous group still needs before its stores: the
   // Kronecker mix, bf16 packing and quantization.
@@ -489,6 +652,40 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
       for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[sg][e])::"memory");
     load(grp + PD * G, d);  // past the end: an empty range, no traffic
     finish(w);
+    if (FAST) {
+      // Phase A per segment, its rows written for the transpose (the LDS
+      // traffic of one segment overlaps the arithmetic of the next); the
+      // previous group's stores once the transpose's barrier is passed;
+      // phase B per segment, written back in layout A for the next slot.
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg) {
+        phase_a(v[sg]);
+        if (S::TWO) put_a(abuf + sg * SEGW2, v[sg]);
+        if (SEGS > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (S::TWO) {
+        sync2();
+        flush(w);
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) get_b(abuf + sg * SEGW2, v[sg]);
+        if (S::LOCAL2) wave_lds_sync();
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) {
+          phase_b(v[sg]);
+          put_b(bbuf + sg * SEGW2, v[sg]);
+          if (SEGS > 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        sync2();
+      } else {
+        flush(w);
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg)
+#pragma unroll
+          for (int e = 0; e < E; ++e) fin[sg][e] = v[sg][e];
+      }
+      held_grp = grp;
+      return;
+    }
     // Phase k: [sync for transpose k] -> read every segment -> per segment:
     // rotate, then write it for transpose k+1.  Segment by segment (kept in
     // that order by scheduling barriers), the LDS traffic of one segment
@@ -659,7 +856,8 @@ fwd_kernel(FwdParams P) {
   InRegs<S, XBF16> in;
 #pragma unroll
   for (int d = 0; d < S::PD; ++d)
-    load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team, t);
+    load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team,
+                         fwd_elem_a(t, 0, S::PL));  // the scaled form's layout A
   load_fast(P.tab.fgt);
   __builtin_amdgcn_sched_barrier(0);
   // The two forms run as consecutive loops, not as two arms of a branch:

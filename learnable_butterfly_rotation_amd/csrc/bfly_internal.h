@@ -17,14 +17,10 @@ enum YKind : int { Y_NONE = -1, Y_F32 = 0, Y_BF16 = 1 };
 //   fgt   float4 [2(L+1)][n/8] the scaled form, in forward-thread order:
 //                             row q of thread t holds what the forward
 //                             kernel's thread t loads q-th, so that every
-//                             load of a wave is one contiguous 1 KiB run.
-//                             Rows 2s and 2s+1 (s < L-1): (beta, gamma) of
-//                             the thread's pairs 0,1 and 2,3 of stage s;
-//                             rows 2(L-1)+j: the last stage of its pair j
-//                             with the scales folded in.  (Thread t of a
-//                             forward phase with base bit b holds the eight
-//                             elements whose bits b..b+2 vary; fwd_pair_slot
-//                             gives the place of each pair.)
+//                             load of a wave is one contiguous 1 KiB run:
+//                             8 floats per stage s < L-1, 16 for the last
+//                             one with the scales folded in (fwd_coef_index
+//                             and fwd_last_index give the places).
 //   lift  float2 [L-1][half]  (p, u): stages 0..L-2 as three shears
 //   last  float4 [half]       the last stage with the tracked signs folded in
 //
@@ -76,23 +72,89 @@ __host__ __device__ inline Table table_at(const void* base, int logn) {
   return t;
 }
 
-// Place of pair (s, p) in fgt: the forward kernel gives stage s to phase
-// s / 3, whose base bit is b = min(3 (s / 3), L - 3); thread t holds the
-// elements with t's bits below b, e at bits b..b+2 and t's other bits above,
-// and its pair slot j is e without the pair bit s - b.  Returns the float4
-// row (2s + j/2 for s < L-1, 2(L-1) + j for the last stage) times n/8 plus
-// t, and sets j.
-__host__ __device__ inline int64_t fwd_pair_slot(int s, int p, int logn, int& j) {
-  const int i = ((p >> s) << (s + 1)) | (p & ((1 << s) - 1));  // lower element
-  const int k = s / 3;
-  const int b = (3 * k < logn - 3) ? 3 * k : logn - 3;
-  const int e = (i >> b) & 7;
-  const int t = (i & ((1 << b) - 1)) | ((i >> (b + 3)) << b);
-  const int q = s - b;
-  j = ((e >> (q + 1)) << q) | (e & ((1 << q) - 1));
-  const int64_t T = (int64_t)1 << (logn - 3);
-  const int row = s < logn - 1 ? 2 * s + (j >> 1) : 2 * (logn - 1) + j;
-  return row * T + t;
+// Forward layouts of the scaled form.  A row goes to a team of T = n/8
+// threads holding 8 elements each, in at most two phases.  A phase rotates
+// element bits that are either register bits (the thread's 8 elements) or
+// lane bits that one DPP lane swap reaches: within 16-lane rows, xor masks
+// 1 and 2 (quad permutes), 7 (half-row mirror) and 15 (row mirror).  The
+// lane-mapped element bits c_0.. sit on lane bits 0..3 through the linear
+// map lane = XOR of mask_j over the c_j set (dpp_mix), so a stage on c_j
+// pairs lane l with l ^ mask_j, and c_0..c_{k-1} range over lanes 0..2^k-1.
+//   phase A: stages 0..SA-1; register bits 0..2, lane-mapped bits 3..SA-1,
+//            thread bits above DL on element bits SA..
+//   phase B: stages SA..L-1; register bits L-3..L-1, lane-mapped bits
+//            SA..L-4, the other thread bits on element bits 0..SA-1
+// with DL = min(4, L-3) lane-mapped bits at most and SA = min(L, 3 + DL).
+// Rows of up to 128 elements need one phase; the others, two transposes.
+__host__ __device__ constexpr int dpp_mix(int c) {
+  return ((c & 1) ? 1 : 0) ^ ((c & 2) ? 2 : 0) ^ ((c & 4) ? 7 : 0) ^ ((c & 8) ? 15 : 0);
+}
+__host__ __device__ constexpr int dpp_unmix(int l) {
+  const int l0 = l & 1, l1 = (l >> 1) & 1, l2 = (l >> 2) & 1, l3 = (l >> 3) & 1;
+  return (l0 ^ l2) | ((l1 ^ l2) << 1) | ((l2 ^ l3) << 2) | (l3 << 3);
+}
+struct FwdPlan {
+  int L, DL, SA, DB;
+};
+__host__ __device__ constexpr FwdPlan fwd_plan(int L) {
+  const int DL = L - 3 < 4 ? L - 3 : 4;
+  const int SA = L < 3 + DL ? L : 3 + DL;
+  const int DB = L - 3 - SA > 0 ? L - 3 - SA : 0;
+  return FwdPlan{L, DL, SA, DB};
+}
+__host__ __device__ constexpr int fwd_elem_a(int t, int e, FwdPlan p) {
+  return e | (dpp_unmix(t & ((1 << p.DL) - 1)) << 3) | ((t >> p.DL) << (3 + p.DL));
+}
+__host__ __device__ constexpr int fwd_elem_b(int t, int e, FwdPlan p) {
+  return (e << (p.L - 3)) | (dpp_unmix(t & ((1 << p.DB) - 1)) << p.SA) | (t >> p.DB);
+}
+// Inverses: the thread and register of element i.
+__host__ __device__ inline void fwd_place_a(int i, FwdPlan p, int& t, int& e) {
+  e = i & 7;
+  t = dpp_mix((i >> 3) & ((1 << p.DL) - 1)) | ((i >> (3 + p.DL)) << p.DL);
+}
+__host__ __device__ inline void fwd_place_b(int i, FwdPlan p, int& t, int& e) {
+  e = i >> (p.L - 3);
+  const int r = i & ((1 << (p.L - 3)) - 1);
+  t = dpp_mix((r >> p.SA) & ((1 << p.DB) - 1)) | ((r & ((1 << p.SA) - 1)) << p.DB);
+}
+// Float index in fgt of the coefficient stage s < L-1 applies at element i
+// (beta at its pair's lower element, gamma at the upper one).  Each stage
+// fills 8 floats of every thread, rows 2s and 2s+1: on register bit q, pair
+// slot j (the register pair (j with a zero inserted at bit q, and | 2^q))
+// holds (beta, gamma) at floats 2j, 2j+1; on a lane-mapped bit, float e is
+// register e's own coefficient.
+__host__ __device__ inline int64_t fwd_coef_index(int s, int i, int L) {
+  const FwdPlan p = fwd_plan(L);
+  const bool in_a = s < p.SA;
+  int t, e;
+  if (in_a) fwd_place_a(i, p, t, e);
+  else fwd_place_b(i, p, t, e);
+  const bool reg = in_a ? s < 3 : s >= L - 3;
+  int comp = e;
+  if (reg) {
+    const int q = in_a ? s : s - (L - 3);
+    const int j = ((e >> (q + 1)) << q) | (e & ((1 << q) - 1));
+    comp = 2 * j + ((e >> q) & 1);
+  }
+  const int64_t T = (int64_t)1 << (L - 3);
+  return ((2 * s + (comp >> 2)) * T + t) * 4 + (comp & 3);
+}
+// The last stage, 16 floats per thread in rows 2(L-1)..2(L-1)+3.  In phase
+// B (register bit 2): pair slot j's 2x2 matrix (k.x, k.y, k.z, k.w) as
+// row 2(L-1)+j; returns the index of its first float, i the lower element.
+// In phase A (one-phase rows, a lane-mapped bit): element e's (a, b) of
+// y_e = a w_e + b w_partner at floats 2e, 2e+1; returns the index of a.
+__host__ __device__ inline int64_t fwd_last_index(int i, int L) {
+  const FwdPlan p = fwd_plan(L);
+  const int64_t T = (int64_t)1 << (L - 3);
+  int t, e;
+  if (p.SA < L) {
+    fwd_place_b(i, p, t, e);
+    return ((2 * (L - 1) + (e & 3)) * T + t) * 4;
+  }
+  fwd_place_a(i, p, t, e);
+  return ((2 * (L - 1) + (e >> 1)) * T + t) * 4 + 2 * (e & 1);
 }
 
 // Everything one forward launch needs.  tab is the prepared table of the
