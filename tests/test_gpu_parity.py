@@ -304,7 +304,7 @@ def _table_uses_scaled_form(theta, n):
     return not np.isnan(fg).any()
 
 
-@pytest.mark.parametrize("n", [256, 4096])
+@pytest.mark.parametrize("n", [128, 256, 4096])
 def test_three_shear_form_for_right_angles(n):
     """Angles of exactly +-pi/2 (as fp32) on every pair: the scaled form's
     scales would shrink by ~4e-8 per stage, so the table falls back to the
@@ -325,15 +325,16 @@ def test_three_shear_form_for_right_angles(n):
     assert_forward(host(y), oracle.forward(xf, th), xf, n)
 
 
-@pytest.mark.parametrize("n", [256, 4096])
+@pytest.mark.parametrize("n", [128, 256, 1024, 4096])
 def test_scaled_form_with_near_right_angles(n):
-    """Two stages of angles 1e-3..3e-3 away from +-pi/2 (scales shrink by
-    ~1e-3 per such stage, still in range): the scaled form stays in use, with
+    """Three stages of angles 1e-3..3e-3 away from +-pi/2 (scales shrink by
+    ~1e-3 per such stage, still in range), on register and lane-mapped bits
+    of the forward's two phases: the scaled form stays in use, with
     coefficients up to ~1e3 times larger; results must match the oracle."""
     L = int(math.log2(n))
     rng = np.random.default_rng(80 + n)
     th = inputs.angles(rng, n)
-    for s in (0, L - 3):
+    for s in sorted({0, 4, L - 3}):
         off = rng.uniform(1e-3, 3e-3, n // 2) * np.sign(rng.standard_normal(n // 2))
         th[s] = (np.sign(rng.standard_normal(n // 2)) * (math.pi / 2) + off).astype(np.float32)
     assert _table_uses_scaled_form(th, n)
