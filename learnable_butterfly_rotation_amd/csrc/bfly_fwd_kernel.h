@@ -74,14 +74,28 @@ struct FwdShape {
 
   // The scaled form's two-phase plan (lane-mapped stages through DPP; see
   // FwdPlan): transposes A -> B and B -> A, wave-local when a team fits in
-  // one wave.  LDS word of element i: i plus PADB pad words per 128, which
-  // spreads phase B's lane-mapped bits (element bits SA.., offsets of 128)
-  // over distinct banks.
+  // one wave.  LDS word of element i (lds2):
+  //   i + 4 (i >> 5) + PADB (i >> 7) + PADE (i >> (L-3)).
+  // The LDS serves 32 lanes of a 4-byte access, or 8 of a 16-byte one, per
+  // pass over 32 banks.  Layout A's 16-byte accesses (8 elements per lane,
+  // 8 lanes at element bits 3..5) need the 4 words per 32; layout B's 4-byte
+  // accesses (32 lanes: element bits 0.. plus the lane-mapped bits SA..,
+  // 128 apart) need lane-mapped blocks an odd multiple of 8 (DB = 2) or of 4
+  // (DB = 3) banks apart, hence PADB; PADE makes the step between layout B's
+  // registers a multiple of 64 words so register pairs share one
+  // ds_read2st64 / ds_write2st64 (from n = 1024 on; smaller rows transpose
+  // within a wave and keep their buffer small).  No pad depends on bits that vary within
+  // one pass, except as stated, so every pass meets 32 distinct banks.
   static constexpr FwdPlan PL = fwd_plan(L);
   static constexpr bool TWO = PL.SA < L;
   static constexpr bool LOCAL2 = T <= 64;
-  static constexpr int PADB = PL.DB == 0 ? 0 : (64 >> PL.DB);
-  static constexpr int SEGW2 = NB + PADB * (NB >> 7);
+  static constexpr int PADB = PL.DB == 2 ? 8 : (PL.DB == 3 ? 4 : 0);
+  static constexpr int RSTEP0 = (1 << (L - 3)) + 4 * ((1 << (L - 3)) >> 5) + PADB * ((1 << (L - 3)) >> 7);
+  static constexpr int PADE = (L >= 10) ? (64 - RSTEP0 % 64) % 64 : 0;
+  static constexpr int lds2w(int i) {
+    return i + 4 * (i >> 5) + PADB * (i >> 7) + PADE * (i >> (L - 3));
+  }
+  static constexpr int SEGW2 = (lds2w(NB - 1) + 4) & ~3;
   static constexpr int BUF2W = R * SEGS * SEGW2;
   static_assert((TWO ? (LOCAL2 ? 1 : 2) * BUF2W : 0) * sizeof(float) <= LDS_BYTES,
                 "the two-phase buffers fit the allocation of the three-shear form");
@@ -89,7 +103,7 @@ struct FwdShape {
 
 // LDS word of element i in the two-phase transposes.
 template <class S>
-__device__ __forceinline__ constexpr int lds2(int i) { return i + S::PADB * (i >> 7); }
+__device__ __forceinline__ constexpr int lds2(int i) { return S::lds2w(i); }
 
 // A lane-mapped stage of the scaled form on a thread's 8 registers: each
 // lane adds k_e times its partner lane's register e (the partner reached by
