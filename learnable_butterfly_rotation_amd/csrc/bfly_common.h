@@ -81,8 +81,12 @@ __device__ __forceinline__ int group_rows(int64_t rows, int64_t grp, int cap) {
   const uint32_t r_lo = (uint32_t)r;
   return (g_hi < 0 || r_hi < 0) ? 0 : (r_hi > 0 || r_lo >= (uint32_t)cap) ? cap : (int)r_lo;
 }
+// Cache policy of a buffer access: kNonTemporal sets the nt bit (streaming:
+// the line is not kept for reuse), for data the kernel touches once.
+constexpr int kCached = 0, kNonTemporal = 2;
+template <int POLICY = kCached>
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 // With a uniform part in the instruction's scalar offset (no address VALU,
@@ -92,18 +96,21 @@ __device__ __forceinline__ uint4 buf_ld16s(__amdgpu_buffer_rsrc_t r, uint32_t vo
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int POLICY = kCached>
 __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, POLICY);
 }
 __device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+template <int POLICY = kCached>
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, POLICY);
 }
+template <int POLICY = kCached>
 __device__ __forceinline__ void buf_st2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, POLICY);
 }
 
 // Allow a kernel more than the default 64 KiB of dynamic LDS (gfx950 has

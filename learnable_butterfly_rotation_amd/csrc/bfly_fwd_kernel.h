@@ -340,6 +340,8 @@ struct InRegs {
 // Issue the loads of row group grp into prefetch slot d, through a buffer
 // resource covering exactly the group's valid rows (none past the end).
 // elem0: the element of the thread's register 0 within its row segment.
+// Non-temporal: every input line is read once (-0.7 us at n = 4096, 8192
+// rows).
 template <class S, bool XBF16>
 __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t rows, const int64_t grp,
                                            InRegs<S, XBF16>& in, const int d, const int team,
@@ -357,7 +359,8 @@ __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t row
     for (int a = 0; a < M; ++a)
 #pragma unroll
       for (int c = 0; c < RAW; ++c)
-        in.r[d][rr * M + a][c] = buf_ld16(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
+        in.r[d][rr * M + a][c] =
+            buf_ld16<kNonTemporal>(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
 }
 
 // PRE: the caller has already issued the prologue's loads (slot d holds row
@@ -416,7 +419,8 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // The previous row group's outputs: bf16 rows, codes and scales (and, for
   // fp32 output, its rows), stored only once the next group's input has
   // arrived, so the wait for that input never has to wait for freshly issued
-  // stores as well.
+  // stores as well.  Non-temporal: every output line is written once
+  // (measured at n = 4096: 36.0 -> 34.3 us for 8192 rows).
   uint32_t held_y[SEGS][E / 2], held_c[SEGS], held_sz[SEGS];
 #pragma unroll
   for (int sg = 0; sg < SEGS; ++sg) {
@@ -444,23 +448,23 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
         if (YK == Y_BF16) {
 #pragma unroll
           for (int c = 0; c < E / 8; ++c)
-            buf_st16(ry, el * 2 + 16 * c,
+            buf_st16<kNonTemporal>(ry, el * 2 + 16 * c,
                      make_uint4(held_y[sg][4 * c], held_y[sg][4 * c + 1], held_y[sg][4 * c + 2],
                                 held_y[sg][4 * c + 3]));
         } else if (YK == Y_F32) {
 #pragma unroll
           for (int c = 0; c < E / 4; ++c)
-            buf_st16(ry4, el * 4 + 16 * c,
+            buf_st16<kNonTemporal>(ry4, el * 4 + 16 * c,
                      make_uint4(__float_as_uint(w[sg][4 * c]), __float_as_uint(w[sg][4 * c + 1]),
                                 __float_as_uint(w[sg][4 * c + 2]), __float_as_uint(w[sg][4 * c + 3])));
         }
         if (QUANT) {
-          if (bits == 4) buf_st4(rc, el / 2, held_c[sg]);
-          else buf_st2(rc, el / 4, (uint16_t)held_c[sg]);
+          if (bits == 4) buf_st4<kNonTemporal>(rc, el / 2, held_c[sg]);
+          else buf_st2<kNonTemporal>(rc, el / 4, (uint16_t)held_c[sg]);
           const uint32_t gi = (uint32_t)((team * RPT + rr) * ngroups_row + ((a * NB + elem0) >> lg_group));
           const uint32_t off = scale_lane ? 2 * gi : kOutOfRange;
-          buf_st2(rsc, off, (uint16_t)held_sz[sg]);
-          if (asym) buf_st2(rz, off, (uint16_t)(held_sz[sg] >> 16));
+          buf_st2<kNonTemporal>(rsc, off, (uint16_t)held_sz[sg]);
+          if (asym) buf_st2<kNonTemporal>(rz, off, (uint16_t)(held_sz[sg] >> 16));
         }
       }
   };
