@@ -247,8 +247,11 @@ __device__ __forceinline__ QParams quant_params(const float (&v)[8], int gt, boo
     lo = group_min(lo, gt);
     hi = group_max(hi, gt);
   } else {
-    hi = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
-               fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    // a chain the compiler maps onto three-input maxima (4 instructions)
+    hi = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+    hi = fmaxf(fmaxf(hi, fabsf(v[3])), fabsf(v[4]));
+    hi = fmaxf(fmaxf(hi, fabsf(v[5])), fabsf(v[6]));
+    hi = fmaxf(hi, fabsf(v[7]));
     hi = group_max(hi, gt);
     lo = 0.f;
   }
@@ -256,7 +259,9 @@ __device__ __forceinline__ QParams quant_params(const float (&v)[8], int gt, boo
   const _Float16 s16 = (_Float16)s_pre;
   const float sc = (float)s16;
   QParams q;
-  q.r = q.clo = q.chi = q.z = 0.f;
+  q.r = q.z = 0.f;
+  q.clo = -top * sc;  // symmetric bounds; zero with the scale
+  q.chi = top * sc;
   if (sc != 0.f) {
     q.r = __builtin_amdgcn_rcpf(sc);
     q.r = fmaf(fmaf(-sc, q.r, 1.0f), q.r, q.r);
@@ -264,9 +269,6 @@ __device__ __forceinline__ QParams quant_params(const float (&v)[8], int gt, boo
       q.z = __builtin_amdgcn_fmed3f(rintf(-lo * q.r), 0.f, top);
       q.clo = -q.z * sc;
       q.chi = (top - q.z) * sc;
-    } else {
-      q.clo = -top * sc;
-      q.chi = top * sc;
     }
   }
   q.sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
