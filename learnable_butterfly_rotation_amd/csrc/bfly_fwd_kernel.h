@@ -7,13 +7,17 @@
 //   column by column] -> store y (bf16 / fp32 / none) -> group max/min ->
 //   fp16 scale (and zero) -> codes, packed, stored.
 //
-// The (cos, sin) of every pair a thread rotates stay in its VGPRs for all
-// the rows it processes (L * E/2 pairs per thread), so after the prologue
-// the only HBM traffic is the rows themselves.  Stages whose pair bit is in
-// the thread's register bits need no data movement; between register
-// phases the row is transposed through LDS (double-buffered, one barrier per
-// transpose).  The grid is persistent: each workgroup walks row groups with
-// stride gridDim.x and prefetches the next group's input while computing.
+// The coefficients of every pair a thread rotates stay in its VGPRs for all
+// the rows it processes (8 per stage, 16 for the last), so after the
+// prologue the only HBM traffic is the rows themselves.  A stage needs both
+// elements of each pair in one thread's registers, or in two lanes one DPP
+// operand connects: the scaled form runs in two phases (register bits plus
+// lane-mapped bits, see FwdPlan) with two LDS transposes per row; the
+// three-shear fallback runs in register-only phases of 3 bits, transposed
+// through LDS between them.  Workgroup transposes are double-buffered, one
+// barrier each.  The grid is persistent: each workgroup walks row groups
+// with stride gridDim.x and prefetches the next group's input while
+// computing.
 #pragma once
 
 #include "bfly_common.h"
@@ -475,6 +479,13 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // body may sit under a branch).
   const bool has_mix1 = M == 1 && P.mix != nullptr;
   const float mix1 = has_mix1 ? P.mix[0] : 1.0f;
+  // The M x M factor, read once into scalar registers (uniform values; the
+  // compiler cannot prove the matrix unaliased by the outputs, and would
+  // otherwise reload it into vector registers for every row group).
+  float mixs[M > 1 ? M * M : 1];
+#pragma unroll
+  for (int i = 0; i < (M > 1 ? M * M : 1); ++i)
+    mixs[i] = M > 1 ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.mix[i]))) : 0.f;
   const int64_t G = gridDim.x;
 
   // The last transpose of a row group leaves its rows in layout 0 in this
@@ -580,9 +591,9 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
           float mw[M];
 #pragma unroll
           for (int a = 0; a < M; ++a) {
-            float acc = P.mix[a * M] * w[rr * M][e];
+            float acc = mixs[a * M] * w[rr * M][e];
 #pragma unroll
-            for (int a2 = 1; a2 < M; ++a2) acc = fmaf(P.mix[a * M + a2], w[rr * M + a2][e], acc);
+            for (int a2 = 1; a2 < M; ++a2) acc = fmaf(mixs[a * M + a2], w[rr * M + a2][e], acc);
             mw[a] = acc;
           }
 #pragma unroll
