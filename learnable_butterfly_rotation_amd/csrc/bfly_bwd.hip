@@ -316,10 +316,12 @@ __device__ __forceinline__ void sincos_of_float(float a, double& sn, double& cn)
 // elements), the scale (scaled form) is the product of their cosines.  So
 // every entry is computed independently from the angles.
 //
-// Eight consecutive lanes share one (s, p): lane q takes the earlier stages
-// s2 = q and q + 8, and the partial histories are combined across the eight
-// lanes, which cuts the chain of fp64 sines and cosines per lane to two.
-constexpr int PREP_LANES = 8;
+// Four consecutive lanes share one (s, p): lane q takes the earlier stages
+// s2 = q, q + 4, q + 8, and the partial histories are combined across the
+// four lanes (measured against 2, 8 and 16 lanes: 4 is fastest).  Then the
+// pair's table entries are split over its lanes, one quotient and one store
+// each, all lanes at once.
+constexpr int PREP_LANES = 4;
 
 __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
   const int half = 1 << (logn - 1);
@@ -379,35 +381,45 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
     par_i ^= __shfl_xor(par_i, d, PREP_LANES);
     par_j ^= __shfl_xor(par_j, d, PREP_LANES);
   }
-  if (q != 0) return;  // one lane per pair writes
-  cs[k] = make_float2((float)cn, (float)sn);
-  if (s < logn - 1) {
-    // phi = t or t -+ pi (|phi| <= pi/2): sin and cos of phi are +-sin t and
-    // +-cos t, and tan(phi/2) = sin(phi) / (1 + cos(phi)), whose denominator
-    // lies in [1, 2] -- one sin and cos serve every coefficient.
-    const bool flip = fabs(t) > halfpi;
-    const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
-    const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
-    lift[k] = make_float2((float)(-eps * (sp / (1.0 + cp))), (float)(eps * sp));
-    const_cast<float*>(tab.eps)[k] = (float)eps;
-    // scaled form: usable while every stored value stays within 2^64 of its
-    // true value (|sigma| >= 2^-64 after this stage)
-    const double tn = sn / cn;
-    const double lim = 5.421010862427522e-20;  // 2^-64
-    const bool ok = fabs(cn * sig_i) >= lim && fabs(cn * sig_j) >= lim;
-    const float nan = __uint_as_float(0x7fc00000u);  // a quiet NaN, as bits
-    fgt[fwd_coef_index(s, i, logn)] = ok ? (float)(-tn * (sig_j / sig_i)) : nan;
-    fgt[fwd_coef_index(s, j, logn)] = ok ? (float)(tn * (sig_i / sig_j)) : nan;
+  // Every lane holds the pair's histories now.  Lane q writes: 0 the
+  // (cos, sin); 1 the three-shear entries (or the signed last stage); 2 and
+  // 3 the scaled form at the lower and the upper element.  Each lane's one
+  // quotient is taken by all lanes together.
+  const bool flip = fabs(t) > halfpi;
+  // phi = t or t -+ pi (|phi| <= pi/2): sin and cos of phi are +-sin t and
+  // +-cos t, and tan(phi/2) = sin(phi) / (1 + cos(phi)), whose denominator
+  // lies in [1, 2] -- one sin and cos serve every coefficient.
+  const double sp = flip ? -sn : sn, cp = flip ? -cn : cn;
+  const double eps = (par_i ^ par_j) ? -1.0 : 1.0;
+  // scaled form: usable while every stored value stays within 2^64 of its
+  // true value (|sigma| >= 2^-64 after this stage); beta = -tan t sig_j /
+  // sig_i and gamma = tan t sig_i / sig_j, each as one quotient
+  const double lim = 5.421010862427522e-20;  // 2^-64
+  const bool ok = fabs(cn * sig_i) >= lim && fabs(cn * sig_j) >= lim;
+  const double num = q == 1 ? sp : (q == 2 ? -sn * sig_j : (q == 3 ? sn * sig_i : 1.0));
+  const double den = q == 1 ? 1.0 + cp : (q == 2 ? cn * sig_i : (q == 3 ? cn * sig_j : 1.0));
+  const double quo = num / den;
+  const float nan = __uint_as_float(0x7fc00000u);  // a quiet NaN, as bits
+  if (q == 0) {
+    cs[k] = make_float2((float)cn, (float)sn);
+  } else if (s < logn - 1) {
+    if (q == 1) {
+      lift[k] = make_float2((float)(-eps * quo), (float)(eps * sp));
+      const_cast<float*>(tab.eps)[k] = (float)eps;
+    } else {
+      fgt[fwd_coef_index(s, q == 2 ? i : j, logn)] = ok ? (float)quo : nan;
+    }
   } else {
     const double si = par_i ? -1.0 : 1.0, sj = par_j ? -1.0 : 1.0;
-    last[p] = make_float4((float)(cn * si), (float)(-sn * sj), (float)(sn * si), (float)(cn * sj));
     const float ki = (float)(cn * sig_i), kij = (float)(-sn * sig_j);
     const float kji = (float)(sn * sig_i), kj = (float)(cn * sig_j);
-    if (fwd_plan(logn).SA < logn) {  // a register pair: its 2x2 matrix
-      *reinterpret_cast<float4*>(fgt + fwd_last_index(i, logn)) = make_float4(ki, kij, kji, kj);
+    if (q == 1) {
+      last[p] = make_float4((float)(cn * si), (float)(-sn * sj), (float)(sn * si), (float)(cn * sj));
+    } else if (fwd_plan(logn).SA < logn) {  // a register pair: its 2x2 matrix
+      if (q == 2) *reinterpret_cast<float4*>(fgt + fwd_last_index(i, logn)) = make_float4(ki, kij, kji, kj);
     } else {  // lane-mapped: each element's (own, partner) weights
-      *reinterpret_cast<float2*>(fgt + fwd_last_index(i, logn)) = make_float2(ki, kij);
-      *reinterpret_cast<float2*>(fgt + fwd_last_index(j, logn)) = make_float2(kj, kji);
+      if (q == 2) *reinterpret_cast<float2*>(fgt + fwd_last_index(i, logn)) = make_float2(ki, kij);
+      else *reinterpret_cast<float2*>(fgt + fwd_last_index(j, logn)) = make_float2(kj, kji);
     }
   }
 }
