@@ -231,8 +231,8 @@ def test_kron_workload_full():
     print("kron n=5120:", rf, rq)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
-@pytest.mark.parametrize("nb", [256, 1024])
+@pytest.mark.parametrize("m,nb", [(m, nb) for m in (1, 2, 3, 5, 8) for nb in (256, 1024)] +
+                         [(2, 2048), (3, 2048), (2, 4096)])
 def test_kron_shapes(m, nb):
     rng = np.random.default_rng(100 * m + nb)
     th = rand_theta(rng, nb)
