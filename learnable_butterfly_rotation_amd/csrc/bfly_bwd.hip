@@ -95,25 +95,27 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
     }
   }
 
-  // Memory through buffer resources whose range is exactly the row (empty
-  // past the last row: loads give zeros, which add nothing to the angle
-  // gradients, and stores are dropped), so no memory operation is under a
-  // branch.  x and dX move in the load layout (16-byte vectors), g and y in
-  // the last phase's layout (4-byte words, 256 contiguous bytes per wave).
+  // Memory through buffer resources whose range is exactly the row group's
+  // valid rows (R rows, one per team; empty past the last row: loads give
+  // zeros, which add nothing to the angle gradients, and stores are
+  // dropped), so no memory operation is under a branch.  Base and size are
+  // uniform (scalar registers) and each thread adds its team's row to its
+  // offsets: a resource built per team would not be provably uniform and
+  // would cost a waterfall loop around every access.  x and dX move in the
+  // load layout (16-byte vectors), g and y in the last phase's layout
+  // (4-byte words, 256 contiguous bytes per wave).
   const int64_t rows = P.rows;
   const int64_t ngrp = (rows + R - 1) / R;
-  const uint32_t off0 = (uint32_t)(t * E) * 4;
-  const uint32_t offl = (uint32_t)lay<LOGE>(t, 0, BL) * 4;
-  auto row_bytes = [&](int64_t grp) -> int64_t {
-    const int64_t row = grp * R + team;
-    return (grp < ngrp && row < rows) ? (int64_t)N * 4 : 0;
+  const uint32_t off0 = (uint32_t)(team * N + t * E) * 4;
+  const uint32_t offl = (uint32_t)(team * N + lay<LOGE>(t, 0, BL)) * 4;
+  auto group_range = [&](const float* base, int64_t grp) {
+    return buffer_range32(base + grp * ((int64_t)R * N), (uint32_t)group_rows(rows, grp, R) * (uint32_t)(N * 4));
   };
   uint4 xc[E / 4];
   uint32_t gc[E];
   auto load = [&](int64_t grp) {
-    const int64_t row = grp * R + team;
-    const auto rx = buffer_range(P.x + row * N, row_bytes(grp));
-    const auto rg = buffer_range(P.g + row * N, row_bytes(grp));
+    const auto rx = group_range(P.x, grp);
+    const auto rg = group_range(P.g, grp);
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) xc[c] = buf_ld16(rx, off0 + 16 * c);
 #pragma unroll
@@ -122,7 +124,6 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
 
   load(blockIdx.x);
   for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
-    const int64_t row = grp * R + team;
     float v[E], g[E];
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
       }
     }
     if (P.y != nullptr) {
-      const auto ry = buffer_range(P.y + row * N, row_bytes(grp));
+      const auto ry = group_range(P.y, grp);
 #pragma unroll
       for (int e = 0; e < E; ++e) buf_st4(ry, offl + ((uint32_t)e << BL) * 4, __float_as_uint(v[e]));
     }
@@ -219,7 +220,7 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
         }
       }
     }
-    const auto rd = buffer_range(P.dx + row * N, row_bytes(grp));
+    const auto rd = group_range(P.dx, grp);
 #pragma unroll
     for (int c = 0; c < E / 4; ++c)
       buf_st16(rd, off0 + 16 * c, make_uint4(__float_as_uint(g[4 * c]), __float_as_uint(g[4 * c + 1]),
