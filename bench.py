@@ -311,8 +311,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the rotation is row-parallel and this build "
-              "runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only (--gpus 1): the rotation is row-parallel, and "
+              "runs on several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
     import learnable_butterfly_rotation_amd as B

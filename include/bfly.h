@@ -100,6 +100,21 @@ size_t bfly_coeff_bytes(int32_t n);
 bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coeff_bytes,
                          void* hip_stream);
 
+/* The Hadamard special case: write into `coeffs` (as for bfly_prepare) the
+ * table of H_n, the orthonormal Sylvester-ordered Walsh-Hadamard matrix
+ * (entries +-1/sqrt(n), H_n[i][j] = (-1)^popcount(i & j) / sqrt(n)).  It is
+ * the butterfly with every angle pi/4 after a fixed diagonal
+ * D = diag((-1)^popcount(i)) on the input: H_n = Q(pi/4) D.  The table is
+ * computed in fp64 from exact constants (no angles are read) and serves
+ * bfly_forward, bfly_forward_quant and bfly_kron_forward (as coeffs or
+ * coeffs_b) exactly as a table from bfly_prepare does; bfly_backward takes
+ * only tables of bfly_prepare.  Errors: BFLY_ERR_NULL (coeffs NULL),
+ * BFLY_ERR_SIZE, BFLY_ERR_WORKSPACE (coeff_bytes too small), BFLY_ERR_ALIGN,
+ * BFLY_ERR_HIP.  Passage: ButterflyQuant (the butterfly section: H_n for
+ * n = 2^k is a butterfly with particular angles) and its abstract (Hadamard
+ * coherence 1/sqrt(n)). */
+bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, void* hip_stream);
+
 /* ---- forward ------------------------------------------------------------ */
 
 /* y[r] = Q(theta) x[r] for r < rows.  x_dt, y_dt in {BFLY_F32, BFLY_BF16};

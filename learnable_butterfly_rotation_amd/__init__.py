@@ -16,8 +16,8 @@ import os
 
 __all__ = [
     "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
-    "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_forward", "bfly_forward_quant",
-    "bfly_kron_forward", "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
+    "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_prepare_hadamard",
+    "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error",
 ]
 
@@ -56,6 +56,7 @@ def lib():
         L.bfly_coeff_bytes.argtypes = [i32]
         L.bfly_coeff_bytes.restype = sz
         L.bfly_prepare.argtypes = [vp, i32, vp, sz, vp]
+        L.bfly_prepare_hadamard.argtypes = [i32, vp, sz, vp]
         L.bfly_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, vp]
         L.bfly_forward_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
                                          vp, vp, i32, i32, ctypes.c_int, vp]
@@ -67,7 +68,7 @@ def lib():
         L.bfly_status_string.argtypes = [ctypes.c_int]
         L.bfly_status_string.restype = ctypes.c_char_p
         L.bfly_last_hip_error.restype = i32
-        for f in (L.bfly_prepare, L.bfly_forward, L.bfly_forward_quant, L.bfly_kron_forward,
+        for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant, L.bfly_kron_forward,
                   L.bfly_backward):
             f.restype = ctypes.c_int
         _lib = L
@@ -119,6 +120,12 @@ def bfly_prepare(theta, n: int, coeffs, stream=None) -> None:
     """coeffs (uint8 tensor of >= bfly_coeff_bytes(n) bytes) <- table of theta."""
     _check(lib().bfly_prepare(_ptr(theta), n, _ptr(coeffs), coeffs.numel() * coeffs.element_size(),
                               _stream(stream)), "bfly_prepare")
+
+
+def bfly_prepare_hadamard(n: int, coeffs, stream=None) -> None:
+    """coeffs <- table of H_n = Q(pi/4) D, the orthonormal Walsh-Hadamard matrix."""
+    _check(lib().bfly_prepare_hadamard(n, _ptr(coeffs), coeffs.numel() * coeffs.element_size(),
+                                       _stream(stream)), "bfly_prepare_hadamard")
 
 
 def bfly_forward(x, y, theta=None, coeffs=None, stream=None) -> None:

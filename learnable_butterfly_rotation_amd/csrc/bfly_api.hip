@@ -139,6 +139,17 @@ bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coe
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
+bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, void* hip_stream) {
+  if (!coeffs) return BFLY_ERR_NULL;
+  int l = 0;
+  const bfly_status st = check_n(n, 13, &l);
+  if (st != BFLY_OK) return st;
+  if (coeff_bytes < coeff_bytes_l(l)) return BFLY_ERR_WORKSPACE;
+  if (!aligned(coeffs, 16)) return BFLY_ERR_ALIGN;
+  const hipError_t e = bfly::launch_prepare(nullptr, coeffs, l, (hipStream_t)hip_stream, true);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
 static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                                   uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
                                   int32_t m, int32_t nb, const float* theta, const void* coeffs,

@@ -324,6 +324,13 @@ __device__ __forceinline__ void sincos_of_float(float a, double& sn, double& cn)
 // each, all lanes at once.
 constexpr int PREP_LANES = 4;
 
+// HAD: the Hadamard special case -- every angle pi/4 (cos = sin = 1/sqrt 2
+// exactly, in fp64) and the +-1 diagonal D = diag((-1)^popcount(i)) on the
+// input side, which every element's history starts with: sign parity (three-
+// shear form) and scale d_i (scaled form).  The forward calls then compute
+// H_n x, H_n the orthonormal Sylvester-ordered Walsh-Hadamard matrix
+// (Q(pi/4) D = H_n).  theta is not read.
+template <bool HAD>
 __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
   const int half = 1 << (logn - 1);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -335,9 +342,11 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   const int i = ((p >> s) << (s + 1)) | (p & ((1 << s) - 1));  // lower element of the pair
   const int j = i | (1 << s);
   const double halfpi = 1.5707963267948966;
-  const double t = (double)theta[k];
+  const double r2 = 0.70710678118654752;  // cos and sin of pi/4
+  const double t = HAD ? 0.78539816339744831 : (double)theta[k];
   double sn, cn;
-  sincos_of_float(theta[k], sn, cn);
+  if (HAD) sn = cn = r2;
+  else sincos_of_float(theta[k], sn, cn);
   const Table tab = table_at(table, logn);
   float2* cs = const_cast<float2*>(tab.cs);
   float* fgt = reinterpret_cast<float*>(const_cast<float4*>(tab.fgt));
@@ -353,14 +362,19 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
     const int s2 = q + PREP_LANES * m;
-    ti[m] = theta[s2 < s ? (int64_t)s2 * half + pair_rank(i, s2) : k];
-    tj[m] = theta[s2 < s ? (int64_t)s2 * half + pair_rank(j, s2) : k];
+    ti[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * half + pair_rank(i, s2) : k];
+    tj[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * half + pair_rank(j, s2) : k];
   }
-  int par_i = 0, par_j = 0;
-  double sig_i = 1.0, sig_j = 1.0;
+  // the input side's diagonal (identity unless HAD), taken by one lane
+  int par_i = (HAD && q == 0) ? (__builtin_popcount(i) & 1) : 0;
+  int par_j = (HAD && q == 0) ? (__builtin_popcount(j) & 1) : 0;
+  double sig_i = par_i ? -1.0 : 1.0, sig_j = par_j ? -1.0 : 1.0;
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
-    if (q + PREP_LANES * m < s) {
+    if (HAD && q + PREP_LANES * m < s) {
+      sig_i *= r2;
+      sig_j *= r2;
+    } else if (q + PREP_LANES * m < s) {
       // the same predicate (in fp64) as the flip decision below
       par_i ^= fabs((double)ti[m]) > halfpi;
       par_j ^= fabs((double)tj[m]) > halfpi;
@@ -425,12 +439,16 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   }
 }
 
-hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s) {
+hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s, bool hadamard) {
   const int threads = 64;  // small blocks spread the angles over every CU
   const int64_t count = ((int64_t)logn << (logn - 1)) * PREP_LANES;
   const int64_t blocks = (count + threads - 1) / threads;
-  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, theta,
-                     static_cast<char*>(table), logn);
+  if (hadamard)
+    hipLaunchKernelGGL(prepare_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, s, theta,
+                       static_cast<char*>(table), logn);
+  else
+    hipLaunchKernelGGL(prepare_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, s, theta,
+                       static_cast<char*>(table), logn);
   return hipGetLastError();
 }
 

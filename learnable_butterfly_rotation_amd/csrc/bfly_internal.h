@@ -191,7 +191,9 @@ struct BwdParams {
 };
 
 // Kernel-launch helpers; each returns the hipError_t of the launch.
-hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s);
+// hadamard: the table of H_n = Q(pi/4) D (theta unused); see prepare_kernel.
+hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s,
+                          bool hadamard = false);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);
 hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s);
 

@@ -17,6 +17,12 @@ Each function cites the passage of the pages it follows:
   are applied before quantization.
 * backward -- ButterflyQuant abstract and duidaima.com section "training and
   results": the angles are learned by gradient descent.
+* hadamard_matrix / hadamard / kron_hadamard -- the Hadamard special case
+  (duidaima.com write-up, section "butterfly": H_n for n = 2^k is a butterfly
+  with particular angles; ButterflyQuant abstract: Hadamard entries are +-1,
+  coherence 1/sqrt(n)).  Written in numpy from the matrix's definition in
+  Sylvester order, H_n[i][j] = (-1)^popcount(i AND j) / sqrt(n), applied by a
+  dense product -- deliberately not by a butterfly, so that it checks one.
 """
 from __future__ import annotations
 
@@ -200,3 +206,42 @@ def dense_q(theta: np.ndarray) -> np.ndarray:
     n = theta.shape[1] * 2
     eye = np.eye(n, dtype=np.float32)
     return forward(eye, theta).T.copy()
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """float32 rows, or bf16 bit patterns (uint16), as fp64 (exact)."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if x.dtype == np.float32:
+        return x.astype(np.float64)
+    raise TypeError("oracle input must be float32 or uint16 (bf16 bits), got %s" % x.dtype)
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Orthonormal Sylvester-ordered Walsh-Hadamard matrix, fp64:
+    entry (i, j) = (-1)^(number of bits set in i AND j) / sqrt(n)."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    idx = np.arange(n, dtype=np.int64)
+    both = idx[:, None] & idx[None, :]
+    parity = np.zeros_like(both)
+    b = 1
+    while b < n:
+        parity ^= (both & b) != 0
+        b <<= 1
+    return np.where(parity == 1, -1.0, 1.0) / np.sqrt(float(n))
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """y = H_n x for every row, fp64.  x: float32 or bf16 bits [rows][n]."""
+    x = widen(np.ascontiguousarray(x))
+    return x @ hadamard_matrix(x.shape[1]).T
+
+
+def kron_hadamard(x: np.ndarray, mix: np.ndarray) -> np.ndarray:
+    """y = (O kron H_nb) x, index i = a*nb + b, O = mix (m x m); fp64."""
+    x = widen(np.ascontiguousarray(x))
+    mix = np.asarray(mix, dtype=np.float32).astype(np.float64)
+    m = mix.shape[0]
+    nb = x.shape[1] // m
+    return x @ np.kron(mix, hadamard_matrix(nb)).T

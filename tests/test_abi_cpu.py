@@ -36,7 +36,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_backward",
-            "bfly_prepare", "bfly_coeff_bytes", "bfly_backward_workspace_bytes",
+            "bfly_prepare", "bfly_prepare_hadamard", "bfly_coeff_bytes", "bfly_backward_workspace_bytes",
             "bfly_status_string", "bfly_last_hip_error"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
@@ -159,3 +159,12 @@ def test_prepare_validation(L):
     assert L.bfly_prepare(TH, 255, CO, 1 << 20, None) == SIZE
     assert L.bfly_prepare(TH, 256, CO, 100, None) == WORKSPACE
     assert L.bfly_prepare(TH, 256, ctypes.c_void_p(0x90008), 1 << 20, None) == ALIGN
+
+
+def test_prepare_hadamard_validation(L):
+    assert L.bfly_prepare_hadamard(256, None, 1 << 20, None) == NULL
+    assert L.bfly_prepare_hadamard(255, CO, 1 << 20, None) == SIZE
+    assert L.bfly_prepare_hadamard(1, CO, 1 << 20, None) == SIZE
+    assert L.bfly_prepare_hadamard(32, CO, 1 << 20, None) == UNSUPPORTED
+    assert L.bfly_prepare_hadamard(256, CO, 100, None) == WORKSPACE
+    assert L.bfly_prepare_hadamard(256, ctypes.c_void_p(0x90008), 1 << 20, None) == ALIGN

@@ -291,6 +291,116 @@ def test_quarter_pi_is_hadamard():
     assert np.abs(host(y) - want).max() < 1e-5
 
 
+# ---------------------------------------------------------------------------
+# the Hadamard special case: table of H_n = Q(pi/4) D from exact constants
+# ---------------------------------------------------------------------------
+
+def hadamard_table(n):
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare_hadamard(n, tab)
+    return tab
+
+
+def _scaled_block(tab, n):
+    L, half = int(math.log2(n)), n // 2
+    raw = tab.cpu().numpy()
+    return raw[half * 8 * L: half * 8 * (2 * L - 1)].view(np.float32)
+
+
+@pytest.mark.parametrize("n", [64, 128, 256, 512, 1024, 2048, 4096])
+def test_hadamard_forward(n):
+    rng = np.random.default_rng(2000 + n)
+    tab = hadamard_table(n)
+    assert not np.isnan(_scaled_block(tab, n)).any()
+    for rows in (1, 37, 301):
+        xf = (rng.standard_normal((rows, n)) * 3).astype(np.float32)
+        y = empty((rows, n), torch.float32)
+        B.bfly_forward(dev(xf), y, coeffs=tab)
+        assert_forward(host(y), oracle.hadamard(xf), xf, n)
+        xb = inputs.f32_to_bf16_bits(xf)
+        yb = empty((rows, n), torch.bfloat16)
+        B.bfly_forward(dev(xb), yb, coeffs=tab)
+        assert_forward(host(yb), oracle.hadamard(xb), xb, n)
+
+
+def test_hadamard_closed_forms_on_gpu():
+    """H e_0 = 1/sqrt(n) everywhere; H applied twice is the identity."""
+    n = 1024
+    tab = hadamard_table(n)
+    e = torch.zeros((1, n), device="cuda")
+    e[0, 0] = 1.0
+    y = empty((1, n), torch.float32)
+    B.bfly_forward(e, y, coeffs=tab)
+    assert np.abs(host(y) - 1 / 32).max() < 1e-7
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((9, n)).astype(np.float32)
+    y1 = empty(x.shape, torch.float32)
+    y2 = empty(x.shape, torch.float32)
+    B.bfly_forward(dev(x), y1, coeffs=tab)
+    B.bfly_forward(y1, y2, coeffs=tab)
+    assert np.abs(host(y2) - x).max() < 1e-5 * math.log2(n) * np.abs(x).max()
+
+
+def test_hadamard_act_int4_workload_full():
+    """H_4096 fused with sym INT4 g128 on the 8192-row bf16 activation batch
+    with outlier channels (the learned rotation's workload, angles fixed)."""
+    w = inputs.act_int4()
+    x = w["x"]
+    rows, n = x.shape
+    tab = hadamard_table(n)
+    y = empty((rows, n), torch.bfloat16)
+    codes = torch.zeros((rows, n // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+    B.bfly_forward_quant(dev(x), y, codes, scales, coeffs=tab, bits=4, group=128, mode=0)
+    out = {"y": host(y), "codes": host(codes), "scales": host(scales)}
+    y64 = oracle.hadamard(x)
+    rf = assert_forward(out["y"], y64, x, n)
+    rq = assert_quant(out, y64, 4, 128, 0)
+    print("hadamard n=4096 bf16 int4:", rf, rq)
+
+
+@pytest.mark.parametrize("bits,mode", [(2, 1), (4, 1), (2, 0)])
+def test_hadamard_quant_modes(bits, mode):
+    rng = np.random.default_rng(40 + bits + 10 * mode)
+    for n in (256, 4096):
+        tab = hadamard_table(n)
+        rows = 67
+        xf = (rng.standard_normal((rows, n)) * np.exp(rng.uniform(-4, 4, (rows, 1)))).astype(np.float32)
+        x = inputs.f32_to_bf16_bits(xf)
+        y = empty((rows, n), torch.bfloat16)
+        codes = torch.zeros((rows, n * bits // 8), dtype=torch.uint8, device="cuda")
+        scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+        zeros = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda") if mode else None
+        B.bfly_forward_quant(dev(x), y, codes, scales, zeros, coeffs=tab, bits=bits, group=128,
+                             mode=mode)
+        out = {"y": host(y), "codes": host(codes), "scales": host(scales)}
+        if mode:
+            out["zeros"] = host(zeros)
+        y64 = oracle.hadamard(x)
+        assert_forward(out["y"], y64, x, n)
+        assert_quant(out, y64, bits, 128, mode)
+
+
+@pytest.mark.parametrize("m,nb", [(5, 1024), (3, 256), (2, 4096)])
+def test_kron_hadamard(m, nb):
+    """(O kron H_nb) with the Hadamard table as the butterfly factor."""
+    rng = np.random.default_rng(3000 + 10 * m + nb)
+    mix = inputs.mixing_factor(rng, m)
+    rows = 301
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((rows, m * nb)).astype(np.float32))
+    n = m * nb
+    tab = hadamard_table(nb)
+    y = empty((rows, n), torch.bfloat16)
+    codes = torch.zeros((rows, n // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+    B.bfly_kron_forward(dev(x), y, dev(mix), codes=codes, scales=scales, coeffs_b=tab, bits=4,
+                        group=128, mode=0)
+    out = {"y": host(y), "codes": host(codes), "scales": host(scales)}
+    y64 = oracle.kron_hadamard(x, mix)
+    assert_forward(out["y"], y64, x, n)
+    assert_quant(out, y64, 4, 128, 0)
+
+
 def _table_uses_scaled_form(theta, n):
     """Whether the prepared table keeps the scaled (two-FMA) rotation form.
     Reads the (beta, gamma) part of the table's scaled-form block (after the

@@ -425,3 +425,71 @@ def test_generators_are_prefix_stable_and_seeded():
     k = inputs.kron_int4(rows=4)
     assert np.abs(k["mix"].astype(np.float64) @ k["mix"].T - np.eye(5)).max() < 1e-6
     assert k["theta_b"].shape == (10, 512)
+
+
+# --- the Hadamard special case (dense definition, checked against a butterfly)
+
+def _golden_h8():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "hadamard_sylvester_n8.txt"))
+            if l.strip() and not l.startswith("#")]
+    return np.array([[float(v) for v in r] for r in rows])
+
+
+def test_hadamard_matrix_golden_n8():
+    assert np.array_equal(oracle.hadamard_matrix(8) * math.sqrt(8), _golden_h8())
+
+
+@pytest.mark.parametrize("n", [2, 4, 16, 128])
+def test_hadamard_matrix_sylvester_recursion_and_involution(n):
+    h = oracle.hadamard_matrix(n)
+    h2 = oracle.hadamard_matrix(2 * n)
+    assert np.abs(h2 - np.block([[h, h], [h, -h]]) / math.sqrt(2)).max() < 1e-15
+    assert np.array_equal(h, h.T)
+    assert np.abs(h @ h - np.eye(n)).max() < 1e-13
+    assert np.array_equal(np.abs(h), np.full((n, n), 1 / math.sqrt(n)))
+
+
+def test_hadamard_closed_forms():
+    n = 64
+    e0 = np.zeros((1, n), dtype=np.float32)
+    e0[0, 0] = 1
+    assert np.abs(oracle.hadamard(e0) - 1 / 8).max() < 1e-16
+    ones = np.ones((1, n), dtype=np.float32)
+    want = np.zeros((1, n))
+    want[0, 0] = 8.0
+    assert np.abs(oracle.hadamard(ones) - want).max() < 1e-14
+    # a single Walsh function, index 5 = 0b101: (-1)^popcount(5 AND j)
+    w = np.array([[(-1.0) ** bin(5 & j).count("1") for j in range(n)]], dtype=np.float32)
+    want = np.zeros((1, n))
+    want[0, 5] = 8.0
+    assert np.abs(oracle.hadamard(w) - want).max() < 1e-14
+
+
+@pytest.mark.parametrize("n", [8, 64, 1024])
+def test_hadamard_is_quarter_pi_butterfly_after_sign_diagonal(n):
+    """H_n x = Q(pi/4) D x, the butterfly oracle in C against the dense
+    definition in numpy (fp32 pi/4 leaves ~1e-7 of slack per entry)."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, n)).astype(np.float32)
+    d = np.array([(-1.0) ** bin(i).count("1") for i in range(n)], dtype=np.float32)
+    th = np.full((int(math.log2(n)), n // 2), math.pi / 4, dtype=np.float32)
+    got = oracle.forward(x * d[None, :], th)
+    want = oracle.hadamard(x)
+    assert np.abs(got - want).max() < 1e-6 * np.abs(x).max()
+
+
+def test_hadamard_bf16_input_and_kron():
+    rng = np.random.default_rng(8)
+    m, nb = 3, 16
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((4, 64)).astype(np.float32))
+    assert np.array_equal(oracle.hadamard(xb), oracle.hadamard(inputs.bf16_bits_to_f32(xb)))
+    x32 = rng.standard_normal((4, m * nb)).astype(np.float32)
+    mix = inputs.mixing_factor(rng, m)
+    d = np.array([(-1.0) ** bin(i % nb).count("1") for i in range(m * nb)], dtype=np.float32)
+    th = np.full((4, nb // 2), math.pi / 4, dtype=np.float32)
+    got = oracle.kron_forward(x32 * d[None, :], th, mix)
+    assert np.abs(got - oracle.kron_hadamard(x32, mix)).max() < 1e-6 * np.abs(x32).max()
+    # m = 1, mix = [1]: the plain transform
+    one = np.ones((1, 1), dtype=np.float32)
+    x64 = rng.standard_normal((4, 64)).astype(np.float32)
+    assert np.abs(oracle.kron_hadamard(x64, one) - oracle.hadamard(x64)).max() < 1e-15
