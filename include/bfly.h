@@ -66,7 +66,7 @@ typedef enum {
     BFLY_ERR_ALIGN = 4,       /* a pointer is not aligned as stated above          */
     BFLY_ERR_QUANT = 5,       /* bits / group / mode / zeros combination invalid   */
     BFLY_ERR_WORKSPACE = 6,   /* workspace or coefficient buffer too small         */
-    BFLY_ERR_UNSUPPORTED = 7, /* a valid size this build does not handle           */
+    BFLY_ERR_UNSUPPORTED = 7, /* a valid size the library does not handle         */
     BFLY_ERR_HIP = 8          /* a HIP runtime call failed                         */
 } bfly_status;
 

@@ -58,7 +58,7 @@ int log2_pow2(int64_t n) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Butterfly length: power of two in [64, 8192] (smaller powers of two are
-// valid sizes this build does not handle).
+// valid sizes the library does not handle).
 bfly_status check_n(int64_t n, int max_log, int* logn) {
   const int l = log2_pow2(n);
   if (l < 1) return BFLY_ERR_SIZE;
@@ -280,7 +280,7 @@ const char* bfly_status_string(bfly_status s) {
     case BFLY_ERR_ALIGN: return "misaligned pointer";
     case BFLY_ERR_QUANT: return "invalid quantization arguments";
     case BFLY_ERR_WORKSPACE: return "workspace or coefficient buffer too small";
-    case BFLY_ERR_UNSUPPORTED: return "size not supported by this build";
+    case BFLY_ERR_UNSUPPORTED: return "size not supported by the library";
     case BFLY_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
