@@ -23,6 +23,12 @@ Each function cites the passage of the pages it follows:
   coherence 1/sqrt(n)).  Written in numpy from the matrix's definition in
   Sylvester order, H_n[i][j] = (-1)^popcount(i AND j) / sqrt(n), applied by a
   dense product -- deliberately not by a butterfly, so that it checks one.
+* dequantize / quant_matmul -- the consumer of the quantized weights:
+  y = W x = (W Q^T)(Q x) with W Q^T stored as 2-bit (or 4-bit) group codes
+  (ButterflyQuant abstract: computational invariance and 2-bit weights;
+  duidaima.com section "training and results": W2A16).  Written in numpy:
+  unpack the codes, s * q or s * (q - zero) per element in fp64, then one
+  fp64 matrix product.
 """
 from __future__ import annotations
 
@@ -245,3 +251,34 @@ def kron_hadamard(x: np.ndarray, mix: np.ndarray) -> np.ndarray:
     m = mix.shape[0]
     nb = x.shape[1] // m
     return x @ np.kron(mix, hadamard_matrix(nb)).T
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, zeros, bits: int, group: int, mode: int,
+               n: int) -> np.ndarray:
+    """Group-quantized rows back to fp64 values: codes u8 [rows][n*bits/8]
+    (element e of a byte in bits [bits*e, bits*(e+1)); symmetric codes are
+    two's-complement fields), scales / zeros fp16 bit patterns
+    [rows][n/group].  Symmetric: s*q; asymmetric: s*(q - zero)."""
+    per = 8 // bits
+    c = np.asarray(codes).astype(np.int64)
+    rows = c.shape[0]
+    q = np.empty((rows, n), dtype=np.int64)
+    for e in range(per):
+        q[:, e::per] = (c >> (bits * e)) & ((1 << bits) - 1)
+    if mode == SYM:
+        q = np.where(q >= (1 << (bits - 1)), q - (1 << bits), q)
+    s = np.asarray(scales, dtype=np.uint16).view(np.float16).astype(np.float64)
+    s = np.repeat(s, group, axis=1)
+    if mode == SYM:
+        return s * q
+    z = np.asarray(zeros, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return s * (q - np.repeat(z, group, axis=1))
+
+
+def quant_matmul(a: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros, bits: int,
+                 group: int, mode: int) -> np.ndarray:
+    """y[m][o] = sum_k a[m][k] * w[o][k], w the dequantized weight rows; fp64.
+    a: float32 or bf16 bits [M][K]; codes etc. as in dequantize, K = a's width."""
+    a = widen(np.ascontiguousarray(a))
+    w = dequantize(codes, scales, zeros, bits, group, mode, a.shape[1])
+    return a @ w.T

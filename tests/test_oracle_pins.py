@@ -493,3 +493,95 @@ def test_hadamard_bf16_input_and_kron():
     one = np.ones((1, 1), dtype=np.float32)
     x64 = rng.standard_normal((4, 64)).astype(np.float32)
     assert np.abs(oracle.kron_hadamard(x64, one) - oracle.hadamard(x64)).max() < 1e-15
+
+
+# --- the quantized-weight product (the consumer of the codes)
+
+def _parse_qmm_golden():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "quant_matmul_hand.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        head, codes, scales, zeros, a, y = [f.strip() for f in line.split("|")]
+        bits, mode, k, group = head.split()
+        rows = lambda f, conv: np.array([[conv(v) for v in r.split()] for r in f.split(";")])
+        cases.append(dict(
+            bits=int(bits), mode=oracle.SYM if mode == "sym" else oracle.ASYM, k=int(k),
+            group=int(group), codes=rows(codes, lambda v: int(v, 16)).astype(np.uint8),
+            scales=rows(scales, lambda v: int(v, 16)).astype(np.uint16),
+            zeros=None if zeros == "-" else rows(zeros, lambda v: int(v, 16)).astype(np.uint16),
+            a=rows(a, float).astype(np.float32), y=rows(y, float)))
+    return cases
+
+
+def test_quant_matmul_hand_examples():
+    cases = _parse_qmm_golden()
+    assert len(cases) == 2
+    for c in cases:
+        got = oracle.quant_matmul(c["a"], c["codes"], c["scales"], c["zeros"], c["bits"],
+                                  c["group"], c["mode"])
+        assert np.array_equal(got, c["y"]), (got, c["y"])
+
+
+def _brute_dequant(codes, scales, zeros, bits, group, mode, k):
+    """One element at a time from the bit string of each byte (tiny sizes)."""
+    out = []
+    for r in range(codes.shape[0]):
+        row = []
+        for e in range(k):
+            byte = int(codes[r, e * bits // 8])
+            field = format(byte, "08b")[::-1][(e * bits) % 8:(e * bits) % 8 + bits][::-1]
+            q = int(field, 2)
+            if mode == oracle.SYM and field[0] == "1":
+                q -= 1 << bits
+            s = float(np.uint16(scales[r, e // group]).view(np.float16))
+            z = 0.0 if mode == oracle.SYM else float(np.uint16(zeros[r, e // group]).view(np.float16))
+            row.append(s * (q - z))
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("bits,mode", [(2, oracle.ASYM), (2, oracle.SYM), (4, oracle.SYM),
+                                       (4, oracle.ASYM)])
+def test_quant_matmul_brute_force(bits, mode):
+    rng = np.random.default_rng(50 + bits + mode)
+    m, o, k, group = 3, 4, 32, 8
+    w = rng.standard_normal((o, k))
+    q = oracle.quantize(w, bits, group, mode)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    w_b = _brute_dequant(q["codes"], q["scales"], q.get("zeros"), bits, group, mode, k)
+    want = [[sum(float(a[i, e]) * w_b[j][e] for e in range(k)) for j in range(o)] for i in range(m)]
+    got = oracle.quant_matmul(a, q["codes"], q["scales"], q.get("zeros"), bits, group, mode)
+    assert np.abs(got - np.array(want)).max() < 1e-12
+
+
+@pytest.mark.parametrize("bits,mode", [(2, oracle.ASYM), (4, oracle.SYM)])
+def test_dequantize_within_half_step(bits, mode):
+    """Dequantized codes are the nearest levels: within half a scale step of
+    the quantized values (plus fp16 rounding of the scale at the clamp)."""
+    rng = np.random.default_rng(60 + bits)
+    y = rng.standard_normal((16, 256)) * np.exp(rng.uniform(-3, 3, (16, 1)))
+    q = oracle.quantize(y, bits, 128, mode)
+    w = oracle.dequantize(q["codes"], q["scales"], q.get("zeros"), bits, 128, mode, 256)
+    s = np.repeat(q["scales"].view(np.float16).astype(np.float64), 128, axis=1)
+    assert (np.abs(w - y) <= 0.5 * s + np.abs(y) * 2.0 ** -10).all()
+
+
+def test_quant_matmul_computational_invariance():
+    """(W Q^T)(Q x) with W Q^T quantized: y = W x up to the quantization
+    error, |y - W x| <= sum_k |(Q x)_k| * s_k / 2 (plus the clamp slack)."""
+    rng = np.random.default_rng(70)
+    n, o, m = 64, 8, 5
+    th = rand_theta(n, rng)
+    w = rng.standard_normal((o, n)).astype(np.float32)
+    x = rng.standard_normal((m, n)).astype(np.float32)
+    wq = oracle.forward(w, th)           # rows of W Q^T
+    qx = oracle.forward(x, th).astype(np.float32)
+    q = oracle.quantize(wq, 2, 32, oracle.ASYM)
+    y = oracle.quant_matmul(qx, q["codes"], q["scales"], q["zeros"], 2, 32, oracle.ASYM)
+    wx = x.astype(np.float64) @ w.astype(np.float64).T
+    s = np.repeat(q["scales"].view(np.float16).astype(np.float64), 32, axis=1)
+    bound = np.abs(qx.astype(np.float64)) @ (0.5 * s + np.abs(wq) * 2.0 ** -10).T
+    bound += 1e-6 * np.abs(x).max() * np.abs(w).max() * n  # fp32 rounding of Q x
+    assert (np.abs(y - wx) <= bound).all()
+    assert np.abs(y - wx).max() > 0  # the quantization is not a no-op
