@@ -175,6 +175,39 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
 
 size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n);
 
+/* ---- consumer of the quantized weights ---------------------------------- */
+
+/* y[r][o] = sum_k a[r][k] * w[o][k] for r < rows, o < n_out: the layer
+ * output W x = (W Q^T)(Q x) with a = Q x (bf16 activations, e.g. from
+ * bfly_forward) and the rows of W Q^T stored as group codes by
+ * bfly_forward_quant (W2A16; 4-bit codes are accepted too).  Passages:
+ * ButterflyQuant abstract (computational invariance, 2-bit weights) and the
+ * ButterflyQuant write-up, section "training and results" (W2A16).
+ *   a      : bf16 [rows][k] (a_dt must be BFLY_BF16), 16-byte aligned
+ *   codes  : u8 [n_out][k*bits/8], the packing of bfly_forward_quant
+ *            (element e of a byte in bits [bits*e, bits*(e+1)); symmetric
+ *            codes are two's-complement fields), 16-byte aligned
+ *   scales : fp16 bit patterns [n_out][k/group], 2-byte aligned
+ *   zeros  : fp16 bit patterns [n_out][k/group] (integers) for
+ *            BFLY_ASYM_MINMAX, NULL for BFLY_SYM_ABSMAX
+ *   y      : [rows][n_out] of y_dt (BFLY_F32 or BFLY_BF16, rounded to
+ *            nearest even from fp32), 16-byte aligned; must not overlap
+ *            the inputs
+ *   w[o][k] = scale * q (symmetric) or scale * (q - zero) (asymmetric).
+ * Arithmetic: each group's sum of a * (q - zero) in fp32 (exact products),
+ * then times the group's scale and added in fp32.
+ * Sizes: bits 2 or 4; k a multiple of 64 in [64, 65536]; group one of 64,
+ * 128, 256, 512 dividing k; n_out a positive multiple of 128 with
+ * n_out <= 1048576.  rows == 0 is a no-op.  Errors: BFLY_ERR_NULL,
+ * BFLY_ERR_SIZE (rows < 0, n_out or k not positive), BFLY_ERR_DTYPE,
+ * BFLY_ERR_QUANT (bits, group, mode or zeros invalid), BFLY_ERR_ALIGN,
+ * BFLY_ERR_UNSUPPORTED (valid sizes outside the ranges above),
+ * BFLY_ERR_HIP. */
+bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, void* y,
+                              bfly_dtype y_dt, int64_t rows, int32_t n_out, int32_t k,
+                              int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 const char* bfly_status_string(bfly_status s);

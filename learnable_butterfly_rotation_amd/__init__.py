@@ -17,7 +17,8 @@ import os
 __all__ = [
     "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
     "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_prepare_hadamard",
-    "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
+    "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_quant_matmul",
+    "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error",
 ]
 
@@ -62,14 +63,16 @@ def lib():
                                          vp, vp, i32, i32, ctypes.c_int, vp]
         L.bfly_kron_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
                                         i32, vp, vp, vp, i32, i32, ctypes.c_int, vp]
+        L.bfly_quant_matmul.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, i64, i32,
+                                        i32, i32, i32, ctypes.c_int, vp]
         L.bfly_backward.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.bfly_backward_workspace_bytes.argtypes = [i64, i32]
         L.bfly_backward_workspace_bytes.restype = sz
         L.bfly_status_string.argtypes = [ctypes.c_int]
         L.bfly_status_string.restype = ctypes.c_char_p
         L.bfly_last_hip_error.restype = i32
-        for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant, L.bfly_kron_forward,
-                  L.bfly_backward):
+        for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
+                  L.bfly_kron_forward, L.bfly_quant_matmul, L.bfly_backward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -154,6 +157,17 @@ def bfly_kron_forward(x, y, mix, codes=None, scales=None, zeros=None, theta_b=No
                                    _ptr(codes), _ptr(scales), _ptr(zeros), rows, m, n // m,
                                    _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), bits, group, mode,
                                    _stream(stream)), "bfly_kron_forward")
+
+
+def bfly_quant_matmul(a, codes, scales, zeros, y, bits=2, group=128, mode=BFLY_ASYM_MINMAX,
+                      stream=None) -> None:
+    """y = a w^T with w's rows as group codes; a: [rows, k] bfloat16, codes:
+    uint8 [n_out, k*bits/8], scales/zeros: float16 [n_out, k/group]."""
+    rows, k = a.shape
+    n_out = codes.shape[0]
+    _check(lib().bfly_quant_matmul(_ptr(a), _dt(a), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                   _ptr(y), _dt(y), rows, n_out, k, bits, group, mode,
+                                   _stream(stream)), "bfly_quant_matmul")
 
 
 def bfly_backward_workspace_bytes(rows: int, n: int) -> int:

@@ -7,6 +7,7 @@
 
 #include "../../include/bfly.h"
 #include "bfly_internal.h"
+#include "bfly_qgemm.h"
 
 namespace bfly {
 hipError_t launch_forward_plain(const FwdParams& p, hipStream_t s);
@@ -268,6 +269,44 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   p.logn = l;
   p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);
   const hipError_t e = bfly::launch_backward(p, dtheta, s);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, void* y,
+                              bfly_dtype y_dt, int64_t rows, int32_t n_out, int32_t k,
+                              int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream) {
+  if (rows < 0 || n_out <= 0 || k <= 0) return BFLY_ERR_SIZE;
+  if (rows > 0 && (!a || !y)) return BFLY_ERR_NULL;
+  if (!codes || !scales) return BFLY_ERR_NULL;
+  if (a_dt != BFLY_BF16 || !dtype_ok(y_dt)) return BFLY_ERR_DTYPE;
+  if ((bits != 2 && bits != 4) || (mode != BFLY_SYM_ABSMAX && mode != BFLY_ASYM_MINMAX) ||
+      (mode == BFLY_ASYM_MINMAX) != (zeros != nullptr))
+    return BFLY_ERR_QUANT;
+  if (group != 64 && group != 128 && group != 256 && group != 512) return BFLY_ERR_QUANT;
+  if (k % group != 0) return BFLY_ERR_QUANT;
+  if (n_out % bfly::QG_BN != 0 || n_out > (1 << 20) || k % bfly::QG_BK != 0 || k > 65536)
+    return BFLY_ERR_UNSUPPORTED;
+  const int64_t tiles = (rows + bfly::QG_BM - 1) / bfly::QG_BM * (n_out / bfly::QG_BN);
+  if (tiles >= (int64_t(1) << 31)) return BFLY_ERR_UNSUPPORTED;
+  if ((a && !aligned(a, 16)) || !aligned(codes, 16) || !aligned(scales, 2) ||
+      (zeros && !aligned(zeros, 2)) || (y && !aligned(y, 16)))
+    return BFLY_ERR_ALIGN;
+  if (rows == 0) return BFLY_OK;
+  bfly::QgemmParams p;
+  p.a = static_cast<const uint16_t*>(a);
+  p.codes = codes;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.y = y;
+  p.rows = rows;
+  p.n_out = n_out;
+  p.k = k;
+  p.group = group;
+  p.bits = bits;
+  p.asym = mode == BFLY_ASYM_MINMAX;
+  p.y_bf16 = y_dt == BFLY_BF16;
+  const hipError_t e = bfly::launch_qgemm(p, (hipStream_t)hip_stream);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 

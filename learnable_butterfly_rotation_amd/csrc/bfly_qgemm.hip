@@ -1,0 +1,266 @@
+// Quantized-weight matrix product on the matrix cores: y = a w^T with w's
+// rows stored as 2- or 4-bit group codes, the consumer of the rotated and
+// quantized weights (ButterflyQuant abstract: W x = (W Q^T)(Q x) with 2-bit
+// weights; the ButterflyQuant write-up, section "training and results":
+// W2A16, bf16 activations against 2-bit weights).
+//
+// Exactness: a code minus its zero point is a small integer (|v| <= 15),
+// exact in bf16, and a bf16 activation times it is exact in fp32.  So the
+// MFMA sums sum_k a[r][k] * (q[o][k] - z) over one quantization group in
+// fp32 with only the accumulation rounding, and the group's fp16 scale is
+// applied afterwards: y += s[o][g] * P_g.  No weight value is rounded to
+// bf16; the result is as accurate as an fp32 dot product.
+//
+// Workgroup: 512 threads (8 waves, 4 along rows x 2 along outputs), a
+// 256 x 128 output tile, k in chunks of 64.  Per chunk the activations
+// (256 x 64 bf16) and the decoded weights (128 x 64 bf16) go through LDS,
+// double-buffered, one barrier per chunk; each wave runs 2 x 2
+// v_mfma_f32_32x32x16_bf16 tiles (64 x 64 outputs).  Each weight code is
+// decoded once per workgroup (by one thread) and then read by the four
+// waves of its output columns.
+#include "bfly_common.h"
+#include "bfly_qgemm.h"
+
+namespace bfly {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int QTHREADS = 512;
+constexpr int QROW = QG_BK * 2 + 16;  // LDS bytes per tile row: 64 bf16 + 16 (banks)
+constexpr int QA_BYTES = QG_BM * QROW;
+constexpr int QB_BYTES = QG_BN * QROW;
+constexpr int QLDS = 2 * (QA_BYTES + QB_BYTES);  // 110 592
+
+__device__ __forceinline__ uint4 lds_ld16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void lds_st16(uint8_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Two small integers given as floats -> their bf16 patterns (the high
+// halves, exact) in one word, lo in the low half.
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+template <int B>
+__device__ __forceinline__ float ubyte(uint32_t m) {
+  return (float)((m >> (8 * B)) & 0xFFu);
+}
+
+// 16 codes of BITS bits (element e of the chunk in bits [BITS*e, ...) of
+// the little-endian words x[]) minus z, as 8 words of bf16 pairs (elements
+// 2i, 2i+1).  Symmetric codes arrive with their sign bit flipped (offset
+// binary) and z = 2^(BITS-1).
+template <int BITS>
+__device__ __forceinline__ void decode16(const uint32_t (&x)[BITS / 2], float z, uint32_t (&w)[8]) {
+  float f[16];
+  if (BITS == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t m = (x[0] >> (2 * j)) & 0x03030303u;  // elements j, j+4, j+8, j+12
+      f[j] = ubyte<0>(m) - z;
+      f[j + 4] = ubyte<1>(m) - z;
+      f[j + 8] = ubyte<2>(m) - z;
+      f[j + 12] = ubyte<3>(m) - z;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t m = (x[h] >> (4 * j)) & 0x0F0F0F0Fu;  // elements j, j+2, j+4, j+6
+        f[8 * h + j] = ubyte<0>(m) - z;
+        f[8 * h + j + 2] = ubyte<1>(m) - z;
+        f[8 * h + j + 4] = ubyte<2>(m) - z;
+        f[8 * h + j + 6] = ubyte<3>(m) - z;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = pack_exact(f[2 * i], f[2 * i + 1]);
+}
+
+template <int BITS, bool ASYM, bool YBF16>
+__global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv & 3, wn = wv >> 2;
+  const int K = P.k, N = P.n_out, G = P.group;
+  const int NT = N / QG_BN;
+
+  // Tile order: workgroups are dealt round-robin to the 8 XCDs; renumber so
+  // that each XCD runs a contiguous range of tiles, outputs fastest: the
+  // workgroups an XCD runs together share their activation rows in its L2.
+  const uint32_t nblk = gridDim.x, b = blockIdx.x;
+  const uint32_t per = nblk >> 3, rem = nblk & 7, xcd = b & 7;
+  const uint32_t logical = xcd * per + (xcd < rem ? xcd : rem) + (b >> 3);
+  const int mt = (int)(logical / (uint32_t)NT);
+  const int nt = (int)(logical - (uint32_t)mt * (uint32_t)NT);
+  const int64_t m0 = (int64_t)mt * QG_BM;
+  const int n0 = nt * QG_BN;
+  const int mrows = group_rows(P.rows, mt, QG_BM);
+
+  constexpr int CB = BITS * 2;  // code bytes per thread per chunk (16 codes)
+  const int KB = K * BITS / 8;  // code bytes per weight row
+  const int NG = K / G;         // groups per weight row
+  const auto ra = buffer_range32(P.a + m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
+  const auto rc = buffer_range32(P.codes + (int64_t)n0 * KB, (uint32_t)(QG_BN * KB));
+  const auto rs = buffer_range32(P.scales + (int64_t)n0 * NG, (uint32_t)(QG_BN * NG * 2));
+  const auto rz = buffer_range32(ASYM ? P.zeros + (int64_t)n0 * NG : P.scales,
+                                 ASYM ? (uint32_t)(QG_BN * NG * 2) : 0u);
+
+  // loads of one chunk: activations 4 x 16 B per thread (rows t/8 + 64 i),
+  // codes of one weight row (t / 4), elements 16 (t % 4) .. + 15
+  const int arow = t >> 3, akc = t & 7;
+  const uint32_t a_off = (uint32_t)(arow * K + akc * 8) * 2u;
+  const uint32_t a_step = (uint32_t)(64 * K) * 2u;  // 64 rows
+  const int cn = t >> 2, cq = t & 3;
+  const uint32_t c_off = (uint32_t)(cn * KB + cq * CB);
+  uint4 ar[4];
+  uint32_t cr[BITS / 2];
+  float zr = ASYM ? 0.f : (float)(1 << (BITS - 1));
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = buf_ld16(ra, a_off + i * a_step + (uint32_t)c * (QG_BK * 2));
+    const uint32_t off = c_off + (uint32_t)c * (QG_BK * BITS / 8);
+    if (BITS == 2) {
+      cr[0] = buf_ld4(rc, off);
+    } else {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)off, 0, 0);
+      cr[0] = v.x;
+      cr[BITS / 2 - 1] = v.y;
+    }
+    if (ASYM) {
+      const int g = c * QG_BK / G;
+      zr = half_to_float(__builtin_amdgcn_raw_buffer_load_b16(rz, (int)((cn * NG + g) * 2), 0, 0));
+    }
+  };
+  auto stash = [&](int bi) {
+    uint8_t* Ab = smem + bi * QA_BYTES;
+    uint8_t* Bb = smem + 2 * QA_BYTES + bi * QB_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_st16(Ab + (arow + 64 * i) * QROW + akc * 16, ar[i]);
+    uint32_t x[BITS / 2];
+#pragma unroll
+    for (int h = 0; h < BITS / 2; ++h)
+      x[h] = ASYM ? cr[h] : cr[h] ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
+    uint32_t w[8];
+    decode16<BITS>(x, zr, w);
+    lds_st16(Bb + cn * QROW + cq * 32, make_uint4(w[0], w[1], w[2], w[3]));
+    lds_st16(Bb + cn * QROW + cq * 32 + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  };
+
+  f32x16_t Y[2][2], Pg[2][2];
+  const f32x16_t zero = {};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) Y[i][j] = zero;
+
+  // this lane's two output columns (C layout of the 32 x 32 tiles: lane l
+  // holds column l % 32)
+  const int col0 = wn * 64 + (lane & 31);
+  float sc[2] = {0.f, 0.f};
+
+  const int nch = K / QG_BK, cpg = G / QG_BK;
+  issue(0);
+  stash(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int bi = c & 1;
+    const bool more = c + 1 < nch;
+    const bool gfirst = (c % cpg) == 0, glast = (c % cpg) == cpg - 1;
+    if (more) issue(c + 1);
+    if (gfirst) {
+      const int g = c / cpg;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sc[j] = half_to_float(
+            __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(((col0 + 32 * j) * NG + g) * 2), 0, 0));
+    }
+    const uint8_t* Ab = smem + bi * QA_BYTES + (wm * 64 + (lane & 31)) * QROW + (lane >> 5) * 16;
+    const uint8_t* Bb = smem + 2 * QA_BYTES + bi * QB_BYTES + col0 * QROW + (lane >> 5) * 16;
+#pragma unroll
+    for (int kk = 0; kk < QG_BK / 16; ++kk) {
+      bf16x8_t af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_t, lds_ld16(Ab + 32 * i * QROW + kk * 32));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8_t, lds_ld16(Bb + 32 * j * QROW + kk * 32));
+      if (kk == 0 && gfirst) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            Pg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], zero, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            Pg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], Pg[i][j], 0, 0, 0);
+      }
+    }
+    if (glast) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Y[i][j][r] = fmaf(sc[j], Pg[i][j][r], Y[i][j][r]);
+    }
+    if (more) stash(bi ^ 1);
+    __syncthreads();
+  }
+
+  // store: register r of tile (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4
+  // of the tile, column lane % 32; rows past the end fall outside the range
+  constexpr int YSZ = YBF16 ? 2 : 4;
+  const auto ry = buffer_range32(static_cast<char*>(P.y) + m0 * N * YSZ,
+                                 (uint32_t)mrows * (uint32_t)N * YSZ);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const uint32_t off = (uint32_t)(row * N + n0 + col0 + 32 * j) * YSZ;
+        if (YBF16) buf_st2(ry, off, (uint16_t)pack_bf16(Y[i][j][r], 0.f));
+        else buf_st4(ry, off, __float_as_uint(Y[i][j][r]));
+      }
+}
+
+template <int BITS, bool ASYM, bool YBF16>
+hipError_t launch_one(const QgemmParams& p, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BITS, ASYM, YBF16>);
+  static const hipError_t lds_ok = allow_lds(fn, QLDS);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int64_t mt = (p.rows + QG_BM - 1) / QG_BM;
+  const int64_t blocks = mt * (p.n_out / QG_BN);
+  hipLaunchKernelGGL((qgemm_kernel<BITS, ASYM, YBF16>), dim3((unsigned)blocks), dim3(QTHREADS),
+                     QLDS, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qgemm(const QgemmParams& p, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  if (p.bits == 2) {
+    if (p.asym) return p.y_bf16 ? launch_one<2, true, true>(p, s) : launch_one<2, true, false>(p, s);
+    return p.y_bf16 ? launch_one<2, false, true>(p, s) : launch_one<2, false, false>(p, s);
+  }
+  if (p.asym) return p.y_bf16 ? launch_one<4, true, true>(p, s) : launch_one<4, true, false>(p, s);
+  return p.y_bf16 ? launch_one<4, false, true>(p, s) : launch_one<4, false, false>(p, s);
+}
+
+}  // namespace bfly

@@ -168,3 +168,35 @@ def test_prepare_hadamard_validation(L):
     assert L.bfly_prepare_hadamard(32, CO, 1 << 20, None) == UNSUPPORTED
     assert L.bfly_prepare_hadamard(256, CO, 100, None) == WORKSPACE
     assert L.bfly_prepare_hadamard(256, ctypes.c_void_p(0x90008), 1 << 20, None) == ALIGN
+
+
+def qm(L, a=X, ad=1, c=C, s=S, z=Z, y=Y, yd=1, rows=0, n_out=11008, k=4096, bits=2, group=128,
+       mode=1):
+    return L.bfly_quant_matmul(a, ad, c, s, z, y, yd, rows, n_out, k, bits, group, mode, None)
+
+
+def test_quant_matmul_validation(L):
+    assert qm(L) == OK                                   # rows == 0: nothing to do
+    assert qm(L, a=None, y=None) == OK
+    assert qm(L, rows=-1) == SIZE
+    assert qm(L, n_out=0) == SIZE
+    assert qm(L, k=0) == SIZE
+    assert qm(L, rows=5, a=None) == NULL
+    assert qm(L, rows=5, y=None) == NULL
+    assert qm(L, c=None) == NULL
+    assert qm(L, s=None) == NULL
+    assert qm(L, ad=0) == DTYPE                          # activations are bf16
+    assert qm(L, yd=2) == DTYPE
+    assert qm(L, bits=3) == QUANT
+    assert qm(L, z=None) == QUANT                        # asymmetric needs zero points
+    assert qm(L, mode=0) == QUANT                        # symmetric takes none
+    assert qm(L, mode=0, z=None) == OK
+    assert qm(L, group=32) == QUANT
+    assert qm(L, group=512, k=4096 + 128) == QUANT       # group must divide k
+    assert qm(L, n_out=11008 + 64) == UNSUPPORTED
+    assert qm(L, k=4096 + 64, group=64) == OK
+    assert qm(L, k=65536 + 128) == UNSUPPORTED
+    assert qm(L, c=ctypes.c_void_p(0x30008)) == ALIGN
+    assert qm(L, a=ctypes.c_void_p(0x10008)) == ALIGN
+    assert qm(L, y=ctypes.c_void_p(0x20004)) == ALIGN
+    assert qm(L, s=ctypes.c_void_p(0x40001)) == ALIGN
