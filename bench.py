@@ -21,7 +21,7 @@ counters recorded for the current kernel sources (null if they changed).
 
 --workload picks one of the other parity workloads for a secondary line
 (tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
-calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4); --copy-probe runs a plain device copy of known
+calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008); --copy-probe runs a plain device copy of known
 size (for calibrating the byte counters).
 """
 from __future__ import annotations
@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "butterfly+quant GB/s (% of HBM roofline), n=4096, 8192 rows bf16"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bfly_fwd_quant_n4096_bf16_int4_traffic.txt")
 NSETS = 5
 
@@ -308,6 +309,48 @@ def bench_secondary(args, torch, B, inputs):
         res.update(us_per_step=t_h * 1e6, bytes=b, GBs=b / t_h / 1e9, rows_per_s=rows / t_h,
                    learned_fixed_us_per_step=t_l * 1e6, learned_prepared_us_per_step=t_lp * 1e6,
                    learned_fixed_over_hadamard=t_l / t_h, learned_prepared_over_hadamard=t_lp / t_h)
+    elif name == "w2a16_m8192_k4096_n11008":
+        # The consumer of the quantized weights: y = (Q x)(W Q^T)^T for the
+        # headline batch (8192 x 4096 bf16, rotated by the library) against
+        # the 11008 x 4096 weight rotated and quantized to asym INT2 g128 by
+        # the library; bf16 out.  One step = one bfly_quant_matmul.
+        w = inputs.act_int4()
+        ww = inputs.weight_int2()
+        rows, k = w["x"].shape
+        n_out = ww["w2"].shape[0]
+        a = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
+        B.bfly_forward(to_dev(w["x"], torch), a, theta=to_dev(w["theta"], torch))
+        w2 = to_dev(ww["w2"], torch)
+        codes = torch.empty((n_out, k // 4), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n_out, k // 128), dtype=torch.float16, device="cuda")
+        zr = torch.empty_like(sc)
+        B.bfly_forward_quant(w2, None, codes, sc, zr, theta=to_dev(ww["theta"], torch), bits=2,
+                             group=128, mode=B.BFLY_ASYM_MINMAX)
+        del w2
+        y = torch.empty((rows, n_out), dtype=torch.bfloat16, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def fn(i, ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            B.bfly_quant_matmul(a, codes, sc, zr, y, bits=2, group=128, mode=B.BFLY_ASYM_MINMAX)
+            if ev is not None:
+                ev[1].record(stream)
+        warm_up(torch, fn, args.warmup)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i, evs[i])
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / args.steps
+        kern_s = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / 1e3
+        flops = 2.0 * rows * k * n_out
+        hbm = rows * k * 2 + codes.numel() + 4 * sc.numel() + rows * n_out * 2
+        res.update(us_per_step=t * 1e6, kernel_avg_us=kern_s * 1e6, flops=flops,
+                   TFLOPs=flops / kern_s / 1e12, mfma_bf16_peak_TFLOPs=MFMA_BF16_PEAK_TFLOPS,
+                   frac_of_mfma_peak=flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                   hbm_bytes=hbm, GBs_hbm=hbm / kern_s / 1e9)
     elif name == "calib_n4096_fp32_fwd_bwd":
         c = inputs.CalibFP32()
         X = torch.empty((c.rows, c.n), device="cuda")

@@ -18,6 +18,8 @@
 // v_mfma_f32_32x32x16_bf16 tiles (64 x 64 outputs).  Each weight code is
 // decoded once per workgroup (by one thread) and then read by the four
 // waves of its output columns.
+#include <type_traits>
+
 #include "bfly_common.h"
 #include "bfly_qgemm.h"
 
@@ -32,7 +34,8 @@ constexpr int QTHREADS = 512;
 constexpr int QROW = QG_BK * 2 + 16;  // LDS bytes per tile row: 64 bf16 + 16 (banks)
 constexpr int QA_BYTES = QG_BM * QROW;
 constexpr int QB_BYTES = QG_BN * QROW;
-constexpr int QLDS = 2 * (QA_BYTES + QB_BYTES);  // 110 592
+constexpr int QS_OFF = 2 * (QA_BYTES + QB_BYTES);  // the chunks' scales, fp16 [2][QG_BN]
+constexpr int QLDS = QS_OFF + 2 * QG_BN * 2;      // 111 104
 
 __device__ __forceinline__ uint4 lds_ld16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -122,38 +125,52 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
   const uint32_t a_step = (uint32_t)(64 * K) * 2u;  // 64 rows
   const int cn = t >> 2, cq = t & 3;
   const uint32_t c_off = (uint32_t)(cn * KB + cq * CB);
-  uint4 ar[4];
-  uint32_t cr[BITS / 2];
-  float zr = ASYM ? 0.f : (float)(1 << (BITS - 1));
-  auto issue = [&](int c) {
+  // Register prefetch two chunks deep: slot c % 2 holds chunk c from its
+  // loads until its LDS stash one iteration before its compute, so a load
+  // has about two chunks of matrix work to arrive.
+  uint4 ar[2][4];
+  uint32_t cr[2][BITS / 2];
+  // fp16 bits (converted where used, so no load is waited for early): the
+  // chunk's zero point (for the decode) and its group's scale of the weight
+  // row t / 4 (stashed to LDS with the chunk, read back by the lanes of its
+  // output column after the chunk's matrix work)
+  uint16_t zr[2] = {0, 0};
+  uint16_t sr[2] = {0, 0};
+  // this lane's two output columns (C layout of the 32 x 32 tiles: lane l
+  // holds column l % 32)
+  const int col0 = wn * 64 + (lane & 31);
+  auto issue = [&](auto slot_c, int c) {
+    constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = buf_ld16(ra, a_off + i * a_step + (uint32_t)c * (QG_BK * 2));
+    for (int i = 0; i < 4; ++i)
+      ar[SL][i] = buf_ld16(ra, a_off + i * a_step + (uint32_t)c * (QG_BK * 2));
     const uint32_t off = c_off + (uint32_t)c * (QG_BK * BITS / 8);
     if (BITS == 2) {
-      cr[0] = buf_ld4(rc, off);
+      cr[SL][0] = buf_ld4(rc, off);
     } else {
       const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)off, 0, 0);
-      cr[0] = v.x;
-      cr[BITS / 2 - 1] = v.y;
+      cr[SL][0] = v.x;
+      cr[SL][BITS / 2 - 1] = v.y;
     }
-    if (ASYM) {
-      const int g = c * QG_BK / G;
-      zr = half_to_float(__builtin_amdgcn_raw_buffer_load_b16(rz, (int)((cn * NG + g) * 2), 0, 0));
-    }
+    const int g = c * QG_BK / G;
+    if (ASYM) zr[SL] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)((cn * NG + g) * 2), 0, 0);
+    sr[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)((cn * NG + g) * 2), 0, 0);
   };
-  auto stash = [&](int bi) {
+  auto stash = [&](auto slot_c, int bi) {
+    constexpr int SL = decltype(slot_c)::value;
     uint8_t* Ab = smem + bi * QA_BYTES;
     uint8_t* Bb = smem + 2 * QA_BYTES + bi * QB_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_st16(Ab + (arow + 64 * i) * QROW + akc * 16, ar[i]);
+    for (int i = 0; i < 4; ++i) lds_st16(Ab + (arow + 64 * i) * QROW + akc * 16, ar[SL][i]);
     uint32_t x[BITS / 2];
 #pragma unroll
     for (int h = 0; h < BITS / 2; ++h)
-      x[h] = ASYM ? cr[h] : cr[h] ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
+      x[h] = ASYM ? cr[SL][h] : cr[SL][h] ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
     uint32_t w[8];
-    decode16<BITS>(x, zr, w);
+    decode16<BITS>(x, ASYM ? half_to_float(zr[SL]) : (float)(1 << (BITS - 1)), w);
     lds_st16(Bb + cn * QROW + cq * 32, make_uint4(w[0], w[1], w[2], w[3]));
     lds_st16(Bb + cn * QROW + cq * 32 + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    if (cq == 0) *reinterpret_cast<uint16_t*>(smem + QS_OFF + bi * (QG_BN * 2) + cn * 2) = sr[SL];
   };
 
   f32x16_t Y[2][2], Pg[2][2];
@@ -163,29 +180,25 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
 #pragma unroll
     for (int j = 0; j < 2; ++j) Y[i][j] = zero;
 
-  // this lane's two output columns (C layout of the 32 x 32 tiles: lane l
-  // holds column l % 32)
-  const int col0 = wn * 64 + (lane & 31);
-  float sc[2] = {0.f, 0.f};
 
   const int nch = K / QG_BK, cpg = G / QG_BK;
-  issue(0);
-  stash(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  issue(S0(), 0);
+  issue(S1(), 1);
+  stash(S0(), 0);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int bi = c & 1;
-    const bool more = c + 1 < nch;
+  // chunk c: its slot and LDS buffer are c % 2 (SL)
+  auto body = [&](auto slot_c, int c) {
+    constexpr int SL = decltype(slot_c)::value;
+    using Next = std::integral_constant<int, SL ^ 1>;
     const bool gfirst = (c % cpg) == 0, glast = (c % cpg) == cpg - 1;
-    if (more) issue(c + 1);
-    if (gfirst) {
-      const int g = c / cpg;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sc[j] = half_to_float(
-            __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(((col0 + 32 * j) * NG + g) * 2), 0, 0));
-    }
-    const uint8_t* Ab = smem + bi * QA_BYTES + (wm * 64 + (lane & 31)) * QROW + (lane >> 5) * 16;
-    const uint8_t* Bb = smem + 2 * QA_BYTES + bi * QB_BYTES + col0 * QROW + (lane >> 5) * 16;
+    // Unconditional (a conditional load makes the waits below conservative
+    // and drains the prefetch): past the last chunk the offsets only reach
+    // other rows' data or fall outside the ranges, and nothing uses them.
+    issue(slot_c, c + 2);
+    const uint8_t* Ab = smem + SL * QA_BYTES + (wm * 64 + (lane & 31)) * QROW + (lane >> 5) * 16;
+    const uint8_t* Bb = smem + 2 * QA_BYTES + SL * QB_BYTES + col0 * QROW + (lane >> 5) * 16;
 #pragma unroll
     for (int kk = 0; kk < QG_BK / 16; ++kk) {
       bf16x8_t af[2], bfr[2];
@@ -210,16 +223,25 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
       }
     }
     if (glast) {
+      const uint16_t* sl = reinterpret_cast<const uint16_t*>(smem + QS_OFF + SL * (QG_BN * 2));
+      const float s_now[2] = {half_to_float(sl[col0]), half_to_float(sl[col0 + 32])};
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) Y[i][j][r] = fmaf(sc[j], Pg[i][j][r], Y[i][j][r]);
+          for (int r = 0; r < 16; ++r)
+            Y[i][j][r] = fmaf(s_now[j], Pg[i][j][r], Y[i][j][r]);
     }
-    if (more) stash(bi ^ 1);
+    stash(Next(), SL ^ 1);  // past the last chunk: into the idle buffer, unread
     __syncthreads();
+  };
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    body(S0(), c);
+    body(S1(), c + 1);
   }
+  if (c < nch) body(S0(), c);
 
   // store: register r of tile (i, j) is row 8 (r / 4) + 4 (lane / 32) + r % 4
   // of the tile, column lane % 32; rows past the end fall outside the range
