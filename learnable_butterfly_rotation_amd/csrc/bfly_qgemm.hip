@@ -30,12 +30,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int QTHREADS = 512;
 constexpr int QROW = QG_BK * 2 + 16;  // LDS bytes per tile row: 64 bf16 + 16 (banks)
-constexpr int QA_BYTES = QG_BM * QROW;
-constexpr int QB_BYTES = QG_BN * QROW;
-constexpr int QS_OFF = 2 * (QA_BYTES + QB_BYTES);  // the chunks' scales, fp16 [2][QG_BN]
-constexpr int QLDS = QS_OFF + 2 * QG_BN * 2;      // 111 104
+
+// Tile shape for BM rows x QG_BN outputs: BM / 64 x 2 waves of 64 x 64.
+template <int BM>
+struct QTile {
+  static constexpr int THREADS = 2 * BM;
+  static constexpr int WMC = BM / 64;                  // waves along the rows
+  static constexpr int A_BYTES = BM * QROW;
+  static constexpr int B_BYTES = QG_BN * QROW;
+  static constexpr int S_OFF = 2 * (A_BYTES + B_BYTES);  // the chunks' scales, fp16 [2][QG_BN]
+  static constexpr int LDS = S_OFF + 2 * QG_BN * 2;
+  static constexpr int TPR = THREADS / QG_BN;          // threads per weight row (decode)
+  static constexpr int CPT = QG_BK / TPR;              // codes per thread per chunk
+};
 
 __device__ __forceinline__ uint4 lds_ld16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -89,11 +97,15 @@ __device__ __forceinline__ void decode16(const uint32_t (&x)[BITS / 2], float z,
   for (int i = 0; i < 8; ++i) w[i] = pack_exact(f[2 * i], f[2 * i + 1]);
 }
 
-template <int BITS, bool ASYM, bool YBF16>
-__global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P) {
+template <int BM, int BITS, bool ASYM, bool YBF16>
+__global__ __launch_bounds__(QTile<BM>::THREADS, BM == 128 ? 2 : 1) void qgemm_kernel(
+    const QgemmParams P) {
+  using T = QTile<BM>;
+  constexpr int QA_BYTES = T::A_BYTES, QB_BYTES = T::B_BYTES, QS_OFF = T::S_OFF;
+  constexpr int TPR = T::TPR, CPT = T::CPT;
   extern __shared__ __align__(16) uint8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wm = wv & 3, wn = wv >> 2;
+  const int wm = wv % T::WMC, wn = wv / T::WMC;
   const int K = P.k, N = P.n_out, G = P.group;
   const int NT = N / QG_BN;
 
@@ -105,11 +117,12 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
   const uint32_t logical = xcd * per + (xcd < rem ? xcd : rem) + (b >> 3);
   const int mt = (int)(logical / (uint32_t)NT);
   const int nt = (int)(logical - (uint32_t)mt * (uint32_t)NT);
-  const int64_t m0 = (int64_t)mt * QG_BM;
+  const int64_t m0 = (int64_t)mt * BM;
   const int n0 = nt * QG_BN;
-  const int mrows = group_rows(P.rows, mt, QG_BM);
+  const int mrows = group_rows(P.rows, mt, BM);
 
-  constexpr int CB = BITS * 2;  // code bytes per thread per chunk (16 codes)
+  constexpr int CB = CPT * BITS / 8;  // code bytes per thread per chunk
+  constexpr int NW = CB / 4;          // ... as 32-bit words
   const int KB = K * BITS / 8;  // code bytes per weight row
   const int NG = K / G;         // groups per weight row
   const auto ra = buffer_range32(P.a + m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
@@ -118,18 +131,18 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
   const auto rz = buffer_range32(ASYM ? P.zeros + (int64_t)n0 * NG : P.scales,
                                  ASYM ? (uint32_t)(QG_BN * NG * 2) : 0u);
 
-  // loads of one chunk: activations 4 x 16 B per thread (rows t/8 + 64 i),
-  // codes of one weight row (t / 4), elements 16 (t % 4) .. + 15
+  // loads of one chunk: activations 4 x 16 B per thread (rows t/8 + BM/4 i),
+  // codes of one weight row (t / TPR), elements CPT (t % TPR) .. + CPT-1
   const int arow = t >> 3, akc = t & 7;
   const uint32_t a_off = (uint32_t)(arow * K + akc * 8) * 2u;
-  const uint32_t a_step = (uint32_t)(64 * K) * 2u;  // 64 rows
-  const int cn = t >> 2, cq = t & 3;
+  const uint32_t a_step = (uint32_t)(BM / 4 * K) * 2u;
+  const int cn = t / TPR, cq = t % TPR;
   const uint32_t c_off = (uint32_t)(cn * KB + cq * CB);
   // Register prefetch two chunks deep: slot c % 2 holds chunk c from its
   // loads until its LDS stash one iteration before its compute, so a load
   // has about two chunks of matrix work to arrive.
   uint4 ar[2][4];
-  uint32_t cr[2][BITS / 2];
+  uint32_t cr[2][NW];
   // fp16 bits (converted where used, so no load is waited for early): the
   // chunk's zero point (for the decode) and its group's scale of the weight
   // row t / 4 (stashed to LDS with the chunk, read back by the lanes of its
@@ -145,12 +158,18 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
     for (int i = 0; i < 4; ++i)
       ar[SL][i] = buf_ld16(ra, a_off + i * a_step + (uint32_t)c * (QG_BK * 2));
     const uint32_t off = c_off + (uint32_t)c * (QG_BK * BITS / 8);
-    if (BITS == 2) {
+    if (NW == 1) {
       cr[SL][0] = buf_ld4(rc, off);
-    } else {
+    } else if (NW == 2) {
       const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)off, 0, 0);
       cr[SL][0] = v.x;
-      cr[SL][BITS / 2 - 1] = v.y;
+      cr[SL][NW - 1] = v.y;
+    } else {
+      const uint4 v = buf_ld16(rc, off);
+      cr[SL][0] = v.x;
+      cr[SL][1 % NW] = v.y;
+      cr[SL][2 % NW] = v.z;
+      cr[SL][3 % NW] = v.w;
     }
     const int g = c * QG_BK / G;
     if (ASYM) zr[SL] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)((cn * NG + g) * 2), 0, 0);
@@ -161,15 +180,22 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
     uint8_t* Ab = smem + bi * QA_BYTES;
     uint8_t* Bb = smem + 2 * QA_BYTES + bi * QB_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_st16(Ab + (arow + 64 * i) * QROW + akc * 16, ar[SL][i]);
-    uint32_t x[BITS / 2];
+    for (int i = 0; i < 4; ++i) lds_st16(Ab + (arow + BM / 4 * i) * QROW + akc * 16, ar[SL][i]);
+    const float z = ASYM ? half_to_float(zr[SL]) : (float)(1 << (BITS - 1));
 #pragma unroll
-    for (int h = 0; h < BITS / 2; ++h)
-      x[h] = ASYM ? cr[SL][h] : cr[SL][h] ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
-    uint32_t w[8];
-    decode16<BITS>(x, ASYM ? half_to_float(zr[SL]) : (float)(1 << (BITS - 1)), w);
-    lds_st16(Bb + cn * QROW + cq * 32, make_uint4(w[0], w[1], w[2], w[3]));
-    lds_st16(Bb + cn * QROW + cq * 32 + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    for (int u = 0; u < CPT / 16; ++u) {  // 16 codes at a time
+      uint32_t x[BITS / 2];
+#pragma unroll
+      for (int h = 0; h < BITS / 2; ++h) {
+        const uint32_t v = cr[SL][u * (BITS / 2) + h];
+        x[h] = ASYM ? v : v ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
+      }
+      uint32_t w[8];
+      decode16<BITS>(x, z, w);
+      uint8_t* dst = Bb + cn * QROW + cq * (CPT * 2) + u * 32;
+      lds_st16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+      lds_st16(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    }
     if (cq == 0) *reinterpret_cast<uint16_t*>(smem + QS_OFF + bi * (QG_BN * 2) + cn * 2) = sr[SL];
   };
 
@@ -263,13 +289,15 @@ __global__ __launch_bounds__(QTHREADS, 1) void qgemm_kernel(const QgemmParams P)
 
 template <int BITS, bool ASYM, bool YBF16>
 hipError_t launch_one(const QgemmParams& p, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BITS, ASYM, YBF16>);
-  static const hipError_t lds_ok = allow_lds(fn, QLDS);
+  constexpr int BM = QG_BM;
+  using T = QTile<BM>;
+  const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BM, BITS, ASYM, YBF16>);
+  static const hipError_t lds_ok = allow_lds(fn, T::LDS);
   if (lds_ok != hipSuccess) return lds_ok;
-  const int64_t mt = (p.rows + QG_BM - 1) / QG_BM;
+  const int64_t mt = (p.rows + BM - 1) / BM;
   const int64_t blocks = mt * (p.n_out / QG_BN);
-  hipLaunchKernelGGL((qgemm_kernel<BITS, ASYM, YBF16>), dim3((unsigned)blocks), dim3(QTHREADS),
-                     QLDS, s, p);
+  hipLaunchKernelGGL((qgemm_kernel<BM, BITS, ASYM, YBF16>), dim3((unsigned)blocks),
+                     dim3(T::THREADS), T::LDS, s, p);
   return hipGetLastError();
 }
 
