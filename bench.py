@@ -21,7 +21,8 @@ counters recorded for the current kernel sources (null if they changed).
 
 --workload picks one of the other parity workloads for a secondary line
 (tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
-calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008); --copy-probe runs a plain device copy of known
+calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
+kron_bwd_n5120_fp32); --copy-probe runs a plain device copy of known
 size (for calibrating the byte counters).
 """
 from __future__ import annotations
@@ -351,6 +352,23 @@ def bench_secondary(args, torch, B, inputs):
                    TFLOPs=flops / kern_s / 1e12, mfma_bf16_peak_TFLOPs=MFMA_BF16_PEAK_TFLOPS,
                    frac_of_mfma_peak=flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                    hbm_bytes=hbm, GBs_hbm=hbm / kern_s / 1e9)
+    elif name == "kron_bwd_n5120_fp32":
+        # Gradients of the composite O5 (x) B1024 on 32768 fp32 rows (x, G
+        # drawn on the GPU from a seeded generator): dX and dtheta_b.
+        w = inputs.kron_int4()
+        rows, m, nb = 32768, 5, 1024
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        X = torch.randn((rows, m * nb), device="cuda", generator=gen)
+        G = torch.randn((rows, m * nb), device="cuda", generator=gen)
+        dX = torch.empty_like(X)
+        dth = torch.empty((10, 512), device="cuda")
+        th, mix = to_dev(w["theta_b"], torch), to_dev(w["mix"], torch)
+        ws = torch.empty(B.bfly_kron_backward_workspace_bytes(rows, m, nb), dtype=torch.uint8,
+                         device="cuda")
+        t = time_loop(torch, lambda i: B.bfly_kron_backward(X, G, dX, dth, mix, ws, theta_b=th),
+                      args.steps, args.warmup)
+        b = rows * m * nb * 12  # x and G read, dX written once
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t)
     elif name == "calib_n4096_fp32_fwd_bwd":
         c = inputs.CalibFP32()
         X = torch.empty((c.rows, c.n), device="cuda")

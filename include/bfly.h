@@ -175,6 +175,28 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
 
 size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n);
 
+/* Gradients of the Kronecker composite y = (O kron B(theta_b)) x (see
+ * bfly_kron_forward; O = mix, fixed), for learning theta_b.  Given X and
+ * G = dL/dY (device fp32 [rows][m*nb]):
+ *   dx       : (O kron B)^T G                   fp32 [rows][m*nb] (may be g)
+ *   dtheta_b : sum over rows and segments of dL/dtheta_b, fp32
+ *              [log2 nb][nb/2], OVERWRITTEN (zeros when rows == 0)
+ * Computed as dL/dz = (O^T kron I) G, then the butterfly backward on the
+ * rows * m segments of length nb (z = (I kron B) x per segment), with the
+ * same fixed-order reduction as bfly_backward.  Sizes: m in [2, 8] (m = 1
+ * is the plain butterfly: bfly_backward), nb a power of two in [256, 4096],
+ * m * nb <= 8192.  workspace: >= bfly_kron_backward_workspace_bytes(rows, m,
+ * nb) bytes of device scratch, 16-byte aligned; the call allocates nothing.
+ * Errors as bfly_backward.  Passages: ButterflyQuant write-up, section
+ * "butterfly" (the Kronecker composite for widths like 5120) and section
+ * "training and results" (the angles are learned by gradient descent). */
+bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float* dtheta_b,
+                               int64_t rows, int32_t m, int32_t nb, const float* theta_b,
+                               const void* coeffs_b, const float* mix, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
+size_t bfly_kron_backward_workspace_bytes(int64_t rows, int32_t m, int32_t nb);
+
 /* ---- consumer of the quantized weights ---------------------------------- */
 
 /* y[r][o] = sum_k a[r][k] * w[o][k] for r < rows, o < n_out: the layer

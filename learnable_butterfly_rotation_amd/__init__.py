@@ -18,7 +18,8 @@ __all__ = [
     "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
     "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_prepare_hadamard",
     "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_quant_matmul",
-    "bfly_backward", "bfly_backward_workspace_bytes", "bfly_status_string",
+    "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
+    "bfly_kron_backward_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error",
 ]
 
@@ -68,11 +69,15 @@ def lib():
         L.bfly_backward.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.bfly_backward_workspace_bytes.argtypes = [i64, i32]
         L.bfly_backward_workspace_bytes.restype = sz
+        L.bfly_kron_backward.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.bfly_kron_backward_workspace_bytes.argtypes = [i64, i32, i32]
+        L.bfly_kron_backward_workspace_bytes.restype = sz
         L.bfly_status_string.argtypes = [ctypes.c_int]
         L.bfly_status_string.restype = ctypes.c_char_p
         L.bfly_last_hip_error.restype = i32
         for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
-                  L.bfly_kron_forward, L.bfly_quant_matmul, L.bfly_backward):
+                  L.bfly_kron_forward, L.bfly_quant_matmul, L.bfly_backward,
+                  L.bfly_kron_backward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,3 +194,19 @@ def bfly_status_string(status: int) -> str:
 
 def bfly_last_hip_error() -> int:
     return lib().bfly_last_hip_error()
+
+
+def bfly_kron_backward_workspace_bytes(rows: int, m: int, nb: int) -> int:
+    return lib().bfly_kron_backward_workspace_bytes(rows, m, nb)
+
+
+def bfly_kron_backward(x, g, dx, dtheta_b, mix, workspace, theta_b=None, coeffs_b=None,
+                       stream=None) -> None:
+    """dx = (O kron B)^T g and dtheta_b (summed over rows and segments);
+    x, g, dx: [rows, m*nb] float32; mix: [m, m] float32 on the GPU."""
+    rows, n = x.shape
+    m = mix.shape[0]
+    _check(lib().bfly_kron_backward(_ptr(x), _ptr(g), _ptr(dx), _ptr(dtheta_b), rows, m, n // m,
+                                    _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "bfly_kron_backward")

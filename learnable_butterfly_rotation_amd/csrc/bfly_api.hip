@@ -18,6 +18,8 @@ hipError_t launch_forward_kron_m5(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m6(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m7(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m8(const FwdParams& p, hipStream_t s);
+hipError_t launch_kron_bwd_setup(const float* mix, int m, float* mix_t, float* theta0, int n_theta,
+                                 hipStream_t s);
 
 bool forward_supported(int lognb, int m) {
   if (m == 1) return lognb >= 6 && lognb <= 12;
@@ -270,6 +272,78 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);
   const hipError_t e = bfly::launch_backward(p, dtheta, s);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+// Workspace of the Kronecker backward: O^T, a zero angle set and its
+// (identity) table, then the butterfly backward's own workspace for the
+// rows * m segments.
+static size_t kron_bwd_parts(int64_t rows, int32_t m, int lognb, size_t* off_theta0,
+                             size_t* off_table, size_t* off_bwd) {
+  const int nb = 1 << lognb;
+  const size_t t0 = 256;
+  const size_t tab = align_up(t0 + sizeof(float) * (size_t)lognb * (nb / 2), 256);
+  const size_t bwd = align_up(tab + coeff_bytes_l(lognb), 256);
+  const size_t total = bwd + bfly_backward_workspace_bytes(rows * m, nb);
+  if (off_theta0) *off_theta0 = t0;
+  if (off_table) *off_table = tab;
+  if (off_bwd) *off_bwd = bwd;
+  return total;
+}
+
+size_t bfly_kron_backward_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
+  int l = 0;
+  if (rows < 0 || m < 2 || m > 8 || check_n(nb, 12, &l) != BFLY_OK) return 0;
+  if (!bfly::forward_supported(l, m)) return 0;
+  return kron_bwd_parts(rows, m, l, nullptr, nullptr, nullptr);
+}
+
+bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float* dtheta_b,
+                               int64_t rows, int32_t m, int32_t nb, const float* theta_b,
+                               const void* coeffs_b, const float* mix, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  if ((rows > 0 && (!x || !g || !dx)) || !dtheta_b || !mix || !workspace) return BFLY_ERR_NULL;
+  if (!theta_b && !coeffs_b) return BFLY_ERR_NULL;
+  if (rows < 0) return BFLY_ERR_SIZE;
+  if (m < 1 || m > 8) return BFLY_ERR_SIZE;
+  int l = 0;
+  const bfly_status st = check_n(nb, 12, &l);
+  if (st != BFLY_OK) return st;
+  if (m == 1 || !bfly::forward_supported(l, m)) return BFLY_ERR_UNSUPPORTED;
+  size_t o_th0 = 0, o_tab = 0, o_bwd = 0;
+  if (workspace_bytes < kron_bwd_parts(rows, m, l, &o_th0, &o_tab, &o_bwd))
+    return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(dx, 16) || !aligned(workspace, 16) ||
+      !aligned(dtheta_b, 4) || !aligned(mix, 4) || (coeffs_b && !aligned(coeffs_b, 16)) ||
+      (theta_b && !aligned(theta_b, 4)))
+    return BFLY_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  float* mix_t = reinterpret_cast<float*>(ws);
+  float* theta0 = reinterpret_cast<float*>(ws + o_th0);
+  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, theta0, l * (nb / 2), s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = bfly::launch_prepare(theta0, ws + o_tab, l, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (rows > 0) {
+    // dL/dz = (O^T kron I) G: the forward with the identity butterfly and O^T
+    bfly::FwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.x = g;
+    p.y = dx;
+    p.mix = mix_t;
+    p.rows = rows;
+    p.m = m;
+    p.lognb = l;
+    p.x_bf16 = 0;
+    p.y_kind = bfly::Y_F32;
+    p.tab = bfly::table_at(ws + o_tab, l);
+    e = bfly::launch_forward(p, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  // then the butterfly backward on the rows * m segments, in place on dx
+  const size_t bwd_bytes = workspace_bytes - o_bwd;
+  return bfly_backward(x, dx, nullptr, dx, dtheta_b, rows * m, nb, theta_b, coeffs_b, ws + o_bwd,
+                       bwd_bytes, hip_stream);
 }
 
 bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* codes,

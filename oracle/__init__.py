@@ -17,6 +17,11 @@ Each function cites the passage of the pages it follows:
   are applied before quantization.
 * backward -- ButterflyQuant abstract and duidaima.com section "training and
   results": the angles are learned by gradient descent.
+* kron_backward -- gradients of the Kronecker composite (duidaima.com
+  section "butterfly" for the composite, section "training and results" for
+  learning the angles): dL/dz = (O^T kron I) G in fp64, then the butterfly
+  backward on the rows * m segments.  The C backward reads its G in fp32,
+  so dL/dz is rounded to fp32 first (2^-24 relative).
 * hadamard_matrix / hadamard / kron_hadamard -- the Hadamard special case
   (duidaima.com write-up, section "butterfly": H_n for n = 2^k is a butterfly
   with particular angles; ButterflyQuant abstract: Hadamard entries are +-1,
@@ -282,3 +287,18 @@ def quant_matmul(a: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros, bi
     a = widen(np.ascontiguousarray(a))
     w = dequantize(codes, scales, zeros, bits, group, mode, a.shape[1])
     return a @ w.T
+
+
+def kron_backward(x: np.ndarray, g: np.ndarray, theta_b: np.ndarray, mix: np.ndarray):
+    """Gradients of y = (O kron B(theta_b)) x with O = mix fixed: returns
+    dict(dx (fp64 [rows][m*nb]), dtheta (fp64 [log2 nb][nb/2]), dabs)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    mix64 = np.asarray(mix, dtype=np.float32).astype(np.float64)
+    m = mix64.shape[0]
+    rows, n = x.shape
+    nb = n // m
+    g3 = np.asarray(g, dtype=np.float32).astype(np.float64).reshape(rows, m, nb)
+    # dL/dz[r][a'][b] = sum_a O[a][a'] G[r][a][b]
+    gz = np.einsum("ab,rai->rbi", mix64, g3).reshape(rows * m, nb)
+    out = backward(x.reshape(rows * m, nb), gz.astype(np.float32), theta_b, want_y=False)
+    return {"dx": out["dx"].reshape(rows, n), "dtheta": out["dtheta"], "dabs": out["dabs"]}

@@ -200,3 +200,31 @@ def test_quant_matmul_validation(L):
     assert qm(L, a=ctypes.c_void_p(0x10008)) == ALIGN
     assert qm(L, y=ctypes.c_void_p(0x20004)) == ALIGN
     assert qm(L, s=ctypes.c_void_p(0x40001)) == ALIGN
+
+
+def kb(L, x=X, g=X, dx=Y, dth=C, rows=16, m=5, nb=1024, th=TH, co=None, mix=MIX, ws=WS,
+       wsb=None):
+    if wsb is None:
+        wsb = B.bfly_kron_backward_workspace_bytes(max(rows, 0), m, nb)
+    return L.bfly_kron_backward(x, g, dx, dth, rows, m, nb, th, co, mix, ws, wsb, None)
+
+
+def test_kron_backward_validation(L):
+    assert B.bfly_kron_backward_workspace_bytes(16, 5, 1024) > B.bfly_backward_workspace_bytes(80, 1024)
+    assert B.bfly_kron_backward_workspace_bytes(16, 1, 1024) == 0
+    assert B.bfly_kron_backward_workspace_bytes(16, 9, 256) == 0
+    assert B.bfly_kron_backward_workspace_bytes(16, 5, 8192) == 0
+    assert kb(L, x=None) == NULL
+    assert kb(L, mix=None) == NULL
+    assert kb(L, dth=None) == NULL
+    assert kb(L, th=None, co=None) == NULL
+    assert kb(L, ws=None) == NULL
+    assert kb(L, rows=-1, wsb=1 << 30) == SIZE
+    assert kb(L, m=0, wsb=1 << 30) == SIZE
+    assert kb(L, m=9, wsb=1 << 30) == SIZE
+    assert kb(L, nb=1000, wsb=1 << 30) == SIZE
+    assert kb(L, m=1, wsb=1 << 30) == UNSUPPORTED
+    assert kb(L, m=3, nb=4096, wsb=1 << 30) == UNSUPPORTED   # m * nb > 8192
+    assert kb(L, wsb=B.bfly_kron_backward_workspace_bytes(16, 5, 1024) - 1) == WORKSPACE
+    assert kb(L, dx=ctypes.c_void_p(0x20008)) == ALIGN
+    assert kb(L, ws=ctypes.c_void_p(0x80008)) == ALIGN

@@ -601,3 +601,33 @@ def test_calibration_workload_full():
         m = x.shape[0]
         assert check_f32(host(Y[r0:r0 + m]), y64, np.abs(x).max(1), n)["ok"]
         assert check_f32(host(dX[r0:r0 + m]), dx64, np.abs(g).max(1), n)["ok"]
+
+
+# ---------------------------------------------------------------------------
+# Kronecker backward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,nb,rows", [(5, 1024, 37), (2, 256, 300), (3, 2048, 9), (8, 1024, 64)])
+def test_kron_backward(m, nb, rows):
+    rng = np.random.default_rng(5000 + 10 * m + nb + rows)
+    th = rand_theta(rng, nb)
+    mix = inputs.mixing_factor(rng, m)
+    n = m * nb
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    g = rng.standard_normal((rows, n)).astype(np.float32)
+    ref = oracle.kron_backward(x, g, th, mix)
+    xd, gd = dev(x), dev(g)
+    dx = empty((rows, n), torch.float32)
+    dth = empty(th.shape, torch.float32)
+    ws = torch.empty(B.bfly_kron_backward_workspace_bytes(rows, m, nb), dtype=torch.uint8,
+                     device="cuda")
+    B.bfly_kron_backward(xd, gd, dx, dth, dev(mix), ws, theta_b=dev(th))
+    L = int(math.log2(nb))
+    # dx: per element against the row's |g| (the fp32 mix and butterfly)
+    ginf = np.abs(g).max(axis=1, keepdims=True)
+    assert (np.abs(host(dx) - ref["dx"]) <= 1e-5 * L * m * ginf).all()
+    r = check_dtheta(host(dth), ref["dtheta"], ref["dabs"], nb)
+    assert r["ok"], r
+    # in place on g gives the same bits; a second call (same workspace) too
+    B.bfly_kron_backward(xd, gd, gd, dth, dev(mix), ws, theta_b=dev(th))
+    assert np.array_equal(host(gd), host(dx))

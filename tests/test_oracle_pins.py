@@ -585,3 +585,31 @@ def test_quant_matmul_computational_invariance():
     bound += 1e-6 * np.abs(x).max() * np.abs(w).max() * n  # fp32 rounding of Q x
     assert (np.abs(y - wx) <= bound).all()
     assert np.abs(y - wx).max() > 0  # the quantization is not a no-op
+
+
+# --- the Kronecker backward
+
+def test_kron_backward_finite_differences_and_dense_transpose():
+    m, nb = 3, 8
+    th = rand_theta(nb)
+    mix = inputs.mixing_factor(RNG, m)
+    x = RNG.standard_normal((4, m * nb)).astype(np.float32)
+    g = RNG.standard_normal((4, m * nb)).astype(np.float32)
+    out = oracle.kron_backward(x, g, th, mix)
+    # dx = G (O kron Q), from the dense matrices
+    dense = np.kron(mix.astype(np.float64), oracle.dense_q(th))
+    assert np.abs(out["dx"] - g.astype(np.float64) @ dense).max() < 1e-6
+    g64 = g.astype(np.float64)
+
+    def loss(t):
+        return float((oracle.kron_forward(x, t, mix) * g64).sum())
+
+    for s in range(3):
+        for p in range(nb // 2):
+            def fd(h):
+                tp, tm = th.copy(), th.copy()
+                tp[s, p] = np.float32(th[s, p] + h)
+                tm[s, p] = np.float32(th[s, p] - h)
+                return (loss(tp) - loss(tm)) / (float(tp[s, p]) - float(tm[s, p]))
+            rich = (4 * fd(2.0 ** -8) - fd(2.0 ** -7)) / 3
+            assert abs(rich - out["dtheta"][s, p]) < 1e-5 * (1 + abs(rich)), (s, p)
