@@ -22,7 +22,7 @@ counters recorded for the current kernel sources (null if they changed).
 --workload picks one of the other parity workloads for a secondary line
 (tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
 calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
-kron_bwd_n5120_fp32); --copy-probe runs a plain device copy of known
+kron_bwd_n5120_fp32, kron_n11008_bf16_int4); --copy-probe runs a plain device copy of known
 size (for calibrating the byte counters).
 """
 from __future__ import annotations
@@ -352,6 +352,29 @@ def bench_secondary(args, torch, B, inputs):
                    TFLOPs=flops / kern_s / 1e12, mfma_bf16_peak_TFLOPs=MFMA_BF16_PEAK_TFLOPS,
                    frac_of_mfma_peak=flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                    hbm_bytes=hbm, GBs_hbm=hbm / kern_s / 1e9)
+    elif name == "kron_n11008_bf16_int4":
+        # O43 (x) B256 on 8192 bf16 rows, sym INT4 g128: the mix pass into an
+        # fp32 workspace, then the fused butterfly + quantizer on the segments.
+        w = inputs.kron_wide_int4()
+        th, mix = to_dev(w["theta_b"], torch), to_dev(w["mix"], torch)
+        rows, n, m, nb = w["rows"], w["n"], w["m"], w["nb"]
+        sets = []  # 3 sets (700 MB) so no step finds its rows in cache
+        for _ in range(3):
+            x = to_dev(w["x"], torch)
+            sets.append((x, torch.empty_like(x), torch.empty((rows, n // 2), dtype=torch.uint8, device="cuda"),
+                         torch.empty((rows, n // 128), dtype=torch.float16, device="cuda")))
+        ws = torch.empty(B.bfly_kron_forward_wide_workspace_bytes(rows, m, nb), dtype=torch.uint8,
+                         device="cuda")
+        tab = torch.empty(B.bfly_coeff_bytes(nb), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            x, y, c, s = sets[i % 3]
+            B.bfly_prepare(th, nb, tab)
+            B.bfly_kron_forward_wide(x, y, mix, ws, c, s, coeffs_b=tab, bits=4, group=128)
+        t = time_loop(torch, fn, args.steps, args.warmup)
+        b = rows * (2 * n + 2 * n + n // 2 + 2 * (n // 128))
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t,
+                   fp32_intermediate_bytes=rows * n * 8)
     elif name == "kron_bwd_n5120_fp32":
         # Gradients of the composite O5 (x) B1024 on 32768 fp32 rows (x, G
         # drawn on the GPU from a seeded generator): dX and dtheta_b.

@@ -155,6 +155,29 @@ bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtyp
                               const void* coeffs_b, const float* mix,
                               int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
 
+/* Kronecker composites with more segments: the same y[r] = (O kron
+ * B(theta_b)) x[r] and optional quantization as bfly_kron_forward, for
+ * m in [2, 64] (e.g. 11008 = 43 * 256), nb a power of two in [256, 4096],
+ * m * nb <= 65536.  Two passes: v = (O kron I) x in fp32 into `workspace`,
+ * then the butterfly with its fused quantizer on the rows * m segments of v
+ * ((O kron B) = (I kron B)(O kron I)).  workspace: >=
+ * bfly_kron_forward_wide_workspace_bytes(rows, m, nb) = rows * m * nb * 4
+ * bytes of device memory, 16-byte aligned, caller-owned.  codes == NULL =>
+ * no quantization (scales, zeros then NULL); otherwise as in
+ * bfly_forward_quant with group dividing nb.  With theta_b (no coeffs_b)
+ * the table is prepared as in bfly_forward.  Errors as bfly_kron_forward,
+ * plus BFLY_ERR_WORKSPACE.  Passage: ButterflyQuant write-up, section
+ * "butterfly" (Kronecker composites for widths that are not powers of
+ * two). */
+bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                   uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                   int64_t rows, int32_t m, int32_t nb, const float* theta_b,
+                                   const void* coeffs_b, const float* mix, int32_t bits,
+                                   int32_t group, bfly_qmode mode, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+
+size_t bfly_kron_forward_wide_workspace_bytes(int64_t rows, int32_t m, int32_t nb);
+
 /* ---- backward ----------------------------------------------------------- */
 
 /* Gradients for learning the angles (ButterflyQuant abstract: smooth

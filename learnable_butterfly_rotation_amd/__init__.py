@@ -17,7 +17,8 @@ import os
 __all__ = [
     "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
     "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_prepare_hadamard",
-    "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_quant_matmul",
+    "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_kron_forward_wide",
+    "bfly_kron_forward_wide_workspace_bytes", "bfly_quant_matmul",
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
     "bfly_kron_backward_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error",
@@ -64,6 +65,11 @@ def lib():
                                          vp, vp, i32, i32, ctypes.c_int, vp]
         L.bfly_kron_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
                                         i32, vp, vp, vp, i32, i32, ctypes.c_int, vp]
+        L.bfly_kron_forward_wide.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64,
+                                             i32, i32, vp, vp, vp, i32, i32, ctypes.c_int, vp, sz,
+                                             vp]
+        L.bfly_kron_forward_wide_workspace_bytes.argtypes = [i64, i32, i32]
+        L.bfly_kron_forward_wide_workspace_bytes.restype = sz
         L.bfly_quant_matmul.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, i64, i32,
                                         i32, i32, i32, ctypes.c_int, vp]
         L.bfly_backward.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
@@ -76,7 +82,8 @@ def lib():
         L.bfly_status_string.restype = ctypes.c_char_p
         L.bfly_last_hip_error.restype = i32
         for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
-                  L.bfly_kron_forward, L.bfly_quant_matmul, L.bfly_backward,
+                  L.bfly_kron_forward, L.bfly_kron_forward_wide, L.bfly_quant_matmul,
+                  L.bfly_backward,
                   L.bfly_kron_backward):
             f.restype = ctypes.c_int
         _lib = L
@@ -162,6 +169,24 @@ def bfly_kron_forward(x, y, mix, codes=None, scales=None, zeros=None, theta_b=No
                                    _ptr(codes), _ptr(scales), _ptr(zeros), rows, m, n // m,
                                    _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), bits, group, mode,
                                    _stream(stream)), "bfly_kron_forward")
+
+
+def bfly_kron_forward_wide_workspace_bytes(rows: int, m: int, nb: int) -> int:
+    return lib().bfly_kron_forward_wide_workspace_bytes(rows, m, nb)
+
+
+def bfly_kron_forward_wide(x, y, mix, workspace, codes=None, scales=None, zeros=None,
+                           theta_b=None, coeffs_b=None, bits=4, group=128,
+                           mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+    """(O kron B) on rows of n = m * nb for m up to 64 (two passes through
+    `workspace`, a uint8 tensor of bfly_kron_forward_wide_workspace_bytes)."""
+    rows, n = x.shape
+    m = mix.shape[0]
+    _check(lib().bfly_kron_forward_wide(
+        _ptr(x), _dt(x), _ptr(y), _dt(y) if y is not None else 0, _ptr(codes), _ptr(scales),
+        _ptr(zeros), rows, m, n // m, _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), bits, group, mode,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "bfly_kron_forward_wide")
 
 
 def bfly_quant_matmul(a, codes, scales, zeros, y, bits=2, group=128, mode=BFLY_ASYM_MINMAX,

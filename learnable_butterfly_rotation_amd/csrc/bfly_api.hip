@@ -18,6 +18,8 @@ hipError_t launch_forward_kron_m5(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m6(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m7(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m8(const FwdParams& p, hipStream_t s);
+hipError_t launch_kron_mix(const void* x, bool xbf16, float* v, const float* mix, int64_t rows,
+                           int m, int nb, hipStream_t s);
 hipError_t launch_kron_bwd_setup(const float* mix, int m, float* mix_t, float* theta0, int n_theta,
                                  hipStream_t s);
 
@@ -272,6 +274,57 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   p.nblk = rows == 0 ? 0 : bfly::backward_blocks(rows, l);
   const hipError_t e = bfly::launch_backward(p, dtheta, s);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+// Wide Kronecker composites: m in [2, 64], nb in [256, 4096], m * nb <= 65536.
+static bool kron_wide_sizes(int32_t m, int32_t nb, int* lognb) {
+  if (m < 2 || m > 64) return false;
+  if (check_n(nb, 12, lognb) != BFLY_OK || *lognb < 8) return false;
+  return (int64_t)m * nb <= 65536;
+}
+
+size_t bfly_kron_forward_wide_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
+  int l = 0;
+  if (rows < 0 || !kron_wide_sizes(m, nb, &l)) return 0;
+  return (size_t)rows * (size_t)m * (size_t)nb * sizeof(float);
+}
+
+bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                   uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                   int64_t rows, int32_t m, int32_t nb, const float* theta_b,
+                                   const void* coeffs_b, const float* mix, int32_t bits,
+                                   int32_t group, bfly_qmode mode, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+  const bool quant = codes != nullptr;
+  if (!mix || !workspace) return BFLY_ERR_NULL;
+  if (rows > 0 && (!x || (!y && !quant))) return BFLY_ERR_NULL;
+  if (!theta_b && !coeffs_b) return BFLY_ERR_NULL;
+  if (!quant && (scales || zeros)) return BFLY_ERR_QUANT;
+  if (!dtype_ok(x_dt) || (y && !dtype_ok(y_dt))) return BFLY_ERR_DTYPE;
+  if (rows < 0 || m < 2 || m > 64) return BFLY_ERR_SIZE;
+  int l = 0;
+  const bfly_status sn = check_n(nb, 13, &l);
+  if (sn != BFLY_OK) return sn;
+  if (!kron_wide_sizes(m, nb, &l)) return BFLY_ERR_UNSUPPORTED;
+  if (quant) {
+    const bfly_status sq = check_quant(codes, scales, zeros, rows, (int64_t)m * nb, nb, l, bits,
+                                       group, mode);
+    if (sq != BFLY_OK) return sq;
+  }
+  if (workspace_bytes < bfly_kron_forward_wide_workspace_bytes(rows, m, nb))
+    return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || (y && !aligned(y, 16)) || !aligned(workspace, 16) || !aligned(mix, 4) ||
+      (coeffs_b && !aligned(coeffs_b, 16)) || (theta_b && !aligned(theta_b, 4)))
+    return BFLY_ERR_ALIGN;
+  if (rows == 0) return BFLY_OK;
+  // v = (O kron I) x into the workspace, then the butterfly (and the
+  // quantizer) on its rows * m segments: (O kron B) = (I kron B)(O kron I)
+  float* v = static_cast<float*>(workspace);
+  const hipError_t e = bfly::launch_kron_mix(x, x_dt == BFLY_BF16, v, mix, rows, m, nb,
+                                             (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return forward_common(v, BFLY_F32, y, y_dt, codes, scales, zeros, rows * m, 1, nb, theta_b,
+                        coeffs_b, nullptr, bits, group, mode, quant, hip_stream);
 }
 
 // Workspace of the Kronecker backward: O^T, a zero angle set and its

@@ -16,7 +16,7 @@ Recipe (every tensor has its own child stream of
   then cast to the storage dtype;
 * weights: N(0, 0.02^2), no outliers;
 * gradients: N(0, 1);
-* Kronecker mixing factor: Q of the QR decomposition of a 5x5 N(0, 1) draw,
+* Kronecker mixing factor: Q of the QR decomposition of an m x m N(0, 1) draw,
   with column signs chosen so that diag(R) > 0, cast to fp32.
 
 bf16 storage is fp64 -> fp32 (round to nearest even) -> bf16 (round to nearest
@@ -77,7 +77,7 @@ def mixing_factor(rng, m: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# The five workloads.  Each returns a dict of numpy arrays plus metadata.
+# The workloads.  Each returns a dict of numpy arrays plus metadata.
 # ``rows`` may be lowered to draw the leading rows of the same workload: the
 # row draws are sequential, so the first r rows are identical whatever the
 # total.
@@ -124,6 +124,21 @@ def kron_int4(rows: int = 8192, m: int = 5, nb: int = 1024, seed: int = 3):
     cols = outlier_columns(r_cols, n)
     x = activations(r_x, rows, n, cols, "bf16")
     return {"name": "kron_n5120_bf16_int4", "n": n, "m": m, "nb": nb, "rows": rows,
+            "theta_b": theta_b, "mix": mix, "x": x, "x_dtype": "bf16", "outliers": cols,
+            "bits": 4, "group": 128, "mode": "sym"}
+
+
+def kron_wide_int4(rows: int = 8192, m: int = 43, nb: int = 256, seed: int = 6):
+    """LLaMA-2-7B MLP width 11008 = 43 x 256 (the down projection's input):
+    O43 (x) B256, bf16 activations with 0.1% x50 outliers; symmetric INT4
+    group 128."""
+    r_theta, r_mix, r_x, r_cols = _streams(seed, 4)
+    theta_b = angles(r_theta, nb)
+    mix = mixing_factor(r_mix, m)
+    n = m * nb
+    cols = outlier_columns(r_cols, n)
+    x = activations(r_x, rows, n, cols, "bf16")
+    return {"name": "kron_n11008_bf16_int4", "n": n, "m": m, "nb": nb, "rows": rows,
             "theta_b": theta_b, "mix": mix, "x": x, "x_dtype": "bf16", "outliers": cols,
             "bits": 4, "group": 128, "mode": "sym"}
 

@@ -228,3 +228,32 @@ def test_kron_backward_validation(L):
     assert kb(L, wsb=B.bfly_kron_backward_workspace_bytes(16, 5, 1024) - 1) == WORKSPACE
     assert kb(L, dx=ctypes.c_void_p(0x20008)) == ALIGN
     assert kb(L, ws=ctypes.c_void_p(0x80008)) == ALIGN
+
+
+def kw(L, x=X, y=Y, c=C, s=S, z=None, rows=16, m=43, nb=256, th=TH, co=None, mix=MIX, ws=WS,
+       wsb=None, group=128, xd=1, yd=1):
+    if wsb is None:
+        wsb = B.bfly_kron_forward_wide_workspace_bytes(max(rows, 0), m, nb)
+    return L.bfly_kron_forward_wide(x, xd, y, yd, c, s, z, rows, m, nb, th, co, mix, 4, group, 0,
+                                    ws, wsb, None)
+
+
+def test_kron_forward_wide_validation(L):
+    assert B.bfly_kron_forward_wide_workspace_bytes(16, 43, 256) == 16 * 11008 * 4
+    assert B.bfly_kron_forward_wide_workspace_bytes(16, 65, 256) == 0
+    assert B.bfly_kron_forward_wide_workspace_bytes(16, 43, 128) == 0
+    assert B.bfly_kron_forward_wide_workspace_bytes(16, 32, 4096) == 0    # m * nb > 65536
+    assert kw(L, rows=0) == OK
+    assert kw(L, x=None) == NULL
+    assert kw(L, mix=None) == NULL
+    assert kw(L, ws=None) == NULL
+    assert kw(L, th=None, co=None) == NULL
+    assert kw(L, c=None) == QUANT                      # scales without codes
+    assert kw(L, xd=5) == DTYPE
+    assert kw(L, m=1, wsb=1 << 30) == SIZE
+    assert kw(L, m=65, wsb=1 << 30) == SIZE
+    assert kw(L, nb=300, wsb=1 << 30) == SIZE
+    assert kw(L, nb=128, wsb=1 << 30) == UNSUPPORTED
+    assert kw(L, group=512) == QUANT                   # group must divide nb
+    assert kw(L, wsb=16 * 11008 * 4 - 1) == WORKSPACE
+    assert kw(L, ws=ctypes.c_void_p(0x80008)) == ALIGN

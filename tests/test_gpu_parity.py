@@ -631,3 +631,67 @@ def test_kron_backward(m, nb, rows):
     # in place on g gives the same bits; a second call (same workspace) too
     B.bfly_kron_backward(xd, gd, gd, dth, dev(mix), ws, theta_b=dev(th))
     assert np.array_equal(host(gd), host(dx))
+
+
+# ---------------------------------------------------------------------------
+# wide Kronecker composites (m up to 64): mix pass, then the fused butterfly
+# ---------------------------------------------------------------------------
+
+def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=torch.bfloat16,
+                  coeffs=False):
+    rows, n = x.shape
+    m = mix.shape[0]
+    y = empty((rows, n), y_dtype)
+    ws = torch.empty(B.bfly_kron_forward_wide_workspace_bytes(rows, m, n // m), dtype=torch.uint8,
+                     device="cuda")
+    args = {}
+    if quant:
+        args = dict(codes=torch.zeros((rows, n * bits // 8), dtype=torch.uint8, device="cuda"),
+                    scales=torch.zeros((rows, n // group), dtype=torch.float16, device="cuda"),
+                    zeros=torch.zeros((rows, n // group), dtype=torch.float16, device="cuda")
+                    if mode else None)
+    if coeffs:
+        tab = torch.empty(B.bfly_coeff_bytes(n // m), dtype=torch.uint8, device="cuda")
+        B.bfly_prepare(dev(th), n // m, tab)
+        args["coeffs_b"] = tab
+    else:
+        args["theta_b"] = dev(th)
+    B.bfly_kron_forward_wide(dev(x), y, dev(mix), ws, bits=bits, group=group, mode=mode, **args)
+    out = {"y": host(y)}
+    if quant:
+        out["codes"] = host(args["codes"])
+        out["scales"] = host(args["scales"])
+        if mode:
+            out["zeros"] = host(args["zeros"])
+    return out
+
+
+@pytest.mark.parametrize("m,nb", [(43, 256), (9, 512), (16, 1024), (64, 256), (2, 4096),
+                                  (5, 1024)])
+def test_kron_wide_shapes(m, nb):
+    rng = np.random.default_rng(7000 + 10 * m + nb)
+    th = rand_theta(rng, nb)
+    mix = inputs.mixing_factor(rng, m)
+    rows = 37
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((rows, m * nb)).astype(np.float32))
+    y64 = oracle.kron_forward(x, th, mix)
+    for quant, mode in ((False, 0), (True, 0), (True, 1)):
+        out = run_kron_wide(x, th, mix, quant=quant, mode=mode)
+        assert_forward(out["y"], y64, x, m * nb)
+        if quant:
+            assert_quant(out, y64, 4, 128, mode)
+    xf = rng.standard_normal((5, m * nb)).astype(np.float32)
+    out = run_kron_wide(xf, th, mix, quant=False, y_dtype=torch.float32, coeffs=True)
+    assert_forward(out["y"], oracle.kron_forward(xf, th, mix), xf, m * nb)
+
+
+def test_kron_wide_workload_full():
+    """n=11008 = O43 (x) B256 (the LLaMA-2-7B down projection's input), 8192
+    bf16 rows with outliers, sym INT4 g128: all rows."""
+    w = inputs.kron_wide_int4()
+    x = w["x"]
+    out = run_kron_wide(x, w["theta_b"], w["mix"])
+    y64 = oracle.kron_forward(x, w["theta_b"], w["mix"])
+    rf = assert_forward(out["y"], y64, x, 11008)
+    rq = assert_quant(out, y64, 4, 128, 0)
+    print("kron n=11008:", rf, rq)

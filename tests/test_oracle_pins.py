@@ -195,7 +195,7 @@ def test_bf16_input_widening():
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("m,nb", [(3, 8), (5, 16), (1, 32)])
+@pytest.mark.parametrize("m,nb", [(3, 8), (5, 16), (1, 32), (43, 4)])
 def test_kron_equals_numpy_kron(m, nb):
     th = rand_theta(nb)
     mix = inputs.mixing_factor(RNG, m)
