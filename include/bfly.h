@@ -220,6 +220,45 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
 
 size_t bfly_kron_backward_workspace_bytes(int64_t rows, int32_t m, int32_t nb);
 
+/* ---- one calibration step for the angles --------------------------------- */
+
+/* Settings of bfly_calib_step (readings of the pages: they name the loss
+ * terms, not these values). */
+typedef struct {
+    int32_t bits;       /* quantizer of the reconstruction term: symmetric absmax, 2 or 4 */
+    int32_t group;      /* its group size: a power of two in [8, 512] dividing n */
+    int32_t bins;       /* histogram bins of the uniformity term, in [2, 32] */
+    float lambda_kl;    /* weight of the uniformity term */
+    float lr, beta1, beta2, eps;  /* Adam */
+} bfly_calib_config;
+
+/* One step of learning the angles on calibration rows X (device fp32
+ * [rows][n], rows >= 1): Y = Q(theta) X, the loss
+ *   L = sum (y - y^)^2 / N + lambda_kl * KL(p || uniform)
+ * (y^ the group quantizer's value of y, held constant; p the distribution of
+ * u = y / (group max |y|) on `bins` bins over [-1, 1], linear-interpolation
+ * weights, smoothed p' = (p + 1e-6) / (1 + bins 1e-6); the group max held
+ * constant), dL/dtheta through the butterfly backward, then one Adam update
+ * of theta with state adam_m, adam_v (device fp32 [log2 n][n/2], zero before
+ * step 1) and step count `step` (1, 2, ...).  theta, adam_m, adam_v are
+ * updated in place; loss (device fp32 [3]) receives L, the reconstruction
+ * term and KL, all at the angles before the update.  workspace: >=
+ * bfly_calib_workspace_bytes(rows, n) bytes of device scratch, 16-byte
+ * aligned; the call allocates nothing.  n: a power of two in [64, 4096].
+ * Errors: BFLY_ERR_NULL, BFLY_ERR_SIZE, BFLY_ERR_QUANT (bits, group or bins
+ * invalid), BFLY_ERR_WORKSPACE, BFLY_ERR_ALIGN, BFLY_ERR_UNSUPPORTED,
+ * BFLY_ERR_HIP.  Passages: ButterflyQuant write-up, section "training and
+ * results" (reconstruction loss plus a KL-to-uniform regulariser on the
+ * rotated activations) and the ButterflyQuant abstract (uniformity
+ * regularisation; gradient-based learning of the angles on calibration
+ * samples). */
+bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* theta, float* adam_m,
+                            float* adam_v, int32_t step, const bfly_calib_config* cfg,
+                            float* loss, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n);
+
 /* ---- consumer of the quantized weights ---------------------------------- */
 
 /* y[r][o] = sum_k a[r][k] * w[o][k] for r < rows, o < n_out: the layer

@@ -20,7 +20,8 @@ __all__ = [
     "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_kron_forward_wide",
     "bfly_kron_forward_wide_workspace_bytes", "bfly_quant_matmul",
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
-    "bfly_kron_backward_workspace_bytes", "bfly_status_string",
+    "bfly_kron_backward_workspace_bytes", "bfly_calib_config", "bfly_calib_step",
+    "bfly_calib_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error",
 ]
 
@@ -75,6 +76,10 @@ def lib():
         L.bfly_backward.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.bfly_backward_workspace_bytes.argtypes = [i64, i32]
         L.bfly_backward_workspace_bytes.restype = sz
+        L.bfly_calib_step.argtypes = [vp, i64, i32, vp, vp, vp, i32,
+                                      ctypes.POINTER(bfly_calib_config), vp, vp, sz, vp]
+        L.bfly_calib_workspace_bytes.argtypes = [i64, i32]
+        L.bfly_calib_workspace_bytes.restype = sz
         L.bfly_kron_backward.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]
         L.bfly_kron_backward_workspace_bytes.argtypes = [i64, i32, i32]
         L.bfly_kron_backward_workspace_bytes.restype = sz
@@ -84,7 +89,7 @@ def lib():
         for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
                   L.bfly_kron_forward, L.bfly_kron_forward_wide, L.bfly_quant_matmul,
                   L.bfly_backward,
-                  L.bfly_kron_backward):
+                  L.bfly_kron_backward, L.bfly_calib_step):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -93,6 +98,13 @@ def lib():
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
+
+class bfly_calib_config(ctypes.Structure):
+    """Settings of bfly_calib_step (include/bfly.h)."""
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("bins", ctypes.c_int32),
+                ("lambda_kl", ctypes.c_float), ("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
 
 def _ptr(t):
     if t is None:
@@ -235,3 +247,18 @@ def bfly_kron_backward(x, g, dx, dtheta_b, mix, workspace, theta_b=None, coeffs_
                                     _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "bfly_kron_backward")
+
+
+def bfly_calib_workspace_bytes(rows: int, n: int) -> int:
+    return lib().bfly_calib_workspace_bytes(rows, n)
+
+
+def bfly_calib_step(x, theta, adam_m, adam_v, step: int, cfg: bfly_calib_config, loss, workspace,
+                    stream=None) -> None:
+    """One calibration step on rows x ([rows, n] float32): theta, adam_m,
+    adam_v ([log2 n, n/2] float32) updated in place; loss [3] float32."""
+    rows, n = x.shape
+    _check(lib().bfly_calib_step(_ptr(x), rows, n, _ptr(theta), _ptr(adam_m), _ptr(adam_v), step,
+                                 ctypes.byref(cfg), _ptr(loss), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "bfly_calib_step")

@@ -22,7 +22,8 @@ SOURCES = [("bfly_api.hip", "bfly_api.o", []), ("bfly_bwd.hip", "bfly_bwd.o", []
            ("bfly_fwd_plain.hip", "bfly_fwd_plain.o", []),
            ("bfly_qgemm.hip", "bfly_qgemm.o", []),
            ("bfly_kron_bwd.hip", "bfly_kron_bwd.o", []),
-           ("bfly_kron_mix.hip", "bfly_kron_mix.o", [])] + \
+           ("bfly_kron_mix.hip", "bfly_kron_mix.o", []),
+           ("bfly_calib.hip", "bfly_calib.o", [])] + \
           [("bfly_fwd_kron.hip", "bfly_fwd_kron_m%d.o" % m, ["-DKRON_M=%d" % m]) for m in range(2, 9)]
 
 FLAGS = [

@@ -7,6 +7,7 @@
 
 #include "../../include/bfly.h"
 #include "bfly_internal.h"
+#include "bfly_calib.h"
 #include "bfly_qgemm.h"
 
 namespace bfly {
@@ -397,6 +398,79 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   const size_t bwd_bytes = workspace_bytes - o_bwd;
   return bfly_backward(x, dx, nullptr, dx, dtheta_b, rows * m, nb, theta_b, coeffs_b, ws + o_bwd,
                        bwd_bytes, hip_stream);
+}
+
+// Workspace of a calibration step: Y (then dL/dY), dtheta, the histogram
+// partials and log-bins, then the backward's workspace (its table first).
+static size_t calib_parts(int64_t rows, int logn, size_t* o_dth, size_t* o_part, size_t* o_lb,
+                          size_t* o_bwd) {
+  const int64_t n = int64_t(1) << logn;
+  const size_t dth = align_up((size_t)rows * (size_t)n * sizeof(float), 256);
+  const size_t part = align_up(dth + sizeof(float) * (size_t)logn * (size_t)(n / 2), 256);
+  const size_t lb = align_up(part + sizeof(float) * (size_t)bfly::CALIB_MAX_BLOCKS *
+                                        (bfly::CALIB_MAX_BINS + 1), 256);
+  const size_t bwd = align_up(lb + sizeof(float) * bfly::CALIB_MAX_BINS, 256);
+  if (o_dth) *o_dth = dth;
+  if (o_part) *o_part = part;
+  if (o_lb) *o_lb = lb;
+  if (o_bwd) *o_bwd = bwd;
+  return bwd + bfly_backward_workspace_bytes(rows, (int32_t)n);
+}
+
+size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n) {
+  int l = 0;
+  if (rows < 1 || check_n(n, 12, &l) != BFLY_OK) return 0;
+  return calib_parts(rows, l, nullptr, nullptr, nullptr, nullptr);
+}
+
+bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* theta, float* adam_m,
+                            float* adam_v, int32_t step, const bfly_calib_config* cfg,
+                            float* loss, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+  if (!x || !theta || !adam_m || !adam_v || !cfg || !loss || !workspace) return BFLY_ERR_NULL;
+  if (rows < 1 || step < 1) return BFLY_ERR_SIZE;
+  int l = 0;
+  const bfly_status sn = check_n(n, 12, &l);
+  if (sn != BFLY_OK) return sn;
+  const int lg = log2_pow2(cfg->group);
+  if ((cfg->bits != 2 && cfg->bits != 4) || lg < 3 || lg > 9 || cfg->group > n ||
+      cfg->bins < 2 || cfg->bins > bfly::CALIB_MAX_BINS)
+    return BFLY_ERR_QUANT;
+  size_t o_dth = 0, o_part = 0, o_lb = 0, o_bwd = 0;
+  if (workspace_bytes < calib_parts(rows, l, &o_dth, &o_part, &o_lb, &o_bwd))
+    return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(workspace, 16) || !aligned(theta, 4) || !aligned(adam_m, 4) ||
+      !aligned(adam_v, 4) || !aligned(loss, 4))
+    return BFLY_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  float* yg = reinterpret_cast<float*>(ws);
+  float* dth = reinterpret_cast<float*>(ws + o_dth);
+  char* wsb = ws + o_bwd;  // the backward's workspace; its table area holds the table
+  hipError_t e = bfly::launch_prepare(theta, wsb, l, s);
+  if (e != hipSuccess) return hip_fail(e);
+  bfly_status st = bfly_forward(x, BFLY_F32, yg, BFLY_F32, rows, n, nullptr, wsb, hip_stream);
+  if (st != BFLY_OK) return st;
+  bfly::CalibLossParams p;
+  p.y = yg;
+  p.rows = rows;
+  p.n = n;
+  p.group = cfg->group;
+  p.bits = cfg->bits;
+  p.bins = cfg->bins;
+  p.lambda_kl = cfg->lambda_kl;
+  p.partials = reinterpret_cast<float*>(ws + o_part);
+  p.lb = reinterpret_cast<float*>(ws + o_lb);
+  p.loss = loss;
+  if ((e = bfly::launch_calib_hist(p, s)) != hipSuccess) return hip_fail(e);
+  if ((e = bfly::launch_calib_reduce(p, s)) != hipSuccess) return hip_fail(e);
+  if ((e = bfly::launch_calib_grad(p, s)) != hipSuccess) return hip_fail(e);
+  st = bfly_backward(x, yg, nullptr, yg, dth, rows, n, nullptr, wsb, wsb,
+                     workspace_bytes - o_bwd, hip_stream);
+  if (st != BFLY_OK) return st;
+  e = bfly::launch_adam(theta, adam_m, adam_v, dth, l * (n / 2), step, cfg->lr, cfg->beta1,
+                        cfg->beta2, cfg->eps, s);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
 bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* codes,

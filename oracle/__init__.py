@@ -22,6 +22,15 @@ Each function cites the passage of the pages it follows:
   learning the angles): dL/dz = (O^T kron I) G in fp64, then the butterfly
   backward on the rows * m segments.  The C backward reads its G in fp32,
   so dL/dz is rounded to fp32 first (2^-24 relative).
+* calib_loss_grad / adam / calib_step -- one calibration step for the
+  angles (duidaima.com section "training and results": a reconstruction
+  loss plus the KL divergence between the rotated activations' distribution
+  and the uniform one; ButterflyQuant abstract: uniformity regularisation,
+  gradient descent on calibration samples).  numpy, fp64: the quantizer is
+  ``quantize`` above, the histogram is linear interpolation onto bin
+  centres, Adam is the textbook update.  The readings (which quantizer,
+  how the histogram is made differentiable, which quantities are held
+  constant, smoothing, the optimiser) are stated where the functions are.
 * hadamard_matrix / hadamard / kron_hadamard -- the Hadamard special case
   (duidaima.com write-up, section "butterfly": H_n for n = 2^k is a butterfly
   with particular angles; ButterflyQuant abstract: Hadamard entries are +-1,
@@ -302,3 +311,68 @@ def kron_backward(x: np.ndarray, g: np.ndarray, theta_b: np.ndarray, mix: np.nda
     gz = np.einsum("ab,rai->rbi", mix64, g3).reshape(rows * m, nb)
     out = backward(x.reshape(rows * m, nb), gz.astype(np.float32), theta_b, want_y=False)
     return {"dx": out["dx"].reshape(rows, n), "dtheta": out["dtheta"], "dabs": out["dabs"]}
+
+
+CALIB_SMOOTH = 1e-6
+
+
+def _group_absmax(y: np.ndarray, group: int) -> np.ndarray:
+    rows, n = y.shape
+    a = np.abs(y).reshape(rows, n // group, group).max(axis=2)
+    return np.repeat(a, group, axis=1)
+
+
+def calib_loss_grad(y: np.ndarray, bits: int, group: int, bins: int, lambda_kl: float):
+    """Loss and dL/dy of one calibration step at Y (fp64 [rows][n]).
+
+    Readings: the reconstruction term is the group quantizer's error,
+    L_rec = sum (y - y^)^2 / N with y^ = dequantized symmetric absmax RTN
+    codes (held constant: no gradient through the rounding or the scale);
+    the uniformity term is KL(p' || uniform) with p the distribution of
+    u = y / a (a = the group's max |y|, held constant) on `bins` centres
+    c_b = -1 + (b + 1/2) h, h = 2 / bins, each u giving linear-interpolation
+    weights to its two nearest centres (u clamped to [c_0, c_{bins-1}];
+    a clamped u has no gradient), p' = (p + 1e-6) / (1 + bins 1e-6).
+    Returns dict(loss, rec, kl, g, t) with t = (u - c_0) / h (unclamped)."""
+    y = np.asarray(y, dtype=np.float64)
+    N = y.size
+    q = quantize(y, bits, group, SYM)
+    yhat = dequantize(q["codes"], q["scales"], None, bits, group, SYM, y.shape[1])
+    rec = float(((y - yhat) ** 2).sum() / N)
+    a = _group_absmax(y, group)
+    u = np.divide(y, a, out=np.zeros_like(y), where=a > 0)
+    h = 2.0 / bins
+    t = (u + 1.0) / h - 0.5
+    inside = (t >= 0) & (t <= bins - 1)
+    tc = np.clip(t, 0, bins - 1)
+    j = np.minimum(np.floor(tc).astype(np.int64), bins - 2)
+    f = tc - j
+    p = (np.bincount(j.ravel(), weights=(1 - f).ravel(), minlength=bins) +
+         np.bincount((j + 1).ravel(), weights=f.ravel(), minlength=bins)) / N
+    ps = (p + CALIB_SMOOTH) / (1 + bins * CALIB_SMOOTH)
+    lb = np.log(bins * ps)
+    kl = float((ps * lb).sum())
+    g = 2.0 * (y - yhat) / N
+    dkl = (lb[j + 1] - lb[j]) / (h * N * (1 + bins * CALIB_SMOOTH))
+    g += lambda_kl * np.where(inside & (a > 0), dkl / np.where(a > 0, a, 1.0), 0.0)
+    return {"loss": rec + lambda_kl * kl, "rec": rec, "kl": kl, "g": g, "t": t, "p": p,
+            "yhat": yhat, "a": a}
+
+
+def adam(theta, m, v, g, step: int, lr: float, beta1: float, beta2: float, eps: float):
+    """The textbook Adam update (bias-corrected moments), fp64."""
+    m = beta1 * np.asarray(m, np.float64) + (1 - beta1) * g
+    v = beta2 * np.asarray(v, np.float64) + (1 - beta2) * g * g
+    mh = m / (1 - beta1 ** step)
+    vh = v / (1 - beta2 ** step)
+    return np.asarray(theta, np.float64) - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+def calib_step(x, theta, m, v, step, bits, group, bins, lambda_kl, lr, beta1, beta2, eps):
+    """One calibration step: Y = Q X (fp64), loss and dL/dY, dtheta by the
+    butterfly backward (its G read in fp32), one Adam update."""
+    y = forward(x, theta)
+    lg = calib_loss_grad(y, bits, group, bins, lambda_kl)
+    bw = backward(x, lg["g"].astype(np.float32), theta, want_y=False, want_dx=False)
+    th2, m2, v2 = adam(theta, m, v, bw["dtheta"], step, lr, beta1, beta2, eps)
+    return dict(lg, y=y, dtheta=bw["dtheta"], dabs=bw["dabs"], theta=th2, m=m2, v=v2)

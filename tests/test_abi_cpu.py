@@ -257,3 +257,27 @@ def test_kron_forward_wide_validation(L):
     assert kw(L, group=512) == QUANT                   # group must divide nb
     assert kw(L, wsb=16 * 11008 * 4 - 1) == WORKSPACE
     assert kw(L, ws=ctypes.c_void_p(0x80008)) == ALIGN
+
+
+def test_calib_step_validation(L):
+    cfg = B.bfly_calib_config(4, 128, 16, 0.1, 1e-3, 0.9, 0.999, 1e-8)
+    wsb = B.bfly_calib_workspace_bytes(64, 4096)
+    assert wsb > 64 * 4096 * 4 + B.bfly_backward_workspace_bytes(64, 4096)
+    assert B.bfly_calib_workspace_bytes(0, 4096) == 0
+    assert B.bfly_calib_workspace_bytes(64, 8192) == 0
+
+    def cs(x=X, rows=64, n=4096, th=TH, m=C, v=S, step=1, c=cfg, loss=Z, ws=WS, wsb=wsb):
+        return L.bfly_calib_step(x, rows, n, th, m, v, step, ctypes.byref(c) if c else None, loss,
+                                 ws, wsb, None)
+    assert cs(x=None) == NULL
+    assert cs(c=None) == NULL
+    assert cs(loss=None) == NULL
+    assert cs(rows=0) == SIZE
+    assert cs(step=0) == SIZE
+    assert cs(n=100) == SIZE
+    assert cs(n=8192) == UNSUPPORTED
+    assert cs(c=B.bfly_calib_config(3, 128, 16, 0.1, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cs(c=B.bfly_calib_config(4, 96, 16, 0.1, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cs(c=B.bfly_calib_config(4, 128, 33, 0.1, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cs(wsb=wsb - 1) == WORKSPACE
+    assert cs(ws=ctypes.c_void_p(0x80008)) == ALIGN

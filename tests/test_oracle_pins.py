@@ -613,3 +613,85 @@ def test_kron_backward_finite_differences_and_dense_transpose():
                 return (loss(tp) - loss(tm)) / (float(tp[s, p]) - float(tm[s, p]))
             rich = (4 * fd(2.0 ** -8) - fd(2.0 ** -7)) / 3
             assert abs(rich - out["dtheta"][s, p]) < 1e-5 * (1 + abs(rich)), (s, p)
+
+
+# --- one calibration step
+
+def test_calib_grad_matches_finite_differences():
+    """dL/dy against central differences of L with the held-constant
+    quantities (y^ and the group max) frozen: checks both terms' formulas."""
+    rng = np.random.default_rng(80)
+    rows, n, group, bins, lam = 3, 64, 16, 8, 0.7
+    y = rng.standard_normal((rows, n))
+    out = oracle.calib_loss_grad(y, 4, group, bins, lam)
+    yhat, a, N = out["yhat"], out["a"], y.size
+    h = 2.0 / bins
+
+    def loss(yy):
+        u = yy / a
+        t = np.clip((u + 1.0) / h - 0.5, 0, bins - 1)
+        j = np.minimum(np.floor(t).astype(np.int64), bins - 2)
+        f = t - j
+        p = (np.bincount(j.ravel(), weights=(1 - f).ravel(), minlength=bins) +
+             np.bincount((j + 1).ravel(), weights=f.ravel(), minlength=bins)) / N
+        ps = (p + oracle.CALIB_SMOOTH) / (1 + bins * oracle.CALIB_SMOOTH)
+        return ((yy - yhat) ** 2).sum() / N + lam * (ps * np.log(bins * ps)).sum()
+
+    tt = out["t"]
+    checked = 0
+    for r in range(rows):
+        for i in range(n):
+            ti = tt[r, i]
+            if not (0.02 < ti < bins - 1.02) or abs(ti - round(ti)) < 0.02 or abs(y[r, i]) == a[r, i]:
+                continue
+            eps = 1e-6 * a[r, i]
+            yp, ym = y.copy(), y.copy()
+            yp[r, i] += eps
+            ym[r, i] -= eps
+            fd = (loss(yp) - loss(ym)) / (2 * eps)
+            assert abs(fd - out["g"][r, i]) < 1e-6 * (abs(fd) + 1e-3), (r, i, fd, out["g"][r, i])
+            checked += 1
+    assert checked > 100
+    assert abs(loss(y) - out["loss"]) < 1e-12
+
+
+def test_calib_kl_bounds_and_uniform_data():
+    rng = np.random.default_rng(81)
+    bins = 16
+    g = oracle.calib_loss_grad(rng.standard_normal((64, 256)), 4, 128, bins, 0.1)
+    u = oracle.calib_loss_grad(rng.uniform(-1, 1, (64, 256)), 4, 128, bins, 0.1)
+    for o in (g, u):
+        assert 0 <= o["kl"] <= math.log(bins)
+        assert abs(o["p"].sum() - 1) < 1e-12
+    assert u["kl"] < 0.01 < g["kl"]   # uniform activations are nearly uniform already
+    # all mass on one centre: KL = log(bins) up to the smoothing
+    y = np.zeros((1, 128))
+    y[0, 0] = 1.0  # sets the group max; the other 127 values sit at u = 0
+    one = oracle.calib_loss_grad(y, 4, 128, 2, 0.1)   # two bins: u = 0 splits evenly
+    assert abs(one["p"][0] - one["p"][1]) < 1 / 128 + 1e-12
+
+
+def test_adam_first_step_closed_form():
+    rng = np.random.default_rng(82)
+    th, gr = rng.standard_normal(50), rng.standard_normal(50)
+    z = np.zeros(50)
+    t1, m1, v1 = oracle.adam(th, z, z, gr, 1, 1e-3, 0.9, 0.999, 1e-8)
+    assert np.allclose(t1, th - 1e-3 * gr / (np.abs(gr) + 1e-8), rtol=0, atol=1e-15)
+    assert np.allclose(m1, 0.1 * gr) and np.allclose(v1, 0.001 * gr * gr)
+
+
+def test_calib_step_reduces_the_loss():
+    """A few oracle steps on a small layer lower the loss (the method's
+    premise; not a bound)."""
+    rng = np.random.default_rng(83)
+    n = 64
+    th = rand_theta(n, rng) * 0.1
+    x = rng.standard_normal((64, n)).astype(np.float32)
+    x[:, 3] *= 20.0                       # an outlier channel
+    m = v = np.zeros_like(th, dtype=np.float64)
+    first = None
+    for step in range(1, 31):
+        o = oracle.calib_step(x, th, m, v, step, 4, 16, 16, 0.05, 0.02, 0.9, 0.999, 1e-8)
+        first = o["loss"] if first is None else first
+        th, m, v = o["theta"].astype(np.float32), o["m"], o["v"]
+    assert o["loss"] < 0.9 * first
