@@ -22,7 +22,7 @@ counters recorded for the current kernel sources (null if they changed).
 --workload picks one of the other parity workloads for a secondary line
 (tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
 calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
-kron_bwd_n5120_fp32, kron_n11008_bf16_int4); --copy-probe runs a plain device copy of known
+kron_bwd_n5120_fp32, kron_n11008_bf16_int4, calib_step_n4096_fp32); --copy-probe runs a plain device copy of known
 size (for calibrating the byte counters).
 """
 from __future__ import annotations
@@ -392,6 +392,23 @@ def bench_secondary(args, torch, B, inputs):
                       args.steps, args.warmup)
         b = rows * m * nb * 12  # x and G read, dX written once
         res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t)
+    elif name == "calib_step_n4096_fp32":
+        # One calibration step (loss, dL/dY, backward, Adam) on the 262144
+        # calibration rows of n = 4096 (128 samples x 2048 tokens).
+        c = inputs.CalibFP32()
+        X = torch.empty((c.rows, c.n), device="cuda")
+        for r0, xb, _ in c.blocks(threads=16):
+            X[r0:r0 + xb.shape[0]].copy_(torch.from_numpy(xb))
+        th = to_dev(c.theta, torch)
+        m, v = torch.zeros_like(th), torch.zeros_like(th)
+        loss = torch.zeros(3, device="cuda")
+        ws = torch.empty(B.bfly_calib_workspace_bytes(c.rows, c.n), dtype=torch.uint8, device="cuda")
+        cfg = B.bfly_calib_config(4, 128, 16, 0.05, 1e-3, 0.9, 0.999, 1e-8)
+        t = time_loop(torch, lambda i: B.bfly_calib_step(X, th, m, v, i + 1, cfg, loss, ws),
+                      args.steps, args.warmup)
+        passes = c.rows * c.n * 4 * 8  # fwd 2, histogram 1, gradient 2, backward 3 tensor passes
+        res.update(us_per_step=t * 1e6, rows_per_s=c.rows / t, bytes_moved=passes,
+                   GBs_moved=passes / t / 1e9, loss=[float(z) for z in loss.cpu()])
     elif name == "calib_n4096_fp32_fwd_bwd":
         c = inputs.CalibFP32()
         X = torch.empty((c.rows, c.n), device="cuda")
