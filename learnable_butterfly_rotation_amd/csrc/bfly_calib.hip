@@ -74,8 +74,10 @@ __device__ __forceinline__ void bin_of(float u, int bins, int& j, float& f, bool
 }
 
 __global__ __launch_bounds__(CALIB_THREADS) void calib_hist_kernel(const CalibLossParams P) {
-  __shared__ float lh[CALIB_MAX_BINS * CALIB_THREADS];  // lane-private bins, bin-major
-  __shared__ float red[CALIB_THREADS];
+  // lane-private bins, bin-major ([bins][256]), sized to `bins` so that more
+  // workgroups fit on a CU; then the lanes' squared errors
+  extern __shared__ float lh[];
+  float* red = lh + P.bins * CALIB_THREADS;
   const int t = threadIdx.x, bins = P.bins;
   for (int b = 0; b < bins; ++b) lh[b * CALIB_THREADS + t] = 0.f;
   const int gt = P.group / CALIB_EPT;
@@ -83,9 +85,26 @@ __global__ __launch_bounds__(CALIB_THREADS) void calib_hist_kernel(const CalibLo
   const int64_t nchunks = P.rows * P.n / CALIB_EPT;
   const int64_t stride = (int64_t)gridDim.x * CALIB_THREADS;
   float sse = 0.f;
-  for (int64_t c = (int64_t)blockIdx.x * CALIB_THREADS + t; c < nchunks; c += stride) {
+  int64_t c = (int64_t)blockIdx.x * CALIB_THREADS + t;
+  // the next chunk's values are loaded before this one's bins are updated
+  float4 n0 = make_float4(0.f, 0.f, 0.f, 0.f), n1 = n0;
+  if (c < nchunks) {
+    n0 = *reinterpret_cast<const float4*>(P.y + c * CALIB_EPT);
+    n1 = *reinterpret_cast<const float4*>(P.y + c * CALIB_EPT + 4);
+  }
+  for (; c < nchunks; c += stride) {
     Elt e;
-    load_chunk(P.y, c, gt, qmax, e);
+    e.y[0] = n0.x; e.y[1] = n0.y; e.y[2] = n0.z; e.y[3] = n0.w;
+    e.y[4] = n1.x; e.y[5] = n1.y; e.y[6] = n1.z; e.y[7] = n1.w;
+    if (c + stride < nchunks) {
+      n0 = *reinterpret_cast<const float4*>(P.y + (c + stride) * CALIB_EPT);
+      n1 = *reinterpret_cast<const float4*>(P.y + (c + stride) * CALIB_EPT + 4);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < CALIB_EPT; ++k) m = fmaxf(m, fabsf(e.y[k]));
+    e.a = group_absmax(m, gt);
+    e.s = fp16_rne(e.a / qmax);
     const float inv_a = e.a > 0.f ? 1.f / e.a : 0.f;
 #pragma unroll
     for (int k = 0; k < CALIB_EPT; ++k) {
@@ -214,8 +233,9 @@ int calib_blocks(int64_t rows, int n) {
 }
 
 hipError_t launch_calib_hist(const CalibLossParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(calib_hist_kernel, dim3(calib_blocks(p.rows, p.n)), dim3(CALIB_THREADS), 0, s,
-                     p);
+  const size_t lds = sizeof(float) * (size_t)(p.bins + 1) * CALIB_THREADS;
+  hipLaunchKernelGGL(calib_hist_kernel, dim3(calib_blocks(p.rows, p.n)), dim3(CALIB_THREADS), lds,
+                     s, p);
   return hipGetLastError();
 }
 
