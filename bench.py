@@ -22,7 +22,8 @@ counters recorded for the current kernel sources (null if they changed).
 --workload picks one of the other parity workloads for a secondary line
 (tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
 calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
-kron_bwd_n5120_fp32, kron_n11008_bf16_int4, calib_step_n4096_fp32); --copy-probe runs a plain device copy of known
+kron_bwd_n5120_fp32, kron_n11008_bf16_int4, calib_step_n4096_fp32,
+w2a16_m1_k4096_n11008, w2a16_m16_k4096_n11008); --copy-probe runs a plain device copy of known
 size (for calibrating the byte counters).
 """
 from __future__ import annotations
@@ -375,6 +376,47 @@ def bench_secondary(args, torch, B, inputs):
         b = rows * (2 * n + 2 * n + n // 2 + 2 * (n // 128))
         res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t,
                    fp32_intermediate_bytes=rows * n * 8)
+    elif name in ("w2a16_m1_k4096_n11008", "w2a16_m16_k4096_n11008"):
+        # Decode-time W2A16: 1 or 16 activation rows against the 11008 x 4096
+        # asym INT2 g128 weight (rotated and quantized by the library): the
+        # product is bound by reading the codes, scales and zero points once.
+        rows = 1 if name == "w2a16_m1_k4096_n11008" else 16
+        ww = inputs.weight_int2()
+        k, n_out = 4096, ww["w2"].shape[0]
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        a = torch.randn((rows, k), device="cuda", generator=gen).to(torch.bfloat16)
+        w2 = to_dev(ww["w2"], torch)
+        sets = []  # 16 weight copies (210 MB): no launch finds its codes in cache
+        codes = torch.empty((n_out, k // 4), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n_out, k // 128), dtype=torch.float16, device="cuda")
+        zr = torch.empty_like(sc)
+        B.bfly_forward_quant(w2, None, codes, sc, zr, theta=to_dev(ww["theta"], torch), bits=2,
+                             group=128, mode=B.BFLY_ASYM_MINMAX)
+        for _ in range(16):
+            sets.append((codes.clone(), sc.clone(), zr.clone()))
+        del w2
+        y = torch.empty((rows, n_out), dtype=torch.bfloat16, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def fn(i, ev=None):
+            c, s_, z = sets[i % 16]
+            if ev is not None:
+                ev[0].record(stream)
+            B.bfly_quant_matmul(a, c, s_, z, y, bits=2, group=128, mode=B.BFLY_ASYM_MINMAX)
+            if ev is not None:
+                ev[1].record(stream)
+        warm_up(torch, fn, args.warmup)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i, evs[i])
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / args.steps
+        kern_s = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) / 1e3
+        hbm = codes.numel() + 4 * sc.numel() + rows * k * 2 + rows * n_out * 2
+        res.update(us_per_step=t * 1e6, kernel_median_us=kern_s * 1e6, hbm_bytes=hbm,
+                   GBs=hbm / kern_s / 1e9, flops=2.0 * rows * k * n_out)
     elif name == "kron_bwd_n5120_fp32":
         # Gradients of the composite O5 (x) B1024 on 32768 fp32 rows (x, G
         # drawn on the GPU from a seeded generator): dX and dtheta_b.

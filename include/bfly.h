@@ -278,8 +278,9 @@ size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n);
  *            nearest even from fp32), 16-byte aligned; must not overlap
  *            the inputs
  *   w[o][k] = scale * q (symmetric) or scale * (q - zero) (asymmetric).
- * Arithmetic: each group's sum of a * (q - zero) in fp32 (exact products),
- * then times the group's scale and added in fp32.
+ * Arithmetic: sums of a * (q - zero) in fp32 (exact products) over one
+ * group (or over 16 codes when rows <= 64), each times its group's scale
+ * and added in fp32.
  * Sizes: bits 2 or 4; k a multiple of 64 in [64, 65536]; group one of 64,
  * 128, 256, 512 dividing k; n_out a positive multiple of 128 with
  * n_out <= 1048576.  rows == 0 is a no-op.  Errors: BFLY_ERR_NULL,

@@ -22,6 +22,9 @@ struct QgemmParams {
 // Tile sizes the launch requires: n_out % QG_BN == 0, k % QG_BK == 0,
 // group % QG_BK == 0.
 constexpr int QG_BM = 256, QG_BN = 128, QG_BK = 64;
+// At most this many rows take the matrix-vector kernel (one wave per four
+// weight rows, dot products on the vector unit) instead of the MFMA tiles.
+constexpr int QG_GEMV_ROWS = 64;
 
 hipError_t launch_qgemm(const QgemmParams& p, hipStream_t s);
 

@@ -287,8 +287,144 @@ __global__ __launch_bounds__(QTile<BM>::THREADS, BM == 128 ? 2 : 1) void qgemm_k
       }
 }
 
+// Few rows (decode time: one to a few dozen tokens): the product is bound by
+// reading and decoding the codes once, and MFMA tiles of 256 rows would be
+// mostly padding.  One wave per QV_OPW weight rows; lane l takes QV_KU
+// consecutive codes per step (k = QV_KU l + 64 QV_KU i, inside one group:
+// group >= 64); with QV_KU = 64 a row of 4096 codes is one step with every
+// load in flight at once.  The codes are decoded to
+// exact bf16 pairs as above; for each of the MR activation rows the 64-term
+// sum is formed with v_dot2c_f32_bf16 (exact products), scaled by the
+// group's scale and accumulated in fp32.  The 64 lanes' sums are then added
+// by an xor-shuffle tree (fixed order) and lane m * QV_OPW + r stores y[m][r].
+constexpr int QV_OPW = 4;   // weight rows per wave
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int BITS, bool ASYM, bool YBF16, int MR, int QV_KU>
+__global__ __launch_bounds__(256) void qgemv_kernel(const QgemmParams P) {
+  static_assert(MR * QV_OPW <= 64, "one lane per output");
+  constexpr int NW = QV_KU * BITS / 32;  // code words per lane per row and step
+  const int lane = threadIdx.x & 63;
+  const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * QV_OPW;  // n_out % 16 == 0
+  const int K = P.k, G = P.group, N = P.n_out, NG = K / G;
+  const int KB = K * BITS / 8;
+  const int64_t m0 = (int64_t)blockIdx.y * MR;
+  const int mrows = group_rows(P.rows, blockIdx.y, MR);
+  const auto ra = buffer_range32(P.a + m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
+  const auto rc = buffer_range32(P.codes + (int64_t)o0 * KB, (uint32_t)(QV_OPW * KB));
+  const auto rs = buffer_range32(P.scales + (int64_t)o0 * NG, (uint32_t)(QV_OPW * NG * 2));
+  const auto rz = buffer_range32(ASYM ? P.zeros + (int64_t)o0 * NG : P.scales,
+                                 ASYM ? (uint32_t)(QV_OPW * NG * 2) : 0u);
+  float acc[MR][QV_OPW];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < QV_OPW; ++r) acc[m][r] = 0.f;
+  for (int k0 = lane * QV_KU; k0 < K; k0 += 64 * QV_KU) {
+    const int g = k0 / G;
+    uint32_t cw[QV_OPW][NW];
+    uint16_t sb[QV_OPW], zb[QV_OPW];
+#pragma unroll
+    for (int r = 0; r < QV_OPW; ++r) {
+      const uint32_t off = (uint32_t)(r * KB + k0 * BITS / 8);
+      if (NW == 1) {
+        cw[r][0] = buf_ld4(rc, off);
+      } else if (NW == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)off, 0, 0);
+        cw[r][0] = v.x;
+        cw[r][NW - 1] = v.y;
+      } else {
+#pragma unroll
+        for (int h = 0; h < NW / 4; ++h) {
+          const uint4 v = buf_ld16(rc, off + 16 * h);
+          cw[r][4 * h] = v.x;
+          cw[r][(4 * h + 1) % NW] = v.y;
+          cw[r][(4 * h + 2) % NW] = v.z;
+          cw[r][(4 * h + 3) % NW] = v.w;
+        }
+      }
+      const uint32_t so = (uint32_t)((r * NG + g) * 2);
+      sb[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+      zb[r] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(rz, (int)so, 0, 0) : (uint16_t)0;
+    }
+    // one weight row at a time (its 32 decoded words), against every
+    // activation row (re-read from the cache for each weight row)
+#pragma unroll
+    for (int r = 0; r < QV_OPW; ++r) {
+      const float z = ASYM ? half_to_float(zb[r]) : (float)(1 << (BITS - 1));
+      uint32_t w[QV_KU / 2];
+#pragma unroll
+      for (int u = 0; u < QV_KU / 16; ++u) {
+        uint32_t x[BITS / 2];
+#pragma unroll
+        for (int h = 0; h < BITS / 2; ++h) {
+          const uint32_t v = cw[r][u * (BITS / 2) + h];
+          x[h] = ASYM ? v : v ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
+        }
+        uint32_t wu[8];
+        decode16<BITS>(x, z, wu);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[8 * u + i] = wu[i];
+      }
+      const float sr = half_to_float(sb[r]);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const uint32_t ao = (uint32_t)(m * K + k0) * 2u;
+        float part = 0.f;
+#pragma unroll
+        for (int q = 0; q < QV_KU / 8; ++q) {
+          const uint4 v = buf_ld16(ra, ao + 16 * q);
+          const uint32_t av[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[i]),
+                                                   __builtin_bit_cast(bf16x2_t, w[4 * q + i]),
+                                                   part, false);
+        }
+        acc[m][r] = fmaf(sr, part, acc[m][r]);
+      }
+    }
+  }
+  // lane sums, fixed-order tree; every lane ends with every total
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < QV_OPW; ++r) acc[m][r] += __shfl_xor(acc[m][r], off, 64);
+  float mine = 0.f;
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int r = 0; r < QV_OPW; ++r)
+      if (lane == m * QV_OPW + r) mine = acc[m][r];
+  if (lane < MR * QV_OPW) {  // rows past the end fall outside the range
+    constexpr int YSZ = YBF16 ? 2 : 4;
+    const auto ry = buffer_range32(static_cast<char*>(P.y) + m0 * N * YSZ,
+                                   (uint32_t)mrows * (uint32_t)N * YSZ);
+    const uint32_t off = (uint32_t)((lane / QV_OPW) * N + o0 + lane % QV_OPW) * YSZ;
+    if (YBF16) buf_st2(ry, off, (uint16_t)pack_bf16(mine, 0.f));
+    else buf_st4(ry, off, __float_as_uint(mine));
+  }
+}
+
+template <int BITS, bool ASYM, bool YBF16, int MR, int KU>
+hipError_t launch_gemv(const QgemmParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.n_out / (4 * QV_OPW)), (unsigned)((p.rows + MR - 1) / MR));
+  hipLaunchKernelGGL((qgemv_kernel<BITS, ASYM, YBF16, MR, KU>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int BITS, bool ASYM, bool YBF16>
 hipError_t launch_one(const QgemmParams& p, hipStream_t s) {
+  if (p.rows <= QG_GEMV_ROWS) {
+    // one row: 64 codes per lane (a 4096-code row in one step, the decode
+    // dominates); more rows: 16 per lane, the dot products dominate
+    if (p.rows == 1) return launch_gemv<BITS, ASYM, YBF16, 1, 64>(p, s);
+    if (p.rows <= 4) return launch_gemv<BITS, ASYM, YBF16, 4, 16>(p, s);
+    return launch_gemv<BITS, ASYM, YBF16, 16, 16>(p, s);
+  }
   constexpr int BM = QG_BM;
   using T = QTile<BM>;
   const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BM, BITS, ASYM, YBF16>);

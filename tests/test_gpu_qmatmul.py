@@ -3,10 +3,11 @@ against the fp64 oracle: ragged small shapes element by element, and the
 full 8192 x 4096 x 11008 W2A16 product (activations of the headline batch
 against the 11008 x 4096 weight) on sampled rows.
 
-Tolerance (derived from the arithmetic): the kernel sums exact products
-a * (q - zero) over one group in fp32, multiplies by the group's scale and
-adds the groups in fp32, so
-    |y - y64| <= (group + k / group + 2) * 2^-24 * sum_k |a_k| |w_k|
+Tolerance (derived from the arithmetic): the kernels sum exact products
+a * (q - zero) in fp32 -- over one group (MFMA tiles) or over 16 codes
+(the few-row kernel) -- multiply by the group's scale and add the partial
+sums in fp32, so
+    |y - y64| <= (group + k / 16 + 2) * 2^-24 * sum_k |a_k| |w_k|
 for fp32 outputs; bf16 outputs add half a bf16 ulp of the result."""
 import math
 
@@ -76,7 +77,7 @@ def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=N
     w = oracle.dequantize(codes, scales, zeros, bits, group, mode, a.shape[1])
     y64 = a @ w.T
     k = a.shape[1]
-    bound = (group + k // group + 2) * U * (np.abs(a) @ np.abs(w).T)
+    bound = (group + k // 16 + 2) * U * (np.abs(a) @ np.abs(w).T)
     if bf16_out:
         mag = np.maximum(np.abs(got), np.abs(y64))
         e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
@@ -93,7 +94,8 @@ def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=N
 def test_small_shapes(bits, mode, y_dt):
     rng = np.random.default_rng(100 + 10 * bits + mode + (5 if y_dt == "bf16" else 0))
     for rows, n_out, k, group in [(1, 128, 64, 64), (37, 256, 128, 128), (300, 384, 640, 64),
-                                  (257, 128, 1024, 256), (513, 256, 512, 512)]:
+                                  (257, 128, 1024, 256), (513, 256, 512, 512), (4, 384, 2112, 64),
+                                  (16, 128, 1024, 512), (64, 256, 4096, 128), (65, 128, 256, 128)]:
         a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, k)).astype(np.float32) * 3)
         codes, scales, zeros = rand_codes(rng, n_out, k, bits, group, mode)
         got = run(a, codes, scales, zeros, bits, group, mode,
@@ -138,3 +140,15 @@ def test_w2a16_full_size_sampled():
     # a 300-row slice computes the same values (tile placement is row-independent)
     part = run(a[:300], q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, torch.bfloat16)
     assert np.array_equal(part, got[:300])
+
+
+@pytest.mark.parametrize("rows", [1, 16])
+def test_w2a16_decode_full_width(rows):
+    """Few rows (decode time) against the full 11008 x 4096 asym INT2 g128
+    weight, quantized by the oracle: every output."""
+    ww = inputs.weight_int2()
+    q = oracle.quantize(oracle.forward(ww["w2"], ww["theta"]), 2, 128, oracle.ASYM)
+    rng = np.random.default_rng(11 + rows)
+    a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, 4096)).astype(np.float32))
+    got = run(a, q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, torch.bfloat16)
+    check(got, a, q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, True)
