@@ -348,6 +348,54 @@ __global__ __launch_bounds__(256) void qgemv_kernel(const QgemmParams P) {
       sb[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
       zb[r] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(rz, (int)so, 0, 0) : (uint16_t)0;
     }
+    if constexpr (BITS == 2 && MR == 1) {
+      // One activation row, 2-bit codes: decode through a byte permute.  The
+      // four values q - z of the row's group are bf16 entries of an 8-byte
+      // table (exact small integers); codes i and i + 8 of a 16-code word sit
+      // 16 bits apart, so one shift and mask put them in the two halves of
+      // t, t * 0x202 + 0x01000100 is the byte selector of their table
+      // entries, and v_perm_b32 gives the pair (w_i, w_i+8).  The activations
+      // are re-paired the same way once, for all the weight rows.
+      uint32_t pa[QV_KU / 2];
+      {
+        const uint32_t ao = (uint32_t)k0 * 2u;
+#pragma unroll
+        for (int u = 0; u < QV_KU / 16; ++u) {
+          const uint4 v0 = buf_ld16(ra, ao + 32 * u), v1 = buf_ld16(ra, ao + 32 * u + 16);
+          const uint32_t av[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pa[8 * u + i] = __builtin_amdgcn_perm(av[4 + i / 2], av[i / 2],
+                                                  (i & 1) ? 0x07060302u : 0x05040100u);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < QV_OPW; ++r) {
+        uint32_t lut_lo, lut_hi;
+        if (ASYM) {
+          const float z = half_to_float(zb[r]);
+          lut_lo = pack_exact(-z, 1.f - z);
+          lut_hi = pack_exact(2.f - z, 3.f - z);
+        } else {  // two's complement: 0, 1, -2, -1
+          lut_lo = 0x3F800000u;  // (0, 1)
+          lut_hi = 0xBF80C000u;              // (-2, -1)
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < QV_KU / 16; ++u) {
+          const uint32_t x = cw[r][u];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t tq = (x >> (2 * i)) & 0x00030003u;
+            const uint32_t w = __builtin_amdgcn_perm(lut_hi, lut_lo, tq * 0x202u + 0x01000100u);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pa[8 * u + i]),
+                                                   __builtin_bit_cast(bf16x2_t, w), part, false);
+          }
+        }
+        acc[0][r] = fmaf(half_to_float(sb[r]), part, acc[0][r]);
+      }
+      continue;
+    }
     // one weight row at a time (its 32 decoded words), against every
     // activation row (re-read from the cache for each weight row)
 #pragma unroll
