@@ -400,16 +400,19 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
                        bwd_bytes, hip_stream);
 }
 
-// Workspace of a calibration step: Y (then dL/dY), dtheta, the histogram
-// partials and log-bins, then the backward's workspace (its table first).
-static size_t calib_parts(int64_t rows, int logn, size_t* o_dth, size_t* o_part, size_t* o_lb,
-                          size_t* o_bwd) {
+// Workspace of a calibration step: Y, the groups' max |y| (sized for the
+// smallest group, 8), dtheta, the histogram partials and log-bins, then the
+// backward's workspace (its table first).
+static size_t calib_parts(int64_t rows, int logn, size_t* o_amax, size_t* o_dth, size_t* o_part,
+                          size_t* o_lb, size_t* o_bwd) {
   const int64_t n = int64_t(1) << logn;
-  const size_t dth = align_up((size_t)rows * (size_t)n * sizeof(float), 256);
+  const size_t amax = align_up((size_t)rows * (size_t)n * sizeof(float), 256);
+  const size_t dth = align_up(amax + (size_t)rows * (size_t)(n / 8) * sizeof(float), 256);
   const size_t part = align_up(dth + sizeof(float) * (size_t)logn * (size_t)(n / 2), 256);
   const size_t lb = align_up(part + sizeof(float) * (size_t)bfly::CALIB_MAX_BLOCKS *
                                         (bfly::CALIB_MAX_BINS + 1), 256);
   const size_t bwd = align_up(lb + sizeof(float) * bfly::CALIB_MAX_BINS, 256);
+  if (o_amax) *o_amax = amax;
   if (o_dth) *o_dth = dth;
   if (o_part) *o_part = part;
   if (o_lb) *o_lb = lb;
@@ -420,7 +423,7 @@ static size_t calib_parts(int64_t rows, int logn, size_t* o_dth, size_t* o_part,
 size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n) {
   int l = 0;
   if (rows < 1 || check_n(n, 12, &l) != BFLY_OK) return 0;
-  return calib_parts(rows, l, nullptr, nullptr, nullptr, nullptr);
+  return calib_parts(rows, l, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* theta, float* adam_m,
@@ -436,23 +439,27 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
   if ((cfg->bits != 2 && cfg->bits != 4) || lg < 3 || lg > 9 || cfg->group > n ||
       cfg->bins < 2 || cfg->bins > bfly::CALIB_MAX_BINS)
     return BFLY_ERR_QUANT;
-  size_t o_dth = 0, o_part = 0, o_lb = 0, o_bwd = 0;
-  if (workspace_bytes < calib_parts(rows, l, &o_dth, &o_part, &o_lb, &o_bwd))
+  size_t o_amax = 0, o_dth = 0, o_part = 0, o_lb = 0, o_bwd = 0;
+  if (workspace_bytes < calib_parts(rows, l, &o_amax, &o_dth, &o_part, &o_lb, &o_bwd))
     return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(workspace, 16) || !aligned(theta, 4) || !aligned(adam_m, 4) ||
       !aligned(adam_v, 4) || !aligned(loss, 4))
     return BFLY_ERR_ALIGN;
   const hipStream_t s = (hipStream_t)hip_stream;
   char* ws = static_cast<char*>(workspace);
-  float* yg = reinterpret_cast<float*>(ws);
+  float* y = reinterpret_cast<float*>(ws);
+  float* amax = reinterpret_cast<float*>(ws + o_amax);
   float* dth = reinterpret_cast<float*>(ws + o_dth);
+  float* lb = reinterpret_cast<float*>(ws + o_lb);
   char* wsb = ws + o_bwd;  // the backward's workspace; its table area holds the table
   hipError_t e = bfly::launch_prepare(theta, wsb, l, s);
   if (e != hipSuccess) return hip_fail(e);
-  bfly_status st = bfly_forward(x, BFLY_F32, yg, BFLY_F32, rows, n, nullptr, wsb, hip_stream);
+  // Y = Q X for the loss statistics
+  const bfly_status st = bfly_forward(x, BFLY_F32, y, BFLY_F32, rows, n, nullptr, wsb, hip_stream);
   if (st != BFLY_OK) return st;
   bfly::CalibLossParams p;
-  p.y = yg;
+  p.y = y;
+  p.amax = amax;
   p.rows = rows;
   p.n = n;
   p.group = cfg->group;
@@ -460,14 +467,30 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
   p.bins = cfg->bins;
   p.lambda_kl = cfg->lambda_kl;
   p.partials = reinterpret_cast<float*>(ws + o_part);
-  p.lb = reinterpret_cast<float*>(ws + o_lb);
+  p.lb = lb;
   p.loss = loss;
   if ((e = bfly::launch_calib_hist(p, s)) != hipSuccess) return hip_fail(e);
   if ((e = bfly::launch_calib_reduce(p, s)) != hipSuccess) return hip_fail(e);
-  if ((e = bfly::launch_calib_grad(p, s)) != hipSuccess) return hip_fail(e);
-  st = bfly_backward(x, yg, nullptr, yg, dth, rows, n, nullptr, wsb, wsb,
-                     workspace_bytes - o_bwd, hip_stream);
-  if (st != BFLY_OK) return st;
+  // dtheta: the backward forms dL/dY itself from the Y it recomputes
+  const double N = (double)rows * (double)n;
+  bfly::CalibGradArgs c;
+  c.amax = amax;
+  c.lb = lb;
+  c.group = cfg->group;
+  c.bits = cfg->bits;
+  c.bins = cfg->bins;
+  c.two_n = (float)(2.0 / N);
+  c.kl_scale = (float)(cfg->lambda_kl / (N * (1.0 + cfg->bins * (double)bfly::kCalibSmooth))) /
+               (2.f / cfg->bins);
+  bfly::BwdParams bp;
+  memset(&bp, 0, sizeof(bp));
+  bp.x = x;
+  bp.partials = reinterpret_cast<float*>(wsb + align_up(coeff_bytes_l(l), 256));
+  bp.tab = bfly::table_at(wsb, l);
+  bp.rows = rows;
+  bp.logn = l;
+  bp.nblk = bfly::backward_blocks(rows, l);
+  if ((e = bfly::launch_backward_calib(bp, c, dth, s)) != hipSuccess) return hip_fail(e);
   e = bfly::launch_adam(theta, adam_m, adam_v, dth, l * (n / 2), step, cfg->lr, cfg->beta1,
                         cfg->beta2, cfg->eps, s);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);

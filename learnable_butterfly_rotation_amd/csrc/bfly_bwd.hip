@@ -24,6 +24,7 @@
 // order fixed by the slot count alone -- the result is bit-identical from
 // run to run and independent of the device (the slot count depends only on
 // rows and n).
+#include "bfly_calib.h"
 #include "bfly_common.h"
 
 namespace bfly {
@@ -58,8 +59,11 @@ struct BwdShape {
   static constexpr size_t LDS_BYTES = (size_t)NBUF * R * W * sizeof(float);
 };
 
-template <int LOGN>
-__global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
+// CALIB: dL/dY is not read but formed from the recomputed Y (calib_grad,
+// with each group's max |y| loaded like g and the log-bins in LDS), and dX
+// is not stored -- the loss of one calibration step.
+template <int LOGN, bool CALIB>
+__global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, CalibGradArgs C) {
   using S = BwdShape<LOGN>;
   constexpr int LOGE = S::LOGE, E = S::E, T = S::T, N = S::N, R = S::R, L = S::L;
   constexpr int NPH = S::NPH, W = S::W;
@@ -113,14 +117,34 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
   };
   uint4 xc[E / 4];
   uint32_t gc[E];
+  // CALIB: the group max of each element this thread holds in the last
+  // phase's layout (element lay(t, 0, BL) + e 2^BL of its team's row)
+  const int lg_group = CALIB ? 31 - __builtin_clz(C.group) : 0;
+  const int ngr = CALIB ? N >> lg_group : 0;
   auto load = [&](int64_t grp) {
     const auto rx = group_range(P.x, grp);
-    const auto rg = group_range(P.g, grp);
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) xc[c] = buf_ld16(rx, off0 + 16 * c);
+    if (CALIB) {
+      const auto ra = buffer_range32(C.amax + grp * ((int64_t)R * ngr),
+                                     (uint32_t)group_rows(rows, grp, R) * (uint32_t)(ngr * 4));
+      const int el0 = lay<LOGE>(t, 0, BL);
 #pragma unroll
-    for (int e = 0; e < E; ++e) gc[e] = buf_ld4(rg, offl + ((uint32_t)e << BL) * 4);
+      for (int e = 0; e < E; ++e)
+        gc[e] = buf_ld4(ra, (uint32_t)(team * ngr + ((el0 + (e << BL)) >> lg_group)) * 4);
+    } else {
+      const auto rg = group_range(P.g, grp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) gc[e] = buf_ld4(rg, offl + ((uint32_t)e << BL) * 4);
+    }
   };
+  __shared__ float lbs[CALIB ? CALIB_MAX_BINS : 1];
+  if (CALIB) {
+    if (tid < C.bins) lbs[tid] = C.lb[tid];
+    __syncthreads();
+  }
+  const float qmax = CALIB ? (float)((1 << (C.bits - 1)) - 1) : 0.f;
+  const float inv_qmax = CALIB ? 1.f / qmax : 0.f;
 
   load(blockIdx.x);
   for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
@@ -175,6 +199,11 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
 #pragma unroll
       for (int e = 0; e < E; ++e) buf_st4(ry, offl + ((uint32_t)e << BL) * 4, __float_as_uint(v[e]));
     }
+    if (CALIB) {  // g held the group maxima: dL/dy from y (= v) and them
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        g[e] = calib_grad(v[e], g[e], qmax, inv_qmax, C.bins, lbs, C.two_n, C.kl_scale);
+    }
 
     // reverse sweep: for each stage from the last, accumulate the angle
     // gradient, then undo the stage on v and apply its transpose to g
@@ -220,11 +249,14 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P) {
         }
       }
     }
-    const auto rd = group_range(P.dx, grp);
+    if (!CALIB) {
+      const auto rd = group_range(P.dx, grp);
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c)
-      buf_st16(rd, off0 + 16 * c, make_uint4(__float_as_uint(g[4 * c]), __float_as_uint(g[4 * c + 1]),
-                                             __float_as_uint(g[4 * c + 2]), __float_as_uint(g[4 * c + 3])));
+      for (int c = 0; c < E / 4; ++c)
+        buf_st16(rd, off0 + 16 * c,
+                 make_uint4(__float_as_uint(g[4 * c]), __float_as_uint(g[4 * c + 1]),
+                            __float_as_uint(g[4 * c + 2]), __float_as_uint(g[4 * c + 3])));
+    }
   }
 
   float* part = P.partials + ((int64_t)blockIdx.x * R + team) * (L * (N / 2));
@@ -462,13 +494,15 @@ int backward_blocks(int64_t rows, int logn) {
   return (int)(ngrp < cap ? (ngrp > 0 ? ngrp : 1) : cap);
 }
 
-template <int LOGN>
-static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t s) {
+template <int LOGN, bool CALIB = false>
+static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t s,
+                                  const CalibGradArgs& c = CalibGradArgs{}) {
   using S = BwdShape<LOGN>;
-  static hipError_t lds_ok = allow_lds(reinterpret_cast<const void*>(bwd_kernel<LOGN>), S::LDS_BYTES);
+  static hipError_t lds_ok =
+      allow_lds(reinterpret_cast<const void*>(bwd_kernel<LOGN, CALIB>), S::LDS_BYTES);
   if (lds_ok != hipSuccess) return lds_ok;
   if (p.nblk > 0) {
-    hipLaunchKernelGGL(bwd_kernel<LOGN>, dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p);
+    hipLaunchKernelGGL((bwd_kernel<LOGN, CALIB>), dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p, c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -477,6 +511,20 @@ static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((count + RED_COLS - 1) / RED_COLS),
                      dim3(RED_PARTS * RED_COLS), 0, s, p.partials, dtheta, nslots, count);
   return hipGetLastError();
+}
+
+hipError_t launch_backward_calib(const BwdParams& p, const CalibGradArgs& c, float* dtheta,
+                                 hipStream_t s) {
+  switch (p.logn) {
+    case 6: return launch_bwd_inst<6, true>(p, dtheta, s, c);
+    case 7: return launch_bwd_inst<7, true>(p, dtheta, s, c);
+    case 8: return launch_bwd_inst<8, true>(p, dtheta, s, c);
+    case 9: return launch_bwd_inst<9, true>(p, dtheta, s, c);
+    case 10: return launch_bwd_inst<10, true>(p, dtheta, s, c);
+    case 11: return launch_bwd_inst<11, true>(p, dtheta, s, c);
+    case 12: return launch_bwd_inst<12, true>(p, dtheta, s, c);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s) {

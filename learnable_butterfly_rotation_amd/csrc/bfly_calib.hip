@@ -16,16 +16,18 @@
 //   + lambda (lb[j+1] - lb[j]) / (h N (1 + bins 1e-6) a)  (u inside, a > 0),
 // lb[b] = log(bins p'_b), j the lower centre of u.
 //
-// Passes: histogram (per-lane LDS bins, fixed-order block sums), a one-block
-// fixed-order reduction (fp64) to lb and the loss, the gradient (in place of
-// Y).  All reductions run in a fixed order: results repeat bit for bit.
+// Passes: histogram (per-lane LDS bins, fixed-order block sums; it also
+// stores each group's max |y|), a one-block fixed-order reduction (fp64) to
+// lb and the loss; the gradient is then formed inside the butterfly
+// backward from the Y it recomputes (calib_grad), so dL/dY never goes
+// through memory.  All reductions run in a fixed order: results repeat bit
+// for bit.
 #include "bfly_calib.h"
 #include "bfly_common.h"
 
 namespace bfly {
 namespace {
 
-constexpr float kSmooth = 1e-6f;
 
 // Per-group quantities of the thread's 8 elements: gt = group / 8 lanes
 // share a group (gt a power of two <= 64).
@@ -40,38 +42,9 @@ __device__ __forceinline__ float group_absmax(float v, int gt) {
   return v;
 }
 
-__device__ __forceinline__ float fp16_rne(float v) {
-  return (float)(_Float16)fminf(v, 65504.f);
-}
 
-__device__ __forceinline__ void load_chunk(const float* y, int64_t c, int gt, float qmax, Elt& e) {
-  const float4 v0 = *reinterpret_cast<const float4*>(y + c * CALIB_EPT);
-  const float4 v1 = *reinterpret_cast<const float4*>(y + c * CALIB_EPT + 4);
-  e.y[0] = v0.x; e.y[1] = v0.y; e.y[2] = v0.z; e.y[3] = v0.w;
-  e.y[4] = v1.x; e.y[5] = v1.y; e.y[6] = v1.z; e.y[7] = v1.w;
-  float m = 0.f;
-#pragma unroll
-  for (int k = 0; k < CALIB_EPT; ++k) m = fmaxf(m, fabsf(e.y[k]));
-  e.a = group_absmax(m, gt);
-  e.s = fp16_rne(e.a / qmax);
-}
 
-// y^ of one element (symmetric absmax RTN at scale s; s == 0: 0)
-__device__ __forceinline__ float dequant(float y, float s, float qmax) {
-  if (s == 0.f) return 0.f;
-  const float q = fminf(fmaxf(rintf(y / s), -qmax), qmax);
-  return q * s;
-}
 
-// bin coordinate of u: lower centre j, fraction f, inside = not clamped
-__device__ __forceinline__ void bin_of(float u, int bins, int& j, float& f, bool& inside) {
-  const float h = 2.f / bins;
-  float t = (u + 1.f) / h - 0.5f;  // (u - c_0) / h
-  inside = t >= 0.f && t <= (float)(bins - 1);
-  t = fminf(fmaxf(t, 0.f), (float)(bins - 1));
-  j = min((int)t, bins - 2);
-  f = t - (float)j;
-}
 
 __global__ __launch_bounds__(CALIB_THREADS) void calib_hist_kernel(const CalibLossParams P) {
   // lane-private bins, bin-major ([bins][256]), sized to `bins` so that more
@@ -104,16 +77,17 @@ __global__ __launch_bounds__(CALIB_THREADS) void calib_hist_kernel(const CalibLo
 #pragma unroll
     for (int k = 0; k < CALIB_EPT; ++k) m = fmaxf(m, fabsf(e.y[k]));
     e.a = group_absmax(m, gt);
-    e.s = fp16_rne(e.a / qmax);
+    e.s = calib_fp16_rne(e.a / qmax);
+    if ((t & (gt - 1)) == 0) P.amax[c * CALIB_EPT / P.group] = e.a;  // one lane per group
     const float inv_a = e.a > 0.f ? 1.f / e.a : 0.f;
 #pragma unroll
     for (int k = 0; k < CALIB_EPT; ++k) {
-      const float d = e.y[k] - dequant(e.y[k], e.s, qmax);
+      const float d = e.y[k] - calib_dequant(e.y[k], e.s, qmax);
       sse = fmaf(d, d, sse);
       int j;
       float f;
       bool inside;
-      bin_of(e.y[k] * inv_a, bins, j, f, inside);
+      calib_bin(e.y[k] * inv_a, bins, j, f, inside);
       // this lane's own bins, in program order (plain read-modify-write:
       // LDS float atomics measured 7x slower here)
       lh[j * CALIB_THREADS + t] += 1.f - f;
@@ -163,52 +137,19 @@ __global__ __launch_bounds__(CALIB_SLICES*(CALIB_MAX_BINS + 1)) void calib_reduc
   }
   __syncthreads();
   if (t < bins) {
-    const double ps = (p[t] + (double)kSmooth) / (1.0 + bins * (double)kSmooth);
+    const double ps = (p[t] + (double)kCalibSmooth) / (1.0 + bins * (double)kCalibSmooth);
     P.lb[t] = (float)log(bins * ps);
   }
   if (t == 0) {
     double kl = 0.0;
     for (int b = 0; b < bins; ++b) {
-      const double ps = (p[b] + (double)kSmooth) / (1.0 + bins * (double)kSmooth);
+      const double ps = (p[b] + (double)kCalibSmooth) / (1.0 + bins * (double)kCalibSmooth);
       kl += ps * log(bins * ps);
     }
     const double rec = p[bins];  // squared error / N
     P.loss[0] = (float)(rec + P.lambda_kl * kl);
     P.loss[1] = (float)rec;
     P.loss[2] = (float)kl;
-  }
-}
-
-__global__ __launch_bounds__(CALIB_THREADS) void calib_grad_kernel(const CalibLossParams P) {
-  __shared__ float lb[CALIB_MAX_BINS];
-  const int t = threadIdx.x, bins = P.bins;
-  if (t < bins) lb[t] = P.lb[t];
-  __syncthreads();
-  const int gt = P.group / CALIB_EPT;
-  const float qmax = (float)((1 << (P.bits - 1)) - 1);
-  const int64_t nchunks = P.rows * P.n / CALIB_EPT;
-  const int64_t stride = (int64_t)gridDim.x * CALIB_THREADS;
-  const double N = (double)P.rows * (double)P.n;
-  const float two_n = (float)(2.0 / N);
-  const float h = 2.f / bins;
-  const float kl_scale = (float)(P.lambda_kl / (N * (1.0 + bins * (double)kSmooth))) / h;
-  for (int64_t c = (int64_t)blockIdx.x * CALIB_THREADS + t; c < nchunks; c += stride) {
-    Elt e;
-    load_chunk(P.y, c, gt, qmax, e);
-    const float inv_a = e.a > 0.f ? 1.f / e.a : 0.f;
-    float g[CALIB_EPT];
-#pragma unroll
-    for (int k = 0; k < CALIB_EPT; ++k) {
-      g[k] = two_n * (e.y[k] - dequant(e.y[k], e.s, qmax));
-      int j;
-      float f;
-      bool inside;
-      bin_of(e.y[k] * inv_a, bins, j, f, inside);
-      if (inside && e.a > 0.f) g[k] = fmaf(kl_scale * inv_a, lb[j + 1] - lb[j], g[k]);
-    }
-    float* dst = P.y + c * CALIB_EPT;
-    *reinterpret_cast<float4*>(dst) = make_float4(g[0], g[1], g[2], g[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(g[4], g[5], g[6], g[7]);
   }
 }
 
@@ -242,12 +183,6 @@ hipError_t launch_calib_hist(const CalibLossParams& p, hipStream_t s) {
 hipError_t launch_calib_reduce(const CalibLossParams& p, hipStream_t s) {
   hipLaunchKernelGGL(calib_reduce_kernel, dim3(1), dim3(CALIB_SLICES * (CALIB_MAX_BINS + 1)), 0, s,
                      p, calib_blocks(p.rows, p.n));
-  return hipGetLastError();
-}
-
-hipError_t launch_calib_grad(const CalibLossParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(calib_grad_kernel, dim3(calib_blocks(p.rows, p.n)), dim3(CALIB_THREADS), 0, s,
-                     p);
   return hipGetLastError();
 }
 
