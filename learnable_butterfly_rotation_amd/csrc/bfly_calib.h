@@ -39,8 +39,8 @@ __device__ __forceinline__ float calib_dequant(float y, float s, float qmax) {
 
 // lower centre j, fraction f, inside = not clamped
 __device__ __forceinline__ void calib_bin(float u, int bins, int& j, float& f, bool& inside) {
-  const float h = 2.f / bins;
-  float t = (u + 1.f) / h - 0.5f;  // (u - c_0) / h
+  const float hb = 0.5f * (float)bins;  // 1 / h (exact for a power-of-two bin count)
+  float t = fmaf(u, hb, hb - 0.5f);     // (u - c_0) / h
   inside = t >= 0.f && t <= (float)(bins - 1);
   t = fminf(fmaxf(t, 0.f), (float)(bins - 1));
   j = min((int)t, bins - 2);

@@ -79,10 +79,13 @@ __global__ __launch_bounds__(CALIB_THREADS) void calib_hist_kernel(const CalibLo
     e.a = group_absmax(m, gt);
     e.s = calib_fp16_rne(e.a / qmax);
     if ((t & (gt - 1)) == 0) P.amax[c * CALIB_EPT / P.group] = e.a;  // one lane per group
-    const float inv_a = e.a > 0.f ? 1.f / e.a : 0.f;
+    // reciprocals instead of divisions: the pass is bound by its vector work
+    const float inv_a = e.a > 0.f ? __builtin_amdgcn_rcpf(e.a) : 0.f;
+    const float inv_s = e.s > 0.f ? __builtin_amdgcn_rcpf(e.s) : 0.f;
 #pragma unroll
     for (int k = 0; k < CALIB_EPT; ++k) {
-      const float d = e.y[k] - calib_dequant(e.y[k], e.s, qmax);
+      const float yq = fminf(fmaxf(rintf(e.y[k] * inv_s), -qmax), qmax) * e.s;
+      const float d = e.y[k] - yq;
       sse = fmaf(d, d, sse);
       int j;
       float f;
