@@ -21,6 +21,15 @@
  *   invariance).  The stage order (s = 0 first), the pairing, the sign of the
  *   rotation and the angle layout are conventions the pages leave open.
  *
+ * Entry points:
+ *   bfly_prepare, bfly_prepare_hadamard          angles (or H_n) -> coefficient table
+ *   bfly_forward, bfly_forward_quant             Q x, fused group quantization
+ *   bfly_kron_forward, bfly_kron_forward_wide    (O kron B) x for n = m * nb
+ *   bfly_backward, bfly_kron_backward            dX and the angle gradients
+ *   bfly_calib_step                              one step of learning the angles
+ *   bfly_quant_matmul                            y = (Q x)(W Q^T)^T from the codes
+ *   bfly_*_bytes, bfly_status_string, bfly_last_hip_error
+ *
  * Conventions common to every call:
  *   - All data pointers are DEVICE pointers owned by the caller, contiguous
  *     row-major with a row stride of n elements (bytes for codes: n*bits/8).
