@@ -13,18 +13,19 @@ timed region; the step cycles through 5 separate input/output buffer sets
 Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step:
 18 496 B per row (8192 in + 8192 out + 2048 codes + 64 scale bytes) plus the
 96 KiB of angles, divided by the mean step time.  `roofline` prices the
-fused kernel alone (HIP events around it, on its stream, every 4th timed
-step) against the
-8 TB/s HBM peak; `traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
-counters recorded for the current kernel sources (null if they changed).
-`cpu_baseline` times the fp64 oracle on the machine's host cores.
+fused kernel alone (HIP events around it, on its stream, every 16th timed
+step) against the 8 TB/s HBM peak; the events also take in the kernel's
+dispatch after the prepare kernel, which the kernel trace does not.
+`traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded
+for the current kernel sources (null if they changed).  `cpu_baseline` times
+the fp64 oracle on the host's cores.
 
---workload picks one of the other parity workloads for a secondary line
-(tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
-calib_n4096_fp32_fwd_bwd, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
-kron_bwd_n5120_fp32, kron_n11008_bf16_int4, calib_step_n4096_fp32,
-w2a16_m1_k4096_n11008, w2a16_m16_k4096_n11008); --copy-probe runs a plain device copy of known
-size (for calibrating the byte counters).
+--workload picks one of the other workloads for a secondary line:
+tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
+kron_n11008_bf16_int4, kron_bwd_n5120_fp32, calib_n4096_fp32_fwd_bwd,
+calib_step_n4096_fp32, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
+w2a16_m1_k4096_n11008, w2a16_m16_k4096_n11008.  --copy-probe runs a plain
+device copy of known size (for calibrating the byte counters).
 """
 from __future__ import annotations
 
