@@ -667,7 +667,7 @@ def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=tor
 
 
 @pytest.mark.parametrize("m,nb", [(43, 256), (9, 512), (16, 1024), (64, 256), (2, 4096),
-                                  (5, 1024)])
+                                  (5, 1024), (16, 4096)])
 def test_kron_wide_shapes(m, nb):
     rng = np.random.default_rng(7000 + 10 * m + nb)
     th = rand_theta(rng, nb)

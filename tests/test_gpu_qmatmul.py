@@ -152,3 +152,15 @@ def test_w2a16_decode_full_width(rows):
     a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, 4096)).astype(np.float32))
     got = run(a, q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, torch.bfloat16)
     check(got, a, q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, True)
+
+
+@pytest.mark.parametrize("rows,bits,mode", [(1, 2, oracle.ASYM), (300, 4, oracle.SYM)])
+def test_longest_k(rows, bits, mode):
+    """k = 65536 (the largest accepted): 1024 chunks through the MFMA tiles,
+    16 steps per lane in the few-row kernel."""
+    rng = np.random.default_rng(21 + rows)
+    k, n_out, group = 65536, 128, 512
+    a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, k)).astype(np.float32))
+    codes, scales, zeros = rand_codes(rng, n_out, k, bits, group, mode)
+    got = run(a, codes, scales, zeros, bits, group, mode, torch.float32)
+    check(got, a, codes, scales, zeros, bits, group, mode, False)
