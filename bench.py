@@ -13,9 +13,9 @@ timed region; the step cycles through 5 separate input/output buffer sets
 Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step:
 18 496 B per row (8192 in + 8192 out + 2048 codes + 64 scale bytes) plus the
 96 KiB of angles, divided by the mean step time.  `roofline` prices the
-fused kernel alone (HIP events around it, on its stream, every 16th timed
-step) against the 8 TB/s HBM peak; the events also take in the kernel's
-dispatch after the prepare kernel, which the kernel trace does not.
+fused kernel alone against the 8 TB/s HBM peak: on every 16th timed step a
+pair of HIP events is attached to its dispatch (bfly_time_next_forward), so
+they time the kernel's own start to end, the span the kernel trace reports.
 `traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded
 for the current kernel sources (null if they changed).  `cpu_baseline` times
 the fp64 oracle on the host's cores.
@@ -163,22 +163,24 @@ def bench_act(args, torch, B, inputs):
     def step(i, ev=None):
         px, py, pc, ps = ptrs[i % NSETS]
         st = lib.bfly_prepare(th_p, n, tab_p, tab_n, sh)
-        if ev is not None:
-            ev[0].record(stream)
+        if ev is not None:  # events on the fused kernel's own dispatch
+            st |= lib.bfly_time_next_forward(ev[0].cuda_event, ev[1].cuda_event)
         st |= lib.bfly_forward_quant(px, B.BFLY_BF16, py, B.BFLY_BF16, pc, ps, None, rows, n,
                                      None, tab_p, bits, group, B.BFLY_SYM_ABSMAX, sh)
-        if ev is not None:
-            ev[1].record(stream)
         if st:
             raise RuntimeError("libbfly call failed with status %d" % st)
 
     warm_s = warm_up(torch, step, args.warmup)
-    # HIP events bracket the fused kernel on every EVENT_EVERY-th timed step
-    # (on its stream): an event pair makes the kernel after it wait for the
-    # timestamp and adds about 4 us to its step, so every 16th step (31
-    # launches of the default 500) keeps that cost off the step rate.
+    # A pair of HIP events is attached to the fused kernel's dispatch on every
+    # EVENT_EVERY-th timed step (bfly_time_next_forward): their timestamps are
+    # the kernel's own start and end on its stream, with no marker packets in
+    # the stream.  Recording each event once beforehand creates it.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
+    for e in evs:
+        if e is not None:
+            e[0].record(stream)
+            e[1].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

@@ -29,6 +29,7 @@
  *   bfly_calib_step                              one step of learning the angles
  *   bfly_quant_matmul                            y = (Q x)(W Q^T)^T from the codes
  *   bfly_*_bytes, bfly_status_string, bfly_last_hip_error
+ *   bfly_time_next_forward                       kernel-only timing of the next forward
  *
  * Conventions common to every call:
  *   - All data pointers are DEVICE pointers owned by the caller, contiguous
@@ -308,6 +309,21 @@ const char* bfly_status_string(bfly_status s);
 
 /* The hipError_t of the last failed HIP call on this thread (0 if none). */
 int32_t bfly_last_hip_error(void);
+
+/* Kernel-only timing of the fused forward kernel (a measurement hook, not
+ * part of the method).  start_event and stop_event are hipEvent_t handles
+ * the caller created (timing enabled) and owns.  The next launch of the
+ * fused forward kernel in this process, by bfly_forward, bfly_forward_quant,
+ * bfly_kron_forward or bfly_kron_forward_wide on any stream, is dispatched
+ * with the two events attached to the dispatch itself, so that
+ * hipEventElapsedTime(start, stop) is that kernel's own start-to-end time
+ * (the span a kernel trace reports), without marker packets on the stream
+ * and the dispatch delay after them.  One-shot: that launch disarms it; a
+ * call that fails validation launches nothing and leaves it armed.  A second
+ * call before the launch replaces the pair; both handles NULL disarms.
+ * Returns BFLY_ERR_NULL if exactly one handle is NULL (nothing changes);
+ * makes no HIP call. */
+bfly_status bfly_time_next_forward(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

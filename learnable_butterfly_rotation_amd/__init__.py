@@ -22,7 +22,7 @@ __all__ = [
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
     "bfly_kron_backward_workspace_bytes", "bfly_calib_config", "bfly_calib_step",
     "bfly_calib_workspace_bytes", "bfly_status_string",
-    "bfly_last_hip_error",
+    "bfly_last_hip_error", "bfly_time_next_forward",
 ]
 
 BFLY_F32 = 0
@@ -86,10 +86,11 @@ def lib():
         L.bfly_status_string.argtypes = [ctypes.c_int]
         L.bfly_status_string.restype = ctypes.c_char_p
         L.bfly_last_hip_error.restype = i32
+        L.bfly_time_next_forward.argtypes = [vp, vp]
         for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
                   L.bfly_kron_forward, L.bfly_kron_forward_wide, L.bfly_quant_matmul,
                   L.bfly_backward,
-                  L.bfly_kron_backward, L.bfly_calib_step):
+                  L.bfly_kron_backward, L.bfly_calib_step, L.bfly_time_next_forward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -231,6 +232,12 @@ def bfly_status_string(status: int) -> str:
 
 def bfly_last_hip_error() -> int:
     return lib().bfly_last_hip_error()
+
+
+def bfly_time_next_forward(start_event: int, stop_event: int) -> None:
+    """Attach two caller-owned hipEvent_t handles (timing enabled) to the
+    next fused forward-kernel dispatch, for kernel-only timing."""
+    _check(lib().bfly_time_next_forward(start_event, stop_event), "bfly_time_next_forward")
 
 
 def bfly_kron_backward_workspace_bytes(rows: int, m: int, nb: int) -> int:

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/bfly.h"
 #include "bfly_internal.h"
 #include "bfly_calib.h"
@@ -42,6 +44,24 @@ hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
     case 8: return launch_forward_kron_m8(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+namespace {
+std::mutex g_events_mu;
+LaunchEvents g_events;  // armed by bfly_time_next_forward, taken by the next forward launch
+}  // namespace
+
+LaunchEvents take_forward_events() {
+  std::lock_guard<std::mutex> lock(g_events_mu);
+  const LaunchEvents ev = g_events;
+  g_events = LaunchEvents{};
+  return ev;
+}
+
+void arm_forward_events(hipEvent_t start, hipEvent_t stop) {
+  std::lock_guard<std::mutex> lock(g_events_mu);
+  g_events.start = start;
+  g_events.stop = stop;
 }
 }  // namespace bfly
 
@@ -143,6 +163,12 @@ bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coe
   if (!aligned(coeffs, 16) || !aligned(theta, 4)) return BFLY_ERR_ALIGN;
   const hipError_t e = bfly::launch_prepare(theta, coeffs, l, (hipStream_t)hip_stream);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+bfly_status bfly_time_next_forward(void* start_event, void* stop_event) {
+  if (!start_event != !stop_event) return BFLY_ERR_NULL;  // both NULL: disarm
+  bfly::arm_forward_events((hipEvent_t)start_event, (hipEvent_t)stop_event);
+  return BFLY_OK;
 }
 
 bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, void* hip_stream) {

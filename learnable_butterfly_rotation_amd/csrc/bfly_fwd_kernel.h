@@ -20,6 +20,8 @@
 // computing.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "bfly_common.h"
 
 namespace bfly {
@@ -925,7 +927,12 @@ hipError_t launch_fwd_variant(const FwdParams& p, hipStream_t stream) {
   const int64_t ngrp = (p.rows + S::ROWS_PER_PASS - 1) / S::ROWS_PER_PASS;
   const int64_t cap = (int64_t)blocks_per_cu * num_cu;
   const int grid = (int)(ngrp < cap ? ngrp : cap);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, p);
+  const LaunchEvents ev = take_forward_events();
+  if (ev.start != nullptr || ev.stop != nullptr)  // timestamps of this dispatch itself
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, ev.start, ev.stop,
+                          0u, p);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

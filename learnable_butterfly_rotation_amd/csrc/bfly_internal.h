@@ -195,6 +195,15 @@ struct BwdParams {
 hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s,
                           bool hadamard = false);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);
+
+// Events attached to the next forward-kernel dispatch (kernel-only timing):
+// returns the pair armed by bfly_time_next_forward and disarms it (both null
+// when nothing is armed).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents take_forward_events();
+void arm_forward_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s);
 
 // Whether a forward instantiation exists for (lognb, m); validation uses it.

@@ -49,6 +49,14 @@ def test_status_strings(L):
     assert B.bfly_last_hip_error() == 0
 
 
+def test_time_next_forward_arming(L):
+    # makes no HIP call: fake handles are armed, then disarmed (both NULL)
+    assert L.bfly_time_next_forward(None, 0x1000) == 1      # BFLY_ERR_NULL
+    assert L.bfly_time_next_forward(0x1000, None) == 1
+    assert L.bfly_time_next_forward(0x1000, 0x2000) == 0
+    assert L.bfly_time_next_forward(None, None) == 0
+
+
 def test_sizes(L):
     # (cos, sin) [L][n/2] + three-shear (p, u) [L-1][n/2] + last stage 4 x [n/2], fp32
     # per pair: (cos, sin) for every stage, two coefficient pairs (scaled and

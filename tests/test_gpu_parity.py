@@ -267,6 +267,39 @@ def test_in_place():
     assert_forward(host(xd), oracle.forward(x, th), x, 1024)
 
 
+def test_timed_forward_launch_is_the_same_kernel():
+    # events attached to the dispatch: same outputs bit for bit, a positive
+    # kernel time, and the arming is consumed by that one launch
+    rng = np.random.default_rng(11)
+    n, rows = 4096, 512
+    th = dev(rand_theta(rng, n))
+    x = dev(inputs.f32_to_bf16_bits(rng.standard_normal((rows, n)).astype(np.float32)))
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare(th, n, tab)
+    outs = []
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for armed in (False, True, False):
+        y = empty((rows, n), torch.bfloat16)
+        codes = torch.zeros((rows, n // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+        if armed:
+            ev[0].record()
+            ev[1].record()
+            torch.cuda.synchronize()
+            B.bfly_time_next_forward(ev[0].cuda_event, ev[1].cuda_event)
+        B.bfly_forward_quant(x, y, codes, scales, coeffs=tab, bits=4, group=128, mode=0)
+        torch.cuda.synchronize()
+        if armed:
+            ms = ev[0].elapsed_time(ev[1])
+            assert 0.0 < ms < 100.0, ms
+        outs.append((host(y), host(codes), host(scales)))
+    assert ev[0].elapsed_time(ev[1]) == ms  # the later launch left the events alone
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    for a, b in zip(outs[0], outs[2]):
+        assert np.array_equal(a, b)
+
+
 def test_zero_angles_identity_bit_exact():
     rng = np.random.default_rng(4)
     x = inputs.f32_to_bf16_bits(rng.standard_normal((20, 512)).astype(np.float32))
