@@ -699,8 +699,11 @@ def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=tor
     return out
 
 
+# m spans every matrix-core tiling of the mixing step (one or two 32-row
+# tiles; one to four 16-deep k steps) and its edges (17, 32, 33, 48, 49).
 @pytest.mark.parametrize("m,nb", [(43, 256), (9, 512), (16, 1024), (64, 256), (2, 4096),
-                                  (5, 1024), (16, 4096)])
+                                  (5, 1024), (16, 4096), (17, 256), (32, 512), (33, 256),
+                                  (48, 256), (49, 512)])
 def test_kron_wide_shapes(m, nb):
     rng = np.random.default_rng(7000 + 10 * m + nb)
     th = rand_theta(rng, nb)
