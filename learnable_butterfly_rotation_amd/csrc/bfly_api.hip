@@ -400,24 +400,14 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   char* ws = static_cast<char*>(workspace);
   float* mix_t = reinterpret_cast<float*>(ws);
   float* theta0 = reinterpret_cast<float*>(ws + o_th0);
-  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, theta0, l * (nb / 2), s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = bfly::launch_prepare(theta0, ws + o_tab, l, s);
+  // O^T into the workspace (the zero-angle and table regions that follow it
+  // are no longer used; the layout keeps the size the query reports)
+  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, theta0, 0, s);
   if (e != hipSuccess) return hip_fail(e);
   if (rows > 0) {
-    // dL/dz = (O^T kron I) G: the forward with the identity butterfly and O^T
-    bfly::FwdParams p;
-    memset(&p, 0, sizeof(p));
-    p.x = g;
-    p.y = dx;
-    p.mix = mix_t;
-    p.rows = rows;
-    p.m = m;
-    p.lognb = l;
-    p.x_bf16 = 0;
-    p.y_kind = bfly::Y_F32;
-    p.tab = bfly::table_at(ws + o_tab, l);
-    e = bfly::launch_forward(p, s);
+    // dL/dz = (O^T kron I) G: the mixing step with O^T (each thread reads all
+    // m segments of its columns before writing them, so dx == g is safe)
+    e = bfly::launch_kron_mix(g, false, dx, mix_t, rows, m, nb, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   // then the butterfly backward on the rows * m segments, in place on dx
