@@ -1,7 +1,7 @@
-// Set-up of the Kronecker backward: the transposed mixing factor and a zero
-// angle set (whose table is the identity butterfly), in the caller's
-// workspace.  The backward itself is composed from the forward and backward
-// kernels: see bfly_kron_backward.
+// Set-up of the Kronecker backward: the transposed mixing factor in the
+// caller's workspace (and, for n_theta > 0, a zero angle set after it).  The
+// backward itself is composed from the mixing kernel and the butterfly
+// backward: see bfly_kron_backward.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
