@@ -92,6 +92,7 @@ def _load():
         lib.bflyref_fp16_value.argtypes = [ctypes.c_uint16]
         lib.bflyref_fp16_value.restype = ctypes.c_double
         lib.bflyref_num_threads.restype = ctypes.c_int
+        lib.bflyref_set_num_threads.argtypes = [ctypes.c_int]
         for f in (lib.bflyref_forward, lib.bflyref_kron_forward, lib.bflyref_quantize,
                   lib.bflyref_backward):
             f.restype = ctypes.c_int
@@ -113,6 +114,11 @@ def _x_dtype(x: np.ndarray) -> int:
 
 def num_threads() -> int:
     return _load().bflyref_num_threads()
+
+
+def set_num_threads(k: int) -> None:
+    """Threads the oracle's parallel loops use from now on."""
+    _load().bflyref_set_num_threads(int(k))
 
 
 def forward(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
@@ -151,23 +157,26 @@ def quantize(y: np.ndarray, bits: int, group: int, mode: int, scales=None, zeros
     Returns a dict with codes (uint8), scales (uint16 fp16 bits), zeros (asym),
     s_pre (fp64 scale before rounding), z_pre (asym) and optionally v (y/scale).
     If ``scales`` (and ``zeros``) are given, the codes are computed at those
-    scales instead of the oracle's own."""
+    scales (and zero points) instead of the oracle's own; with ``scales``
+    alone in asymmetric mode, the zero points are derived at those scales."""
     y = np.ascontiguousarray(y, dtype=np.float64)
     rows, n = y.shape
     ng = n // group
     codes = np.zeros((rows, n * bits // 8), dtype=np.uint8)
     use_given = scales is not None
+    given_zeros = use_given and mode == ASYM and zeros is not None
     sc = np.ascontiguousarray(scales, dtype=np.uint16).copy() if use_given else \
         np.zeros((rows, ng), dtype=np.uint16)
     if mode == ASYM:
-        zr = np.ascontiguousarray(zeros, dtype=np.uint16).copy() if use_given else \
+        zr = np.ascontiguousarray(zeros, dtype=np.uint16).copy() if given_zeros else \
             np.zeros((rows, ng), dtype=np.uint16)
     else:
         zr = None
+    how = 0 if not use_given else (1 if (mode == SYM or given_zeros) else 2)
     s_pre = np.empty((rows, ng), dtype=np.float64)
     z_pre = np.zeros((rows, ng), dtype=np.float64) if mode == ASYM else None
     v = np.empty((rows, n), dtype=np.float64) if want_v else None
-    rc = _load().bflyref_quantize(_ptr(y), rows, n, group, bits, mode, 1 if use_given else 0,
+    rc = _load().bflyref_quantize(_ptr(y), rows, n, group, bits, mode, how,
                                    _ptr(codes), _ptr(sc), _ptr(zr), _ptr(s_pre), _ptr(z_pre),
                                    _ptr(v))
     if rc != 0:

@@ -126,11 +126,13 @@ double bflyref_fp16_value(uint16_t h)
 
 void bflyref_round_bf16(const double* in, uint16_t* out, int64_t count)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t k = 0; k < count; ++k) out[k] = bflyref_bf16_rne(in[k]);
 }
 
 void bflyref_round_fp16(const double* in, uint16_t* out, int64_t count)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t k = 0; k < count; ++k) out[k] = bflyref_fp16_rne(in[k]);
 }
 
@@ -279,15 +281,18 @@ int bflyref_kron_forward(const void* x, int x_dtype, double* y, int64_t rows, in
  *   s_pre  f64 [rows][n/group]    optional: the scale before fp16 rounding
  *   z_pre  f64 [rows][n/group]    optional (asym): -min/scale before rounding
  *   v      f64 [rows][n]          optional: y / scale, the value that is rounded
- * If use_given is non-zero, scales (and zeros) are INPUTS: the codes are
- * computed at those scales (used to re-quantize at another implementation's
- * scale when a scale rounding tie made both neighbours acceptable).
+ * If use_given is 1, scales (and zeros) are INPUTS: the codes are computed
+ * at those scales (used to re-quantize at another implementation's scale
+ * when a scale rounding tie made both neighbours acceptable).  If use_given
+ * is 2, the scales are inputs and the asymmetric zero points are derived at
+ * them (clamp(rne(-min / scale))), as the quantizer would with that scale.
  * Returns 0, or -1 on bad arguments. */
 int bflyref_quantize(const double* y, int64_t rows, int32_t n, int32_t group, int32_t bits,
                      int32_t mode, int32_t use_given, uint8_t* codes, uint16_t* scales,
                      uint16_t* zeros, double* s_pre, double* z_pre, double* v)
 {
     if (rows < 0 || n < 1 || group < 1 || n % group != 0) return -1;
+    if (use_given < 0 || use_given > 2) return -1;
     if (bits != 2 && bits != 4) return -1;
     if (mode != REF_SYM && mode != REF_ASYM) return -1;
     if (((int64_t)n * bits) % 8 != 0) return -1;
@@ -336,7 +341,7 @@ int bflyref_quantize(const double* y, int64_t rows, int32_t n, int32_t group, in
                 if (sc != 0.0) {
                     double zq = zp / sc;
                     if (z_pre) z_pre[gi] = zq;
-                    if (use_given) {
+                    if (use_given == 1) {
                         z = bflyref_fp16_value(zeros[gi]);
                     } else {
                         z = rne(zq);
@@ -346,8 +351,8 @@ int bflyref_quantize(const double* y, int64_t rows, int32_t n, int32_t group, in
                     }
                 } else {
                     if (z_pre) z_pre[gi] = 0.0;
-                    if (!use_given) zeros[gi] = 0;
-                    z = use_given ? bflyref_fp16_value(zeros[gi]) : 0.0;
+                    if (use_given != 1) zeros[gi] = 0;
+                    z = use_given == 1 ? bflyref_fp16_value(zeros[gi]) : 0.0;
                 }
             }
             for (int k = 0; k < group; ++k) {
@@ -464,5 +469,15 @@ int bflyref_num_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads the parallel loops above use from now on (k >= 1). */
+void bflyref_set_num_threads(int k)
+{
+#ifdef _OPENMP
+    if (k >= 1) omp_set_num_threads(k);
+#else
+    (void)k;
 #endif
 }

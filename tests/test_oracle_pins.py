@@ -326,6 +326,27 @@ def test_quant_requantize_at_given_scale():
     assert np.allclose(q3["v"], y / sc, rtol=0, atol=1e-15)
 
 
+def test_asym_zero_point_derived_at_a_given_scale():
+    """Asymmetric INT2 group with min -1 and max 2 (worked by hand): its own
+    scale is fp16(3 / 3) = 1.0 (0x3C00) and zero rne(1 / 1) = 1.  Given other
+    scales, the zero point is re-derived at them: at 0.5 (0x3800) -min/s = 2
+    -> 2; at 1.0009765625 (0x3C01) 0.99902 -> 1; at 0.333251953125 (0x3555)
+    3.0007 -> clamped to the top level 3; at 2.0 (0x4000) 0.5 -> 0 (tie to
+    even)."""
+    y = np.array([[-1.0, 0.5, 2.0, 0.25, -0.75, 1.0, 0.0, 1.5]])
+    own = oracle.quantize(y, 2, 8, oracle.ASYM)
+    assert int(own["scales"][0, 0]) == 0x3C00 and int(own["zeros"][0, 0]) == 0x3C00  # 1.0
+    for s16, z16 in ((0x3800, 0x4000), (0x3C01, 0x3C00), (0x3555, 0x4200), (0x4000, 0x0000)):
+        q = oracle.quantize(y, 2, 8, oracle.ASYM, scales=np.array([[s16]], dtype=np.uint16))
+        assert int(q["scales"][0, 0]) == s16
+        assert int(q["zeros"][0, 0]) == z16, (hex(s16), hex(int(q["zeros"][0, 0])))
+    # with the oracle's own scale, the derived zero points are its own
+    yy = RNG.standard_normal((6, 256))
+    a = oracle.quantize(yy, 2, 128, oracle.ASYM)
+    b = oracle.quantize(yy, 2, 128, oracle.ASYM, scales=a["scales"])
+    assert np.array_equal(a["zeros"], b["zeros"]) and np.array_equal(a["codes"], b["codes"])
+
+
 def test_scale_saturates_at_fp16_max():
     y = np.full((1, 8), 1e6)
     y[0, 1] = -1e6
@@ -678,6 +699,66 @@ def test_adam_first_step_closed_form():
     t1, m1, v1 = oracle.adam(th, z, z, gr, 1, 1e-3, 0.9, 0.999, 1e-8)
     assert np.allclose(t1, th - 1e-3 * gr / (np.abs(gr) + 1e-8), rtol=0, atol=1e-15)
     assert np.allclose(m1, 0.1 * gr) and np.allclose(v1, 0.001 * gr * gr)
+
+
+def test_calib_hand_example():
+    """The loss terms, the histogram and dL/dy of a one-group example worked
+    out by hand (tests/golden/calib_hand_example.txt): pins the bin
+    assignment and interpolation weights, the direction and base of the KL
+    term, the smoothing and both gradient terms."""
+    kv = {}
+    for line in open(os.path.join(GOLDEN, "calib_hand_example.txt")):
+        if line.startswith("#") or "|" not in line:
+            continue
+        k, v = (s.strip() for s in line.split("|", 1))
+        kv[k] = v
+    vals = lambda k: np.array([float(t) for t in kv[k].split()])
+    y = vals("y")[None, :]
+    out = oracle.calib_loss_grad(y, int(kv["bits"]), int(kv["group"]), int(kv["bins"]),
+                                 float(kv["lambda"]))
+    q = oracle.quantize(y, int(kv["bits"]), int(kv["group"]), oracle.SYM)
+    assert int(q["scales"][0, 0]) == int(kv["scale_fp16"], 16)
+    assert np.array_equal(out["yhat"][0], vals("yhat"))
+    assert abs(out["rec"] - float(kv["rec"])) < 1e-15
+    assert np.allclose(out["p"], vals("p"), rtol=0, atol=1e-15)
+    assert abs(out["kl"] - float(kv["kl"])) < 1e-14
+    assert abs(out["loss"] - float(kv["loss"])) < 1e-14
+    assert np.allclose(out["g"][0], vals("grad"), rtol=1e-12, atol=1e-16)
+
+
+def test_adam_constant_gradient_closed_form():
+    """With the same gradient g at every step from zero moments,
+    m_t = (1 - b1^t) g and v_t = (1 - b2^t) g^2, so the bias-corrected
+    moments are exactly g and g^2 and each step moves theta by
+    lr g / (|g| + eps): theta_t = theta_0 - t lr g / (|g| + eps).  A bias
+    correction with the wrong power (b^1 instead of b^t) moves every step
+    after the first differently."""
+    rng = np.random.default_rng(84)
+    th0, gr = rng.standard_normal(40), rng.standard_normal(40)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    th, m, v = th0.copy(), np.zeros(40), np.zeros(40)
+    for t in range(1, 21):
+        th, m, v = oracle.adam(th, m, v, gr, t, lr, b1, b2, eps)
+        assert np.allclose(m, (1 - b1 ** t) * gr, rtol=1e-12, atol=0)
+        assert np.allclose(v, (1 - b2 ** t) * gr * gr, rtol=1e-12, atol=0)
+        assert np.allclose(th, th0 - t * lr * gr / (np.abs(gr) + eps), rtol=0, atol=1e-13)
+
+
+def test_adam_second_step_after_zero_gradient():
+    """Gradient g at step 1, then 0 at step 2: m_2 = b1 (1 - b1) g and
+    v_2 = b2 (1 - b2) g^2, so m^_2 = b1 g / (1 + b1), v^_2 = b2 g^2 / (1 + b2)
+    (worked by hand from the recurrences), and the second step moves theta
+    by lr m^_2 / (sqrt(v^_2) + eps)."""
+    rng = np.random.default_rng(85)
+    th0, gr = rng.standard_normal(30), rng.standard_normal(30)
+    lr, b1, b2, eps = 1e-2, 0.8, 0.95, 1e-8
+    z = np.zeros(30)
+    th1, m1, v1 = oracle.adam(th0, z, z, gr, 1, lr, b1, b2, eps)
+    th2, m2, v2 = oracle.adam(th1, m1, v1, np.zeros(30), 2, lr, b1, b2, eps)
+    mh = b1 * gr / (1 + b1)
+    vh = b2 * gr * gr / (1 + b2)
+    assert np.allclose(m2, b1 * (1 - b1) * gr, rtol=1e-12, atol=0)
+    assert np.allclose(th2, th1 - lr * mh / (np.sqrt(vh) + eps), rtol=0, atol=1e-13)
 
 
 def test_calib_step_reduces_the_loss():
