@@ -7,7 +7,9 @@ Tolerances (the readings the design documents give them):
   |gpu - y64| <= 4 * ceil(log2 n) * 2^-24 * ||x_r||_2 -- counted separately.
 * fp16 scales: bit-exact, except where the oracle's pre-rounding scale lies
   within 1e-6 (relative) of an fp16 rounding midpoint: either neighbour
-  passes (counted).  Zero points the same, window 1e-6 absolute on -min/s.
+  passes (counted).  Zero points: the oracle derives them again at the
+  scale the GPU emitted; they must match except within 1e-6 (absolute) of a
+  rounding boundary of -min/s.
 * codes: the oracle re-quantizes its fp64 y at the scales (and zero points)
   the GPU emitted; codes must match bit for bit except where y64/scale lies
   within 1e-6 of a rounding boundary (counted).
@@ -87,9 +89,13 @@ def check_quant(y64: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros, b
         res["ok"] = False
         res["scale_bad"] = int((sdiff & ~in_win).sum())
     if mode == oracle.ASYM:
-        zdiff = zeros != ref["zeros"]
-        zin = _near_half(ref["z_pre"], 1e-6) | sdiff  # a moved scale moves the zero point
+        # zero points re-derived at the scales the GPU emitted (its own where
+        # the scales agree), window 1e-6 on -min / scale
+        zref = oracle.quantize(y64, bits, group, mode, scales=scales)
+        zdiff = zeros != zref["zeros"]
+        zin = _near_half(zref["z_pre"], 1e-6)
         res["zero_mismatch"] = int(zdiff.sum())
+        res["zero_in_window"] = int((zdiff & zin).sum())
         if (zdiff & ~zin).any():
             res["ok"] = False
             res["zero_bad"] = int((zdiff & ~zin).sum())

@@ -3,12 +3,17 @@ against the fp64 oracle: ragged small shapes element by element, and the
 full 8192 x 4096 x 11008 W2A16 product (activations of the headline batch
 against the 11008 x 4096 weight) on sampled rows.
 
-Tolerance (derived from the arithmetic): the kernels sum exact products
-a * (q - zero) in fp32 -- over one group (MFMA tiles) or over 16 codes
-(the few-row kernel) -- multiply by the group's scale and add the partial
-sums in fp32, so
-    |y - y64| <= (group + k / 16 + 2) * 2^-24 * sum_k |a_k| |w_k|
-for fp32 outputs; bf16 outputs add half a bf16 ulp of the result."""
+Tolerance (derived from each kernel's arithmetic; a sum whose terms pass
+through at most D fp32 roundings is within D * 2^-24 * sum |terms| of the
+exact sum): every product a * (q - zero) is exact in fp32.
+* MFMA tiles (more than 64 rows): one group's products summed in fp32
+  (at most `group` roundings), times the group's scale (1), added over the
+  k / group groups:  D = group + k / group + 2.
+* few-row kernel (64 rows or fewer): each lane sums KU codes with v_dot2
+  (counted as one rounding per product: KU), scales the chunk (1), adds
+  its k / (64 KU) chunks, and the 64 lanes are added by a 6-level tree:
+  D = KU + k / (64 KU) + 9, with KU = 64 for one row and 16 otherwise.
+bf16 outputs add half a bf16 ulp of the result."""
 import math
 
 import numpy as np
@@ -69,15 +74,24 @@ def run(a_bits, codes, scales, zeros, bits, group, mode, y_dtype):
     return (host_bits(y).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def rounding_depth(call_rows, k, group):
+    """D of the kernel that a call with `call_rows` rows runs (see above)."""
+    if call_rows > 64:
+        return group + k // group + 2
+    ku = 64 if call_rows == 1 else 16
+    return ku + max(1, k // (64 * ku)) + 9
+
+
 def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=None):
     a = inputs.bf16_bits_to_f32(a_bits).reshape(a_bits.shape).astype(np.float64)
+    call_rows = a.shape[0]
     if rows is not None:
         a = a[rows]
         got = got[rows]
     w = oracle.dequantize(codes, scales, zeros, bits, group, mode, a.shape[1])
     y64 = a @ w.T
     k = a.shape[1]
-    bound = (group + k // 16 + 2) * U * (np.abs(a) @ np.abs(w).T)
+    bound = rounding_depth(call_rows, k, group) * U * (np.abs(a) @ np.abs(w).T)
     if bf16_out:
         mag = np.maximum(np.abs(got), np.abs(y64))
         e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
