@@ -12,13 +12,15 @@ timed region; the step cycles through 5 separate input/output buffer sets
 
 Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step:
 18 496 B per row (8192 in + 8192 out + 2048 codes + 64 scale bytes) plus the
-96 KiB of angles, divided by the mean step time.  `roofline` prices the
-fused kernel alone against the 8 TB/s HBM peak: on every 16th timed step a
-pair of HIP events is attached to its dispatch (bfly_time_next_forward), so
-they time the kernel's own start to end, the span the kernel trace reports.
-`traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded
-for the current kernel sources (null if they changed).  `cpu_baseline` times
-the fp64 oracle on the host's cores.
+96 KiB of angles, divided by the mean step time.  After the timed steps the
+fused kernel runs again with its table made once (fixed angles, as at
+inference): back to back (`table_made_once_*`), and 240 times with a pair of
+HIP events attached to its dispatch (bfly_time_next_forward), whose median
+is the kernel's own duration, the span a kernel trace reports; `roofline`
+prices that median against the 8 TB/s HBM peak.  `traffic` comes from
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded for the current kernel
+sources (null if they changed).  `cpu_baseline` times the fp64 oracle on the
+host's cores (all threads; one-thread timings of three workloads beside it).
 
 --workload picks one of the other workloads for a secondary line:
 tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
@@ -93,29 +95,74 @@ def to_dev(a, torch):
 # CPU baseline: the fp64 oracle, as it stands
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_act(w, bytes_per_row, passes=3):
-    import oracle
-    x, th = w["x"], w["theta"]
-    times = []
-    for _ in range(passes):
-        t0 = time.perf_counter()
-        y64 = oracle.forward(x, th)
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_pass(oracle, w, kind):
+    """One pass of the oracle over a workload: fp64 forward (or Kronecker
+    forward), bf16 rounding of y, the workload's quantizer."""
+    if kind == "tiny":
+        oracle.forward(w["x"], w["theta"])
+    elif kind == "act":
+        y64 = oracle.forward(w["x"], w["theta"])
         oracle.round_bf16(y64)
         oracle.quantize(y64, 4, 128, oracle.SYM)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    rows = x.shape[0]
-    return {"value": rows * bytes_per_row / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+    else:  # kron
+        y64 = oracle.kron_forward(w["x"], w["theta_b"], w["mix"])
+        oracle.round_bf16(y64)
+        oracle.quantize(y64, 4, 128, oracle.SYM)
+
+
+def _median_time(fn, passes):
+    ts = []
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline_act(w, bytes_per_row, inputs, passes=3):
+    """The oracle on the headline workload with all host threads (the
+    reported baseline), plus one-thread timings of the tiny, headline and
+    n = 5120 Kronecker workloads."""
+    import oracle
+    threads = oracle.num_threads()
+    rows = w["x"].shape[0]
+    t = _median_time(lambda: _oracle_pass(oracle, w, "act"), passes)
+    one = {}
+    try:
+        oracle.set_num_threads(1)
+        for name, wl, kind, bpr in (
+                ("tiny_n256_fp32", inputs.tiny_fp32(), "tiny", 256 * 8),
+                ("act_n4096_bf16_int4", w, "act", bytes_per_row),
+                ("kron_n5120_bf16_int4", inputs.kron_int4(rows=2048), "kron",
+                 10240 + 10240 + 2560 + 80)):
+            r = wl["x"].shape[0]
+            t1 = _median_time(lambda: _oracle_pass(oracle, wl, kind), 3 if kind == "tiny" else 1)
+            one[name] = {"rows": r, "s": round(t1, 4), "rows_per_s": round(r / t1),
+                         "GBs": round(r * bpr / t1 / 1e9, 5)}
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": rows * bytes_per_row / t / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "all %d rows of the workload (fp64 forward, bf16 rounding, INT4 quantization),"
-                      " median of %d passes: %.3f s per pass, %.0f rows/s" % (rows, passes, t, rows / t)}
+                      " median of %d passes: %.3f s per pass, %.0f rows/s" % (rows, passes, t, rows / t),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "one_thread": one}
 
 
 # ---------------------------------------------------------------------------
 # the headline workload
 # ---------------------------------------------------------------------------
 
-EVENT_EVERY = 16
+KERNEL_TIMED_LAUNCHES = 240   # event-timed launches of the fused kernel, whatever --steps is
 
 
 def warm_up(torch, fn, steps, min_seconds=0.3):
@@ -160,62 +207,87 @@ def bench_act(args, torch, B, inputs):
             for s in sets]
     th_p, tab_p, tab_n = theta.data_ptr(), tab.data_ptr(), tab.numel()
 
-    def step(i, ev=None):
+    def fused(i, ev=None):
         px, py, pc, ps = ptrs[i % NSETS]
-        st = lib.bfly_prepare(th_p, n, tab_p, tab_n, sh)
+        st = 0
         if ev is not None:  # events on the fused kernel's own dispatch
             st |= lib.bfly_time_next_forward(ev[0].cuda_event, ev[1].cuda_event)
         st |= lib.bfly_forward_quant(px, B.BFLY_BF16, py, B.BFLY_BF16, pc, ps, None, rows, n,
-                                     None, tab_p, bits, group, B.BFLY_SYM_ABSMAX, sh)
+                                     None, tab_p, bits, group, B.BFLY_SYM_ABSMAX, None, 0, sh)
         if st:
             raise RuntimeError("libbfly call failed with status %d" % st)
 
+    def step(i):
+        # the whole path: angles -> coefficient table, then the fused kernel
+        st = lib.bfly_prepare(th_p, n, tab_p, tab_n, sh)
+        if st:
+            raise RuntimeError("bfly_prepare failed with status %d" % st)
+        fused(i)
+
+    # 1. the timed steps (the headline value)
     warm_s = warm_up(torch, step, args.warmup)
-    # A pair of HIP events is attached to the fused kernel's dispatch on every
-    # EVENT_EVERY-th timed step (bfly_time_next_forward): their timestamps are
-    # the kernel's own start and end on its stream, with no marker packets in
-    # the stream.  Recording each event once beforehand creates it.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
-    for e in evs:
-        if e is not None:
-            e[0].record(stream)
-            e[1].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [e[0].elapsed_time(e[1]) for e in evs if e is not None]
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
-    achieved = kernel_bytes / kern_avg_s / 1e9
-    traffic = recorded_traffic()
     value = step_bytes / (ms_step / 1e3) / 1e9
+
+    # 2. the fused kernel with the table made once (fixed angles, as at
+    # inference), back to back
+    nfixed = max(args.steps, 200)
+    warm_up(torch, fused, 20, min_seconds=0.1)
+    t0 = time.perf_counter()
+    for i in range(nfixed):
+        fused(i)
+    torch.cuda.synchronize()
+    us_fixed = (time.perf_counter() - t0) * 1e6 / nfixed
+
+    # 3. the fused kernel's own duration: HIP events attached to its dispatch
+    # (bfly_time_next_forward), KERNEL_TIMED_LAUNCHES launches rotating the
+    # buffer sets, median and spread.  Recording each event once creates it.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(KERNEL_TIMED_LAUNCHES)]
+    for e in evs:
+        e[0].record(stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        fused(i, e)
+    torch.cuda.synchronize()
+    kern_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    kern_med_s = float(np.median(kern_ms)) / 1e3
+    achieved = kernel_bytes / kern_med_s / 1e9
+    traffic = recorded_traffic()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w["name"] + ": 8192 rows x n=4096, bf16 in, bf16 Q x out, "
-                               "symmetric absmax INT4 codes per group of 128, fp16 scales",
+                               "symmetric absmax INT4 codes per group of 128, fp16 scales; "
+                               "a step = bfly_prepare + bfly_forward_quant",
                    "rows": rows, "n": n, "bits": bits, "group": group,
                    "bytes_per_step": step_bytes, "rows_per_s": round(rows / (ms_step / 1e3)),
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "table_made_once_us_per_launch": round(us_fixed, 3),
+                   "table_made_once_GBs": round(kernel_bytes / (us_fixed / 1e6) / 1e9, 2),
+                   "table_made_once_launches": nfixed,
                    "buffer_sets": NSETS, "warmup_s": round(warm_s, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "fwd_kernel<12,1,2,bf16,bf16 out,int4 g128> (bfly_forward_quant)",
                      "timed_launches": len(kern_ms),
-                     "kernel_avg_us": round(kern_avg_s * 1e6, 3),
+                     "kernel_median_us": round(kern_med_s * 1e6, 3),
                      "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
                      "algorithmic_bytes_per_launch": kernel_bytes},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_act(w, bytes_per_row)
+        out["cpu_baseline"] = cpu_baseline_act(w, bytes_per_row, inputs)
     return out
 
 

@@ -31,6 +31,13 @@
  *   bfly_*_bytes, bfly_status_string, bfly_last_hip_error
  *   bfly_time_next_forward                       kernel-only timing of the next forward
  *
+ * Extensions beyond the four calls the pages' problem statement gives
+ * (forward, fused forward + quantization, Kronecker forward, backward):
+ * the prepared table (`coeffs`, bfly_prepare) that lets fixed angles skip
+ * their preparation on every call, the workspace arguments that carry the
+ * table when it is prepared per call, and the measurement hook
+ * bfly_time_next_forward.  None of them changes what is computed.
+ *
  * Conventions common to every call:
  *   - All data pointers are DEVICE pointers owned by the caller, contiguous
  *     row-major with a row stride of n elements (bytes for codes: n*bits/8).
@@ -38,11 +45,17 @@
  *   - y == x (in place) is allowed, as is dx == g; no other aliasing.
  *   - theta: fp32 angles [log2 n][n/2] on the device.
  *   - coeffs: optional device table prepared from theta by bfly_prepare().
- *     When coeffs is non-NULL, theta is not read (it may be NULL) and no
- *     preparation runs.  When coeffs is NULL the call prepares the table
- *     itself from theta into stream-ordered scratch taken with
- *     hipMallocAsync/hipFreeAsync on hip_stream (bfly_backward uses its
- *     workspace instead and allocates nothing).
+ *     When coeffs is non-NULL, theta is not read (it may be NULL), no
+ *     preparation runs and a forward call's workspace is not used (it may
+ *     be NULL).  When coeffs is NULL the call first prepares the table from
+ *     theta into the caller's workspace: the forward calls then need
+ *     workspace_bytes >= bfly_coeff_bytes(n) (16-byte aligned), the other
+ *     calls size their workspace with their own *_workspace_bytes query.
+ *   - The library allocates no memory in any call: every buffer, scratch
+ *     included, comes from the caller.  Its only state is a fixed-size
+ *     per-device cache of launch facts (CU count, resident workgroups per
+ *     kernel; filled on first use under a lock), the armed events of
+ *     bfly_time_next_forward and the per-thread last HIP error.
  *   - hip_stream: a hipStream_t (NULL = the null stream).  Calls enqueue work
  *     and return; results are valid once the stream is synchronised.
  *   - rows == 0 is a no-op returning BFLY_OK (bfly_backward then writes
@@ -52,9 +65,11 @@
  *     BFLY_ERR_HIP; the HIP error code is then available from
  *     bfly_last_hip_error() on the calling thread.
  *   - Supported sizes: n a power of two in [64, 4096] (smaller powers of
- *     two and 8192 return BFLY_ERR_UNSUPPORTED); for the Kronecker call
+ *     two and 8192 return BFLY_ERR_UNSUPPORTED); for bfly_kron_forward
  *     m in [1, 8] and nb a power of two with m * nb <= 8192, nb in
- *     [256, 4096] for m >= 2 and in [64, 4096] for m = 1.
+ *     [256, 4096] for m >= 2 and in [64, 4096] for m = 1; for the wide
+ *     forward and the Kronecker backward m in [2, 64], nb in [256, 4096],
+ *     m * nb <= 65536.
  *   - Results do not depend on the launch configuration or on the device's
  *     compute-unit count (the angle-gradient reduction order is fixed).
  */
@@ -128,11 +143,14 @@ bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, v
 /* ---- forward ------------------------------------------------------------ */
 
 /* y[r] = Q(theta) x[r] for r < rows.  x_dt, y_dt in {BFLY_F32, BFLY_BF16};
- * bf16 outputs are rounded to nearest even from fp32.  Passage: ButterflyQuant
- * abstract (Q x and W Q^T). */
+ * bf16 outputs are rounded to nearest even from fp32.  workspace: with
+ * coeffs == NULL, >= bfly_coeff_bytes(n) bytes of device scratch that
+ * receives the table (BFLY_ERR_NULL if missing, BFLY_ERR_WORKSPACE if
+ * smaller); ignored with coeffs.  Passage: ButterflyQuant abstract (Q x and
+ * W Q^T). */
 bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                          int64_t rows, int32_t n, const float* theta, const void* coeffs,
-                         void* hip_stream);
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* The forward, fused with per-group round-to-nearest quantization of y.
  *   y      : may be NULL (codes only); else [rows][n] of y_dt
@@ -143,12 +161,14 @@ bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_d
  *            NULL for BFLY_SYM_ABSMAX
  *   bits   : 2 or 4; group: 8, 16, 32, 64, 128, 256 or 512, dividing n;
  *            groups are runs of `group` consecutive output elements.
+ *   workspace, workspace_bytes: as in bfly_forward.
  * Passages: ButterflyQuant abstract (orthogonal transforms applied before
  * quantization), WUSH technical summary section 2 (RTN absmax quantizer). */
 bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                                uint8_t* codes, uint16_t* scales, uint16_t* zeros,
                                int64_t rows, int32_t n, const float* theta, const void* coeffs,
-                               int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
+                               int32_t bits, int32_t group, bfly_qmode mode, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
 
 /* Kronecker composite for widths n = m * nb that are not a power of two
  * (duidaima.com write-up, section "butterfly": LLaMA-2-13B's 5120):
@@ -158,12 +178,15 @@ bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dty
  *   mix (device fp32, row-major) mixes the segments column by column:
  *   y[a*nb + b] = sum_a' mix[a][a'] z[a'*nb + b].
  * codes == NULL => no quantization (scales and zeros must then be NULL);
- * otherwise as in bfly_forward_quant, with group dividing nb. */
+ * otherwise as in bfly_forward_quant, with group dividing nb.  workspace:
+ * with coeffs_b == NULL, >= bfly_coeff_bytes(nb) bytes (as in
+ * bfly_forward). */
 bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                               uint8_t* codes, uint16_t* scales, uint16_t* zeros,
                               int64_t rows, int32_t m, int32_t nb, const float* theta_b,
                               const void* coeffs_b, const float* mix,
-                              int32_t bits, int32_t group, bfly_qmode mode, void* hip_stream);
+                              int32_t bits, int32_t group, bfly_qmode mode, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
 
 /* Kronecker composites with more segments: the same y[r] = (O kron
  * B(theta_b)) x[r] and optional quantization as bfly_kron_forward, for
@@ -171,12 +194,12 @@ bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtyp
  * m * nb <= 65536.  Two passes: v = (O kron I) x in fp32 into `workspace`,
  * then the butterfly with its fused quantizer on the rows * m segments of v
  * ((O kron B) = (I kron B)(O kron I)).  workspace: >=
- * bfly_kron_forward_wide_workspace_bytes(rows, m, nb) = rows * m * nb * 4
- * bytes of device memory, 16-byte aligned, caller-owned.  codes == NULL =>
- * no quantization (scales, zeros then NULL); otherwise as in
- * bfly_forward_quant with group dividing nb.  With theta_b (no coeffs_b)
- * the table is prepared as in bfly_forward.  Errors as bfly_kron_forward,
- * plus BFLY_ERR_WORKSPACE.  Passage: ButterflyQuant write-up, section
+ * bfly_kron_forward_wide_workspace_bytes(rows, m, nb) bytes of device
+ * memory (the table's bytes rounded up to 256, then rows * m * nb * 4),
+ * 16-byte aligned, caller-owned.  codes == NULL => no quantization
+ * (scales, zeros then NULL); otherwise as in bfly_forward_quant with group
+ * dividing nb.  With theta_b (no coeffs_b) the table is prepared into the
+ * workspace.  Errors as bfly_kron_forward, plus BFLY_ERR_WORKSPACE.  Passage: ButterflyQuant write-up, section
  * "butterfly" (Kronecker composites for widths that are not powers of
  * two). */
 bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
@@ -216,9 +239,9 @@ size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n);
  *              [log2 nb][nb/2], OVERWRITTEN (zeros when rows == 0)
  * Computed as dL/dz = (O^T kron I) G, then the butterfly backward on the
  * rows * m segments of length nb (z = (I kron B) x per segment), with the
- * same fixed-order reduction as bfly_backward.  Sizes: m in [2, 8] (m = 1
+ * same fixed-order reduction as bfly_backward.  Sizes: m in [2, 64] (m = 1
  * is the plain butterfly: bfly_backward), nb a power of two in [256, 4096],
- * m * nb <= 8192.  workspace: >= bfly_kron_backward_workspace_bytes(rows, m,
+ * m * nb <= 65536.  workspace: >= bfly_kron_backward_workspace_bytes(rows, m,
  * nb) bytes of device scratch, 16-byte aligned; the call allocates nothing.
  * Errors as bfly_backward.  Passages: ButterflyQuant write-up, section
  * "butterfly" (the Kronecker composite for widths like 5120) and section
@@ -311,7 +334,7 @@ const char* bfly_status_string(bfly_status s);
 int32_t bfly_last_hip_error(void);
 
 /* Kernel-only timing of the fused forward kernel (a measurement hook, not
- * part of the method).  start_event and stop_event are hipEvent_t handles
+ * part of the method; an extension of the ABI, see above).  start_event and stop_event are hipEvent_t handles
  * the caller created (timing enabled) and owns.  The next launch of the
  * fused forward kernel in this process, by bfly_forward, bfly_forward_quant,
  * bfly_kron_forward or bfly_kron_forward_wide on any stream, is dispatched

@@ -61,11 +61,12 @@ def lib():
         L.bfly_coeff_bytes.restype = sz
         L.bfly_prepare.argtypes = [vp, i32, vp, sz, vp]
         L.bfly_prepare_hadamard.argtypes = [i32, vp, sz, vp]
-        L.bfly_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, vp]
+        L.bfly_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, vp, sz,
+                                   vp]
         L.bfly_forward_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
-                                         vp, vp, i32, i32, ctypes.c_int, vp]
+                                         vp, vp, i32, i32, ctypes.c_int, vp, sz, vp]
         L.bfly_kron_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
-                                        i32, vp, vp, vp, i32, i32, ctypes.c_int, vp]
+                                        i32, vp, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp]
         L.bfly_kron_forward_wide.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64,
                                              i32, i32, vp, vp, vp, i32, i32, ctypes.c_int, vp, sz,
                                              vp]
@@ -136,6 +137,22 @@ def _check(status, where):
         raise BflyError(status, where)
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _table_ws(n, theta, coeffs, workspace, like):
+    """The workspace a forward call prepares its table into: the caller's,
+    or -- when angles are given without a table or a workspace -- a fresh
+    uint8 tensor of bfly_coeff_bytes(n) from torch's allocator on the
+    device of `like` (torch supplies the device memory; the library
+    allocates none)."""
+    if coeffs is not None or workspace is not None or theta is None:
+        return workspace
+    import torch
+    return torch.empty(max(1, bfly_coeff_bytes(n)), dtype=torch.uint8, device=like.device)
+
+
 # ---------------------------------------------------------------------------
 # the C ABI, one function per entry point
 # ---------------------------------------------------------------------------
@@ -156,32 +173,37 @@ def bfly_prepare_hadamard(n: int, coeffs, stream=None) -> None:
                                        _stream(stream)), "bfly_prepare_hadamard")
 
 
-def bfly_forward(x, y, theta=None, coeffs=None, stream=None) -> None:
+def bfly_forward(x, y, theta=None, coeffs=None, workspace=None, stream=None) -> None:
     """y[r] = Q(theta) x[r]; x, y: [rows, n] float32/bfloat16 on the GPU."""
     rows, n = x.shape
+    ws = _table_ws(n, theta, coeffs, workspace, x)
     _check(lib().bfly_forward(_ptr(x), _dt(x), _ptr(y), _dt(y), rows, n, _ptr(theta),
-                              _ptr(coeffs), _stream(stream)), "bfly_forward")
+                              _ptr(coeffs), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "bfly_forward")
 
 
 def bfly_forward_quant(x, y, codes, scales, zeros=None, theta=None, coeffs=None, bits=4,
-                       group=128, mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+                       group=128, mode=BFLY_SYM_ABSMAX, workspace=None, stream=None) -> None:
     """Forward fused with per-group RTN quantization (y may be None)."""
     rows, n = x.shape
+    ws = _table_ws(n, theta, coeffs, workspace, x)
     _check(lib().bfly_forward_quant(_ptr(x), _dt(x), _ptr(y), _dt(y) if y is not None else 0,
                                     _ptr(codes), _ptr(scales), _ptr(zeros), rows, n, _ptr(theta),
-                                    _ptr(coeffs), bits, group, mode, _stream(stream)),
+                                    _ptr(coeffs), bits, group, mode, _ptr(ws), _nbytes(ws),
+                                    _stream(stream)),
            "bfly_forward_quant")
 
 
 def bfly_kron_forward(x, y, mix, codes=None, scales=None, zeros=None, theta_b=None, coeffs_b=None,
-                      bits=4, group=128, mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+                      bits=4, group=128, mode=BFLY_SYM_ABSMAX, workspace=None, stream=None) -> None:
     """(O kron B) on rows of n = m * nb; mix: [m, m] float32 on the GPU."""
     rows, n = x.shape
     m = mix.shape[0]
+    ws = _table_ws(n // m, theta_b, coeffs_b, workspace, x)
     _check(lib().bfly_kron_forward(_ptr(x), _dt(x), _ptr(y), _dt(y) if y is not None else 0,
                                    _ptr(codes), _ptr(scales), _ptr(zeros), rows, m, n // m,
                                    _ptr(theta_b), _ptr(coeffs_b), _ptr(mix), bits, group, mode,
-                                   _stream(stream)), "bfly_kron_forward")
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), "bfly_kron_forward")
 
 
 def bfly_kron_forward_wide_workspace_bytes(rows: int, m: int, nb: int) -> int:

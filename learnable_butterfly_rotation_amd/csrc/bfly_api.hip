@@ -9,6 +9,7 @@
 
 #include "../../include/bfly.h"
 #include "bfly_internal.h"
+#include "bfly_common.h"
 #include "bfly_calib.h"
 #include "bfly_qgemm.h"
 
@@ -23,8 +24,7 @@ hipError_t launch_forward_kron_m7(const FwdParams& p, hipStream_t s);
 hipError_t launch_forward_kron_m8(const FwdParams& p, hipStream_t s);
 hipError_t launch_kron_mix(const void* x, bool xbf16, float* v, const float* mix, int64_t rows,
                            int m, int nb, hipStream_t s);
-hipError_t launch_kron_bwd_setup(const float* mix, int m, float* mix_t, float* theta0, int n_theta,
-                                 hipStream_t s);
+hipError_t launch_kron_bwd_setup(const float* mix, int m, float* mix_t, hipStream_t s);
 
 bool forward_supported(int lognb, int m) {
   if (m == 1) return lognb >= 6 && lognb <= 12;
@@ -62,6 +62,54 @@ void arm_forward_events(hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lock(g_events_mu);
   g_events.start = start;
   g_events.stop = stop;
+}
+
+namespace {
+// Fixed-size open-addressing cache of kernel_setup's results (no heap
+// allocation): one entry per (kernel, device) that has been launched.
+struct SetupEntry {
+  const void* kernel;
+  int device, per_cu, num_cu;
+};
+constexpr int kSetupSlots = 4096;  // well above the library's kernel count
+std::mutex g_setup_mu;
+SetupEntry g_setup[kSetupSlots];
+}  // namespace
+
+hipError_t kernel_setup(const void* kernel, int threads, size_t lds_bytes, int* per_cu,
+                        int* num_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_setup_mu);
+  size_t h = (reinterpret_cast<uintptr_t>(kernel) >> 4) * 0x9E3779B97F4A7C15ull + (size_t)dev;
+  SetupEntry* slot = nullptr;
+  for (int probe = 0; probe < kSetupSlots; ++probe) {
+    SetupEntry& c = g_setup[(h + probe) % kSetupSlots];
+    if (c.kernel == kernel && c.device == dev) {
+      slot = &c;
+      break;
+    }
+    if (c.kernel == nullptr) {  // not cached yet: work it out into this slot
+      e = allow_lds(kernel, lds_bytes);
+      if (e != hipSuccess) return e;
+      int cus = 0, bpc = 0;
+      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, kernel, threads, lds_bytes);
+      if (e != hipSuccess) return e;
+      c.kernel = kernel;
+      c.device = dev;
+      c.per_cu = bpc > 0 ? bpc : 1;
+      c.num_cu = cus;
+      slot = &c;
+      break;
+    }
+  }
+  if (!slot) return hipErrorOutOfMemory;  // more (kernel, device) pairs than slots
+  if (per_cu) *per_cu = slot->per_cu;
+  if (num_cu) *num_cu = slot->num_cu;
+  return hipSuccess;
 }
 }  // namespace bfly
 
@@ -124,25 +172,6 @@ bfly_status check_quant(const uint8_t* codes, const uint16_t* scales, const uint
   return BFLY_OK;
 }
 
-// Runs `launch` with the coefficient table `coeffs`, or -- when coeffs is
-// NULL -- prepares the table from theta into stream-ordered scratch first.
-template <class F>
-bfly_status with_table(const float* theta, const void* coeffs, int logn, hipStream_t s, F launch) {
-  if (coeffs) {
-    const hipError_t e = launch(coeffs);
-    return e == hipSuccess ? BFLY_OK : hip_fail(e);
-  }
-  void* tab = nullptr;
-  hipError_t e = hipMallocAsync(&tab, coeff_bytes_l(logn), s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = bfly::launch_prepare(theta, tab, logn, s);
-  if (e == hipSuccess) e = launch(tab);
-  const hipError_t ef = hipFreeAsync(tab, s);
-  if (e != hipSuccess) return hip_fail(e);
-  if (ef != hipSuccess) return hip_fail(ef);
-  return BFLY_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -182,13 +211,17 @@ bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, v
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
-static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
-                                  uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
-                                  int32_t m, int32_t nb, const float* theta, const void* coeffs,
-                                  const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
-                                  bool quant, void* hip_stream) {
+// Validates a forward call and fills its launch parameters (all but the
+// table).  With coeffs == NULL the table is prepared from theta into the
+// first bfly_coeff_bytes(nb) bytes of `workspace`.
+static bfly_status forward_args(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                                int32_t m, int32_t nb, const float* theta, const void* coeffs,
+                                const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
+                                bool quant, const void* workspace, size_t workspace_bytes,
+                                bfly::FwdParams* p) {
   if (rows > 0 && !x) return BFLY_ERR_NULL;
-  if (!theta && !coeffs) return BFLY_ERR_NULL;
+  if (!coeffs && (!theta || !workspace)) return BFLY_ERR_NULL;
   if (rows > 0 && !y && !quant) return BFLY_ERR_NULL;
   if (!dtype_ok(x_dt) || (y && !dtype_ok(y_dt))) return BFLY_ERR_DTYPE;
   if (rows < 0) return BFLY_ERR_SIZE;
@@ -202,61 +235,89 @@ static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_
     if (st != BFLY_OK) return st;
   }
   if (!bfly::forward_supported(lognb, m)) return BFLY_ERR_UNSUPPORTED;
+  if (!coeffs && workspace_bytes < coeff_bytes_l(lognb)) return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || (y && !aligned(y, 16))) return BFLY_ERR_ALIGN;
   if ((coeffs && !aligned(coeffs, 16)) || (theta && !aligned(theta, 4)) ||
-      (mix && !aligned(mix, 4)))
+      (mix && !aligned(mix, 4)) || (!coeffs && !aligned(workspace, 16)))
     return BFLY_ERR_ALIGN;
-  if (rows == 0) return BFLY_OK;
+  memset(p, 0, sizeof(*p));
+  p->x = x;
+  p->y = y;
+  p->codes = quant ? codes : nullptr;
+  p->scales = quant ? scales : nullptr;
+  p->zeros = quant ? zeros : nullptr;
+  p->mix = mix;
+  p->rows = rows;
+  p->m = m;
+  p->lognb = lognb;
+  p->x_bf16 = x_dt == BFLY_BF16;
+  p->y_kind = !y ? bfly::Y_NONE : (y_dt == BFLY_BF16 ? bfly::Y_BF16 : bfly::Y_F32);
+  p->bits = quant ? bits : 0;
+  p->group = quant ? group : 0;
+  p->asym = quant && mode == BFLY_ASYM_MINMAX;
+  return BFLY_OK;
+}
 
+// Enqueues a validated forward: the table (prepared into `table_ws` from
+// theta when coeffs is NULL), then the fused kernel.  Nothing for rows == 0.
+static bfly_status forward_run(bfly::FwdParams& p, const float* theta, const void* coeffs,
+                               void* table_ws, hipStream_t s) {
+  if (p.rows == 0) return BFLY_OK;
+  const void* tab = coeffs;
+  if (!tab) {
+    const hipError_t e = bfly::launch_prepare(theta, table_ws, p.lognb, s);
+    if (e != hipSuccess) return hip_fail(e);
+    tab = table_ws;
+  }
+  p.tab = bfly::table_at(tab, p.lognb);
+  const hipError_t e = bfly::launch_forward(p, s);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                  uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                                  int32_t m, int32_t nb, const float* theta, const void* coeffs,
+                                  const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
+                                  bool quant, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream) {
   bfly::FwdParams p;
-  memset(&p, 0, sizeof(p));
-  p.x = x;
-  p.y = y;
-  p.codes = quant ? codes : nullptr;
-  p.scales = quant ? scales : nullptr;
-  p.zeros = quant ? zeros : nullptr;
-  p.mix = mix;
-  p.rows = rows;
-  p.m = m;
-  p.lognb = lognb;
-  p.x_bf16 = x_dt == BFLY_BF16;
-  p.y_kind = !y ? bfly::Y_NONE : (y_dt == BFLY_BF16 ? bfly::Y_BF16 : bfly::Y_F32);
-  p.bits = quant ? bits : 0;
-  p.group = quant ? group : 0;
-  p.asym = quant && mode == BFLY_ASYM_MINMAX;
-  const hipStream_t s = (hipStream_t)hip_stream;
-  return with_table(theta, coeffs, lognb, s, [&](const void* tab) {
-    p.tab = bfly::table_at(tab, lognb);
-    return bfly::launch_forward(p, s);
-  });
+  const bfly_status st = forward_args(x, x_dt, y, y_dt, codes, scales, zeros, rows, m, nb, theta,
+                                      coeffs, mix, bits, group, mode, quant, workspace,
+                                      workspace_bytes, &p);
+  if (st != BFLY_OK) return st;
+  return forward_run(p, theta, coeffs, workspace, (hipStream_t)hip_stream);
 }
 
 bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt, int64_t rows,
-                         int32_t n, const float* theta, const void* coeffs, void* hip_stream) {
+                         int32_t n, const float* theta, const void* coeffs, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
   if (rows > 0 && !y) return BFLY_ERR_NULL;
   return forward_common(x, x_dt, y, y_dt, nullptr, nullptr, nullptr, rows, 1, n, theta, coeffs,
-                        nullptr, 0, 0, BFLY_SYM_ABSMAX, false, hip_stream);
+                        nullptr, 0, 0, BFLY_SYM_ABSMAX, false, workspace, workspace_bytes,
+                        hip_stream);
 }
 
 bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                                uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
                                int32_t n, const float* theta, const void* coeffs, int32_t bits,
-                               int32_t group, bfly_qmode mode, void* hip_stream) {
+                               int32_t group, bfly_qmode mode, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
   return forward_common(x, x_dt, y, y_dt, codes, scales, zeros, rows, 1, n, theta, coeffs,
-                        nullptr, bits, group, mode, true, hip_stream);
+                        nullptr, bits, group, mode, true, workspace, workspace_bytes, hip_stream);
 }
 
 bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                               uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
                               int32_t m, int32_t nb, const float* theta_b, const void* coeffs_b,
                               const float* mix, int32_t bits, int32_t group, bfly_qmode mode,
-                              void* hip_stream) {
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (!mix) return BFLY_ERR_NULL;
   if (m < 1 || m > 8) return BFLY_ERR_SIZE;
   if (!codes && (scales || zeros)) return BFLY_ERR_QUANT;
   if (log2_pow2(nb) >= 13) return BFLY_ERR_UNSUPPORTED;
   return forward_common(x, x_dt, y, y_dt, codes, scales, zeros, rows, m, nb, theta_b, coeffs_b,
-                        mix, bits, group, mode, codes != nullptr, hip_stream);
+                        mix, bits, group, mode, codes != nullptr, workspace, workspace_bytes,
+                        hip_stream);
 }
 
 size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n) {
@@ -310,10 +371,18 @@ static bool kron_wide_sizes(int32_t m, int32_t nb, int* lognb) {
   return (int64_t)m * nb <= 65536;
 }
 
+// Workspace of the wide composite: the coefficient table (when prepared
+// from theta_b), then v = (O kron I) x in fp32.
+static size_t kron_wide_parts(int64_t rows, int32_t m, int lognb, size_t* o_v) {
+  const size_t v = align_up(coeff_bytes_l(lognb), 256);
+  if (o_v) *o_v = v;
+  return v + (size_t)rows * (size_t)m * ((size_t)1 << lognb) * sizeof(float);
+}
+
 size_t bfly_kron_forward_wide_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
   int l = 0;
   if (rows < 0 || !kron_wide_sizes(m, nb, &l)) return 0;
-  return (size_t)rows * (size_t)m * (size_t)nb * sizeof(float);
+  return kron_wide_parts(rows, m, l, nullptr);
 }
 
 bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
@@ -333,48 +402,38 @@ bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly
   const bfly_status sn = check_n(nb, 13, &l);
   if (sn != BFLY_OK) return sn;
   if (!kron_wide_sizes(m, nb, &l)) return BFLY_ERR_UNSUPPORTED;
-  if (quant) {
-    const bfly_status sq = check_quant(codes, scales, zeros, rows, (int64_t)m * nb, nb, l, bits,
-                                       group, mode);
-    if (sq != BFLY_OK) return sq;
-  }
-  if (workspace_bytes < bfly_kron_forward_wide_workspace_bytes(rows, m, nb))
-    return BFLY_ERR_WORKSPACE;
-  if (!aligned(x, 16) || (y && !aligned(y, 16)) || !aligned(workspace, 16) || !aligned(mix, 4) ||
-      (coeffs_b && !aligned(coeffs_b, 16)) || (theta_b && !aligned(theta_b, 4)))
-    return BFLY_ERR_ALIGN;
-  if (rows == 0) return BFLY_OK;
+  size_t o_v = 0;
+  if (workspace_bytes < kron_wide_parts(rows, m, l, &o_v)) return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(workspace, 16) || !aligned(mix, 4)) return BFLY_ERR_ALIGN;
   // v = (O kron I) x into the workspace, then the butterfly (and the
-  // quantizer) on its rows * m segments: (O kron B) = (I kron B)(O kron I)
-  float* v = static_cast<float*>(workspace);
-  const hipError_t e = bfly::launch_kron_mix(x, x_dt == BFLY_BF16, v, mix, rows, m, nb,
-                                             (hipStream_t)hip_stream);
+  // quantizer) on its rows * m segments: (O kron B) = (I kron B)(O kron I).
+  // The second pass is validated in full before the first is enqueued.
+  char* ws = static_cast<char*>(workspace);
+  float* v = reinterpret_cast<float*>(ws + o_v);
+  bfly::FwdParams p;
+  const bfly_status st = forward_args(v, BFLY_F32, y, y_dt, codes, scales, zeros, rows * m, 1, nb,
+                                      theta_b, coeffs_b, nullptr, bits, group, mode, quant, ws,
+                                      o_v, &p);
+  if (st != BFLY_OK) return st;
+  if (rows == 0) return BFLY_OK;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  const hipError_t e = bfly::launch_kron_mix(x, x_dt == BFLY_BF16, v, mix, rows, m, nb, s);
   if (e != hipSuccess) return hip_fail(e);
-  return forward_common(v, BFLY_F32, y, y_dt, codes, scales, zeros, rows * m, 1, nb, theta_b,
-                        coeffs_b, nullptr, bits, group, mode, quant, hip_stream);
+  return forward_run(p, theta_b, coeffs_b, ws, s);
 }
 
-// Workspace of the Kronecker backward: O^T, a zero angle set and its
-// (identity) table, then the butterfly backward's own workspace for the
-// rows * m segments.
-static size_t kron_bwd_parts(int64_t rows, int32_t m, int lognb, size_t* off_theta0,
-                             size_t* off_table, size_t* off_bwd) {
-  const int nb = 1 << lognb;
-  const size_t t0 = 256;
-  const size_t tab = align_up(t0 + sizeof(float) * (size_t)lognb * (nb / 2), 256);
-  const size_t bwd = align_up(tab + coeff_bytes_l(lognb), 256);
-  const size_t total = bwd + bfly_backward_workspace_bytes(rows * m, nb);
-  if (off_theta0) *off_theta0 = t0;
-  if (off_table) *off_table = tab;
+// Workspace of the Kronecker backward: O^T, then the butterfly backward's
+// own workspace for the rows * m segments.
+static size_t kron_bwd_parts(int64_t rows, int32_t m, int lognb, size_t* off_bwd) {
+  const size_t bwd = align_up(sizeof(float) * (size_t)m * (size_t)m, 256);
   if (off_bwd) *off_bwd = bwd;
-  return total;
+  return bwd + bfly_backward_workspace_bytes(rows * m, 1 << lognb);
 }
 
 size_t bfly_kron_backward_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
   int l = 0;
-  if (rows < 0 || m < 2 || m > 8 || check_n(nb, 12, &l) != BFLY_OK) return 0;
-  if (!bfly::forward_supported(l, m)) return 0;
-  return kron_bwd_parts(rows, m, l, nullptr, nullptr, nullptr);
+  if (rows < 0 || !kron_wide_sizes(m, nb, &l)) return 0;
+  return kron_bwd_parts(rows, m, l, nullptr);
 }
 
 bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float* dtheta_b,
@@ -384,14 +443,14 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   if ((rows > 0 && (!x || !g || !dx)) || !dtheta_b || !mix || !workspace) return BFLY_ERR_NULL;
   if (!theta_b && !coeffs_b) return BFLY_ERR_NULL;
   if (rows < 0) return BFLY_ERR_SIZE;
-  if (m < 1 || m > 8) return BFLY_ERR_SIZE;
+  if (m < 1 || m > 64) return BFLY_ERR_SIZE;
   int l = 0;
   const bfly_status st = check_n(nb, 12, &l);
   if (st != BFLY_OK) return st;
-  if (m == 1 || !bfly::forward_supported(l, m)) return BFLY_ERR_UNSUPPORTED;
-  size_t o_th0 = 0, o_tab = 0, o_bwd = 0;
-  if (workspace_bytes < kron_bwd_parts(rows, m, l, &o_th0, &o_tab, &o_bwd))
-    return BFLY_ERR_WORKSPACE;
+  // m = 1 is the plain butterfly (bfly_backward)
+  if (m == 1 || !kron_wide_sizes(m, nb, &l)) return BFLY_ERR_UNSUPPORTED;
+  size_t o_bwd = 0;
+  if (workspace_bytes < kron_bwd_parts(rows, m, l, &o_bwd)) return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(dx, 16) || !aligned(workspace, 16) ||
       !aligned(dtheta_b, 4) || !aligned(mix, 4) || (coeffs_b && !aligned(coeffs_b, 16)) ||
       (theta_b && !aligned(theta_b, 4)))
@@ -399,10 +458,7 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   const hipStream_t s = (hipStream_t)hip_stream;
   char* ws = static_cast<char*>(workspace);
   float* mix_t = reinterpret_cast<float*>(ws);
-  float* theta0 = reinterpret_cast<float*>(ws + o_th0);
-  // O^T into the workspace (the zero-angle and table regions that follow it
-  // are no longer used; the layout keeps the size the query reports)
-  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, theta0, 0, s);
+  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, s);  // O^T
   if (e != hipSuccess) return hip_fail(e);
   if (rows > 0) {
     // dL/dz = (O^T kron I) G: the mixing step with O^T (each thread reads all
@@ -471,7 +527,8 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
   hipError_t e = bfly::launch_prepare(theta, wsb, l, s);
   if (e != hipSuccess) return hip_fail(e);
   // Y = Q X for the loss statistics
-  const bfly_status st = bfly_forward(x, BFLY_F32, y, BFLY_F32, rows, n, nullptr, wsb, hip_stream);
+  const bfly_status st =
+      bfly_forward(x, BFLY_F32, y, BFLY_F32, rows, n, nullptr, wsb, nullptr, 0, hip_stream);
   if (st != BFLY_OK) return st;
   bfly::CalibLossParams p;
   p.y = y;

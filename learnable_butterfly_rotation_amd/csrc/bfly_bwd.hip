@@ -498,8 +498,9 @@ template <int LOGN, bool CALIB = false>
 static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t s,
                                   const CalibGradArgs& c = CalibGradArgs{}) {
   using S = BwdShape<LOGN>;
-  static hipError_t lds_ok =
-      allow_lds(reinterpret_cast<const void*>(bwd_kernel<LOGN, CALIB>), S::LDS_BYTES);
+  const hipError_t lds_ok =
+      kernel_setup(reinterpret_cast<const void*>(bwd_kernel<LOGN, CALIB>), S::NT, S::LDS_BYTES,
+                   nullptr, nullptr);
   if (lds_ok != hipSuccess) return lds_ok;
   if (p.nblk > 0) {
     hipLaunchKernelGGL((bwd_kernel<LOGN, CALIB>), dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p, c);

@@ -808,6 +808,11 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
 #pragma unroll
     for (int w = 0; w < NW; ++w) seen |= nan_wave[w];
     usable = __builtin_amdgcn_readfirstlane(seen) == 0;
+    // An unusable form leaves the first group's results unstored: the
+    // epilogue below then writes an empty range, so nothing reaches memory
+    // before the fallback loop re-reads that group's input (which an
+    // in-place call shares with the output).
+    if (!usable) held_grp = -1;
   }
   const int64_t nrun = usable ? ngrp : 0;
   for (; g0 + (PD - 1) * G < nrun; g0 += PD * G) {
@@ -909,21 +914,10 @@ template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM>
 hipError_t launch_fwd_variant(const FwdParams& p, hipStream_t stream) {
   using S = FwdShape<LOGNB, M, RPT>;
   auto kern = fwd_kernel<LOGNB, M, RPT, XBF16, YK, QM>;
-  static int blocks_per_cu = -1;
-  static int num_cu = 0;
-  if (blocks_per_cu < 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = allow_lds(reinterpret_cast<const void*>(kern), S::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    int bpc = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, kern, S::NT, S::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    blocks_per_cu = bpc > 0 ? bpc : 1;
-  }
+  int blocks_per_cu = 0, num_cu = 0;
+  const hipError_t e =
+      kernel_setup(reinterpret_cast<const void*>(kern), S::NT, S::LDS_BYTES, &blocks_per_cu, &num_cu);
+  if (e != hipSuccess) return e;
   const int64_t ngrp = (p.rows + S::ROWS_PER_PASS - 1) / S::ROWS_PER_PASS;
   const int64_t cap = (int64_t)blocks_per_cu * num_cu;
   const int grid = (int)(ngrp < cap ? ngrp : cap);

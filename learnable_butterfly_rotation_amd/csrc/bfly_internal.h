@@ -55,7 +55,7 @@ struct Table {
   const float* eps;
 };
 
-__host__ __device__ inline size_t table_bytes(int logn) {
+__host__ __device__ constexpr size_t table_bytes(int logn) {
   const size_t half = (size_t)1 << (logn - 1);
   return half * 8 * (size_t)(3 * logn + 2) + half * 4 * (size_t)(logn - 1);
 }
@@ -208,6 +208,14 @@ hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s);
 
 // Whether a forward instantiation exists for (lognb, m); validation uses it.
 bool forward_supported(int lognb, int m);
+
+// Launch facts of one kernel on the current device: its dynamic-LDS limit
+// raised to lds_bytes (when above the 64 KiB default), how many of its
+// workgroups of `threads` threads one CU holds at once (per_cu >= 1) and the
+// device's CU count.  Worked out once per (kernel, device) under a lock and
+// cached; thread-safe.  Either output pointer may be NULL.
+hipError_t kernel_setup(const void* kernel, int threads, size_t lds_bytes, int* per_cu,
+                        int* num_cu);
 
 // Grid size of the backward: a function of (rows, logn) only, so that the
 // angle-gradient summation order never depends on the device.

@@ -220,15 +220,10 @@ __global__ __launch_bounds__(256) void kron_mix_mfma_kernel(const KronMixParams 
 template <int MT, int KS>
 hipError_t launch_mfma(const KronMixParams& p, hipStream_t s) {
   auto kern = kron_mix_mfma_kernel<MT, KS>;
-  static int cap = 0;  // resident workgroups on the device (first use)
-  if (cap == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
-    if (e != hipSuccess) return e;
-    cap = (per_cu > 0 ? per_cu : 1) * cus;
-  }
+  int cus = 0, per_cu = 0;  // resident workgroups on the device
+  const hipError_t e = kernel_setup(reinterpret_cast<const void*>(kern), 256, 0, &per_cu, &cus);
+  if (e != hipSuccess) return e;
+  const int cap = per_cu * cus;
   const int64_t items = p.rows * (p.nb / 64);
   const int64_t want = (items + 3) / 4;
   const int blocks = (int)(want < cap ? want : cap);

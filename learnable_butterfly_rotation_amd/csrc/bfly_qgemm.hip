@@ -476,7 +476,7 @@ hipError_t launch_one(const QgemmParams& p, hipStream_t s) {
   constexpr int BM = QG_BM;
   using T = QTile<BM>;
   const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BM, BITS, ASYM, YBF16>);
-  static const hipError_t lds_ok = allow_lds(fn, T::LDS);
+  const hipError_t lds_ok = kernel_setup(fn, T::THREADS, T::LDS, nullptr, nullptr);
   if (lds_ok != hipSuccess) return lds_ok;
   const int64_t mt = (p.rows + BM - 1) / BM;
   const int64_t blocks = mt * (p.n_out / QG_BN);

@@ -73,8 +73,10 @@ def test_sizes(L):
     assert B.bfly_backward_workspace_bytes(100, 8192) == 0
 
 
-def fwd(L, x=X, xd=0, y=Y, yd=0, rows=4, n=256, th=TH, co=None):
-    return L.bfly_forward(x, xd, y, yd, rows, n, th, co, None)
+def fwd(L, x=X, xd=0, y=Y, yd=0, rows=4, n=256, th=TH, co=None, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = B.bfly_coeff_bytes(n)
+    return L.bfly_forward(x, xd, y, yd, rows, n, th, co, ws, wsb, None)
 
 
 def test_forward_validation(L):
@@ -95,10 +97,20 @@ def test_forward_validation(L):
     assert fwd(L, x=ctypes.c_void_p(0x10008)) == ALIGN
     assert fwd(L, y=ctypes.c_void_p(0x20004)) == ALIGN
     assert fwd(L, co=ctypes.c_void_p(0x90008), rows=0) == ALIGN
+    # angles without a table: the table goes into the caller's workspace
+    assert fwd(L, rows=0, ws=None) == NULL
+    assert fwd(L, rows=0, wsb=B.bfly_coeff_bytes(256) - 1) == WORKSPACE
+    assert fwd(L, rows=0, ws=ctypes.c_void_p(0x80008)) == ALIGN
+    # with a table the workspace is not used
+    assert fwd(L, rows=0, th=None, co=CO, ws=None, wsb=0) == OK
+    assert fwd(L, rows=0, co=CO, ws=None, wsb=0) == OK
 
 
-def fq(L, y=Y, c=C, s=S, z=None, bits=4, group=128, mode=0, n=4096, rows=0):
-    return L.bfly_forward_quant(X, 1, y, 1, c, s, z, rows, n, TH, None, bits, group, mode, None)
+def fq(L, y=Y, c=C, s=S, z=None, bits=4, group=128, mode=0, n=4096, rows=0, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = B.bfly_coeff_bytes(n)
+    return L.bfly_forward_quant(X, 1, y, 1, c, s, z, rows, n, TH, None, bits, group, mode, ws, wsb,
+                                None)
 
 
 def test_forward_quant_validation(L):
@@ -121,10 +133,18 @@ def test_forward_quant_validation(L):
         assert fq(L, group=g) == OK
     assert fq(L, c=ctypes.c_void_p(0x30004)) == ALIGN
     assert fq(L, s=ctypes.c_void_p(0x40001)) == ALIGN
+    assert fq(L, ws=None) == NULL
+    assert fq(L, wsb=B.bfly_coeff_bytes(4096) - 1) == WORKSPACE
+    assert fq(L, ws=ctypes.c_void_p(0x80004)) == ALIGN
 
 
-def kf(L, m=5, nb=1024, c=C, s=S, z=None, mix=MIX, group=128, rows=0):
-    return L.bfly_kron_forward(X, 1, Y, 1, c, s, z, rows, m, nb, TH, None, mix, 4, group, 0, None)
+
+
+def kf(L, m=5, nb=1024, c=C, s=S, z=None, mix=MIX, group=128, rows=0, ws=WS, wsb=None, co=None):
+    if wsb is None:
+        wsb = B.bfly_coeff_bytes(nb)
+    return L.bfly_kron_forward(X, 1, Y, 1, c, s, z, rows, m, nb, TH, co, mix, 4, group, 0, ws, wsb,
+                               None)
 
 
 def test_kron_validation(L):
@@ -141,6 +161,9 @@ def test_kron_validation(L):
     assert kf(L, m=5, nb=256, group=512) == QUANT     # group must divide nb
     for m in range(2, 9):
         assert kf(L, m=m, nb=512) == OK
+    assert kf(L, ws=None) == NULL
+    assert kf(L, wsb=B.bfly_coeff_bytes(1024) - 1) == WORKSPACE
+    assert kf(L, ws=None, wsb=0, co=CO) == OK
 
 
 def bw(L, x=X, g=X, y=None, dx=Y, dth=C, rows=16, n=4096, th=TH, ws=WS, wsb=None):
@@ -220,8 +243,10 @@ def kb(L, x=X, g=X, dx=Y, dth=C, rows=16, m=5, nb=1024, th=TH, co=None, mix=MIX,
 def test_kron_backward_validation(L):
     assert B.bfly_kron_backward_workspace_bytes(16, 5, 1024) > B.bfly_backward_workspace_bytes(80, 1024)
     assert B.bfly_kron_backward_workspace_bytes(16, 1, 1024) == 0
-    assert B.bfly_kron_backward_workspace_bytes(16, 9, 256) == 0
+    assert B.bfly_kron_backward_workspace_bytes(16, 65, 256) == 0
     assert B.bfly_kron_backward_workspace_bytes(16, 5, 8192) == 0
+    assert B.bfly_kron_backward_workspace_bytes(16, 32, 4096) == 0         # m * nb > 65536
+    assert B.bfly_kron_backward_workspace_bytes(16, 43, 256) > B.bfly_backward_workspace_bytes(16 * 43, 256)
     assert kb(L, x=None) == NULL
     assert kb(L, mix=None) == NULL
     assert kb(L, dth=None) == NULL
@@ -229,10 +254,15 @@ def test_kron_backward_validation(L):
     assert kb(L, ws=None) == NULL
     assert kb(L, rows=-1, wsb=1 << 30) == SIZE
     assert kb(L, m=0, wsb=1 << 30) == SIZE
-    assert kb(L, m=9, wsb=1 << 30) == SIZE
+    assert kb(L, m=65, wsb=1 << 30) == SIZE
     assert kb(L, nb=1000, wsb=1 << 30) == SIZE
     assert kb(L, m=1, wsb=1 << 30) == UNSUPPORTED
-    assert kb(L, m=3, nb=4096, wsb=1 << 30) == UNSUPPORTED   # m * nb > 8192
+    assert kb(L, m=32, nb=4096, wsb=1 << 30) == UNSUPPORTED  # m * nb > 65536
+    assert kb(L, nb=128, wsb=1 << 30) == UNSUPPORTED
+    # wide composites pass the size checks (and reach the workspace check,
+    # the last before any HIP call)
+    assert kb(L, m=43, nb=256, wsb=B.bfly_kron_backward_workspace_bytes(16, 43, 256) - 1) == WORKSPACE
+    assert kb(L, m=9, nb=512, wsb=B.bfly_kron_backward_workspace_bytes(16, 9, 512) - 1) == WORKSPACE
     assert kb(L, wsb=B.bfly_kron_backward_workspace_bytes(16, 5, 1024) - 1) == WORKSPACE
     assert kb(L, dx=ctypes.c_void_p(0x20008)) == ALIGN
     assert kb(L, ws=ctypes.c_void_p(0x80008)) == ALIGN
@@ -247,7 +277,8 @@ def kw(L, x=X, y=Y, c=C, s=S, z=None, rows=16, m=43, nb=256, th=TH, co=None, mix
 
 
 def test_kron_forward_wide_validation(L):
-    assert B.bfly_kron_forward_wide_workspace_bytes(16, 43, 256) == 16 * 11008 * 4
+    tab = (B.bfly_coeff_bytes(256) + 255) // 256 * 256
+    assert B.bfly_kron_forward_wide_workspace_bytes(16, 43, 256) == tab + 16 * 11008 * 4
     assert B.bfly_kron_forward_wide_workspace_bytes(16, 65, 256) == 0
     assert B.bfly_kron_forward_wide_workspace_bytes(16, 43, 128) == 0
     assert B.bfly_kron_forward_wide_workspace_bytes(16, 32, 4096) == 0    # m * nb > 65536
@@ -263,7 +294,7 @@ def test_kron_forward_wide_validation(L):
     assert kw(L, nb=300, wsb=1 << 30) == SIZE
     assert kw(L, nb=128, wsb=1 << 30) == UNSUPPORTED
     assert kw(L, group=512) == QUANT                   # group must divide nb
-    assert kw(L, wsb=16 * 11008 * 4 - 1) == WORKSPACE
+    assert kw(L, wsb=tab + 16 * 11008 * 4 - 1) == WORKSPACE
     assert kw(L, ws=ctypes.c_void_p(0x80008)) == ALIGN
 
 
