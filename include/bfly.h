@@ -29,6 +29,7 @@
  *   bfly_calib_step                              one step of learning the angles
  *   bfly_quant_matmul                            y = (Q x)(W Q^T)^T from the codes
  *   bfly_*_bytes, bfly_status_string, bfly_last_hip_error
+ *   bfly_forward_quant_noalloc                   bfly_forward_quant with a fixed scratch
  *   bfly_time_next_forward                       kernel-only timing of the next forward
  *
  * Extensions beyond the four calls the pages' problem statement gives
@@ -52,7 +53,8 @@
  *     workspace_bytes >= bfly_coeff_bytes(n) (16-byte aligned), the other
  *     calls size their workspace with their own *_workspace_bytes query.
  *   - The library allocates no memory in any call: every buffer, scratch
- *     included, comes from the caller.  Its only state is a fixed-size
+ *     included, comes from the caller (bfly_forward_quant_noalloc uses a
+ *     fixed array of the library instead).  Its only state is a fixed-size
  *     per-device cache of launch facts (CU count, resident workgroups per
  *     kernel; filled on first use under a lock), the armed events of
  *     bfly_time_next_forward and the per-thread last HIP error.
@@ -169,6 +171,22 @@ bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dty
                                int64_t rows, int32_t n, const float* theta, const void* coeffs,
                                int32_t bits, int32_t group, bfly_qmode mode, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
+
+/* bfly_forward_quant for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation from theta, with the coefficient table
+ * prepared into a fixed scratch array inside the library instead of a
+ * caller workspace.  Each device the library runs on holds one such array
+ * (713 KiB: the table of n = 4096) until the process ends; every call on a
+ * device shares it, so calls that overlap on one device (two streams, two
+ * threads) race on it and must be serialised by the caller.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Arguments and errors as bfly_forward_quant with theta required (there is
+ * no coeffs); n above 4096 returns BFLY_ERR_UNSUPPORTED. */
+bfly_status bfly_forward_quant_noalloc(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                       uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                       int64_t rows, int32_t n, const float* theta, int32_t bits,
+                                       int32_t group, bfly_qmode mode, void* hip_stream);
 
 /* Kronecker composite for widths n = m * nb that are not a power of two
  * (duidaima.com write-up, section "butterfly": LLaMA-2-13B's 5120):

@@ -22,7 +22,7 @@ __all__ = [
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
     "bfly_kron_backward_workspace_bytes", "bfly_calib_config", "bfly_calib_step",
     "bfly_calib_workspace_bytes", "bfly_status_string",
-    "bfly_last_hip_error", "bfly_time_next_forward",
+    "bfly_last_hip_error", "bfly_time_next_forward", "bfly_forward_quant_noalloc",
 ]
 
 BFLY_F32 = 0
@@ -65,6 +65,8 @@ def lib():
                                    vp]
         L.bfly_forward_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
                                          vp, vp, i32, i32, ctypes.c_int, vp, sz, vp]
+        L.bfly_forward_quant_noalloc.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp,
+                                                 i64, i32, vp, i32, i32, ctypes.c_int, vp]
         L.bfly_kron_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64, i32,
                                         i32, vp, vp, vp, i32, i32, ctypes.c_int, vp, sz, vp]
         L.bfly_kron_forward_wide.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, i64,
@@ -89,6 +91,7 @@ def lib():
         L.bfly_last_hip_error.restype = i32
         L.bfly_time_next_forward.argtypes = [vp, vp]
         for f in (L.bfly_prepare, L.bfly_prepare_hadamard, L.bfly_forward, L.bfly_forward_quant,
+                  L.bfly_forward_quant_noalloc,
                   L.bfly_kron_forward, L.bfly_kron_forward_wide, L.bfly_quant_matmul,
                   L.bfly_backward,
                   L.bfly_kron_backward, L.bfly_calib_step, L.bfly_time_next_forward):
@@ -192,6 +195,18 @@ def bfly_forward_quant(x, y, codes, scales, zeros=None, theta=None, coeffs=None,
                                     _ptr(coeffs), bits, group, mode, _ptr(ws), _nbytes(ws),
                                     _stream(stream)),
            "bfly_forward_quant")
+
+
+def bfly_forward_quant_noalloc(x, y, codes, scales, zeros=None, theta=None, bits=4, group=128,
+                               mode=BFLY_SYM_ABSMAX, stream=None) -> None:
+    """bfly_forward_quant from angles, its table in the library's fixed
+    per-device scratch (no allocation; overlapping calls on one device race)."""
+    rows, n = x.shape
+    _check(lib().bfly_forward_quant_noalloc(_ptr(x), _dt(x), _ptr(y),
+                                            _dt(y) if y is not None else 0, _ptr(codes),
+                                            _ptr(scales), _ptr(zeros), rows, n, _ptr(theta), bits,
+                                            group, mode, _stream(stream)),
+           "bfly_forward_quant_noalloc")
 
 
 def bfly_kron_forward(x, y, mix, codes=None, scales=None, zeros=None, theta_b=None, coeffs_b=None,

@@ -174,6 +174,35 @@ bfly_status check_quant(const uint8_t* codes, const uint16_t* scales, const uint
 
 }  // namespace
 
+// The fixed scratch of bfly_forward_quant_noalloc: room for the coefficient
+// table of the longest butterfly the forward handles.  Every device the
+// library runs on holds its own copy until the process ends.
+constexpr int kScratchMaxLogN = 12;
+constexpr size_t kScratchBytes = (bfly::table_bytes(kScratchMaxLogN) + 255) / 256 * 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// scratch's device address, looked up once per device with that device
+// current (the host-side name is only a stand-in for it).
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 extern "C" {
 
 size_t bfly_coeff_bytes(int32_t n) {
@@ -605,6 +634,26 @@ bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* cod
   p.y_bf16 = y_dt == BFLY_BF16;
   const hipError_t e = bfly::launch_qgemm(p, (hipStream_t)hip_stream);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+bfly_status bfly_forward_quant_noalloc(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                       uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                       int64_t rows, int32_t n, const float* theta, int32_t bits,
+                                       int32_t group, bfly_qmode mode, void* hip_stream) {
+  if (!theta) return BFLY_ERR_NULL;
+  // Validated as bfly_forward_quant with a workspace of the scratch's size;
+  // the placeholder pointer is never dereferenced.
+  bfly::FwdParams p;
+  const bfly_status st =
+      forward_args(x, x_dt, y, y_dt, codes, scales, zeros, rows, 1, n, theta, nullptr, nullptr,
+                   bits, group, mode, true, reinterpret_cast<const void*>(uintptr_t(256)),
+                   kScratchBytes, &p);
+  if (st != BFLY_OK) return st;
+  if (rows == 0) return BFLY_OK;
+  void* table = nullptr;
+  const hipError_t e = scratch_address(&table);
+  if (e != hipSuccess) return hip_fail(e);
+  return forward_run(p, theta, nullptr, table, (hipStream_t)hip_stream);
 }
 
 const char* bfly_status_string(bfly_status s) {

@@ -138,6 +138,26 @@ def test_forward_quant_validation(L):
     assert fq(L, ws=ctypes.c_void_p(0x80004)) == ALIGN
 
 
+def test_forward_quant_noalloc_validation(L):
+    # validated like bfly_forward_quant (its scratch replaces the workspace);
+    # rows == 0 returns before any HIP call
+    def nq(y=Y, c=C, s=S, z=None, bits=4, group=128, mode=0, n=4096, rows=0, th=TH):
+        return L.bfly_forward_quant_noalloc(X, 1, y, 1, c, s, z, rows, n, th, bits, group, mode,
+                                            None)
+    assert nq() == OK
+    assert nq(y=None) == OK
+    assert nq(th=None) == NULL
+    assert nq(c=None, rows=1) == NULL
+    assert nq(bits=3) == QUANT
+    assert nq(mode=1, rows=1) == QUANT
+    assert nq(mode=1, z=Z) == OK
+    assert nq(n=100) == SIZE
+    assert nq(n=32) == UNSUPPORTED
+    assert nq(n=8192) == UNSUPPORTED
+    assert nq(rows=-1) == SIZE
+    assert nq(c=ctypes.c_void_p(0x30004)) == ALIGN
+    for n in (64, 128, 256, 512, 1024, 2048, 4096):
+        assert nq(n=n, group=min(128, n)) == OK
 
 
 def kf(L, m=5, nb=1024, c=C, s=S, z=None, mix=MIX, group=128, rows=0, ws=WS, wsb=None, co=None):
