@@ -49,7 +49,10 @@ struct FwdShape {
   // Row groups whose input is in flight ahead of the one being computed
   // (each slot holds SEGS segments of the input in registers).  Measured at
   // n = 4096: two slots of one segment beat one (the load of the next group
-  // is issued a full group earlier) and three (more registers, no gain).
+  // is issued a full group earlier) and three (more registers, no gain); with
+  // two segments (two rows per thread) one slot beats two and three (more
+  // requests in flight lower the streaming rate), and three or four rows per
+  // thread are slower than two.
   static constexpr int PD = SEGS == 1 ? 2 : 1;
   static constexpr int BUFW = R * SEGS * SEGW;     // words per LDS buffer
   // LDS addressing of the transpose into phase k (see LdsMode).
@@ -477,10 +480,6 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
       }
   };
 
-  // A 1 x 1 Kronecker factor, read once (no memory operation in the loop
-  // body may sit under a branch).
-  const bool has_mix1 = M == 1 && P.mix != nullptr;
-  const float mix1 = has_mix1 ? P.mix[0] : 1.0f;
   // The M x M factor, read once into scalar registers (uniform values; the
   // compiler cannot prove the matrix unaliased by the outputs, and would
   // otherwise reload it into vector registers for every row group).
@@ -579,12 +578,6 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // Everything the previous group still needs before its stores: the
   // Kronecker mix, bf16 packing and quantization.
   auto finish = [&](float (&w)[SEGS][E]) {
-    if (M == 1 && has_mix1) {  // a 1 x 1 Kronecker factor: a scalar
-#pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg)
-#pragma unroll
-        for (int e = 0; e < E; ++e) w[sg][e] *= mix1;
-    }
     if (M > 1) {  // Kronecker mix across a row's segments, column by column
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr)
@@ -898,12 +891,30 @@ fwd_kernel(FwdParams P) {
                          fwd_elem_a(t, 0, S::PL));  // the scaled form's layout A
   load_fast(P.tab.fgt);
   __builtin_amdgcn_sched_barrier(0);
+  // A 1 x 1 Kronecker factor scales the last stage's coefficients (a scalar
+  // read once; no branch in the row loop).
+  const float mix1 = (M == 1 && P.mix != nullptr)
+                         ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.mix[0])))
+                         : 1.0f;
+  auto scale_last = [&]() {
+    if (M == 1) {
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j) {
+        C.last[j].x *= mix1;
+        C.last[j].y *= mix1;
+        C.last[j].z *= mix1;
+        C.last[j].w *= mix1;
+      }
+    }
+  };
+  scale_last();
   // The two forms run as consecutive loops, not as two arms of a branch:
   // the register allocator then never holds both coefficient sets at once.
   const bool usable = row_loop<S, XBF16, YK, QM, true, true, true>(P, P.rows, lds, team, t, C, in);
   if (!usable) {
     // Three-shear form, with the general quantizer for every format.
     load_coeffs(P.tab.lift, P.tab.last);
+    scale_last();
     row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false, false>(P, P.rows, lds, team, t, C, in);
   }
 }
