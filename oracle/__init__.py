@@ -22,6 +22,12 @@ Each function cites the passage of the pages it follows:
   learning the angles): dL/dz = (O^T kron I) G in fp64, then the butterfly
   backward on the rows * m segments.  The C backward reads its G in fp32,
   so dL/dz is rounded to fp32 first (2^-24 relative).
+* calib_weight_loss_grad / calib_weight_step -- the same step with the
+  layer's output as the reconstruction target (duidaima.com section
+  "training and results"; ButterflyQuant abstract: computational invariance
+  and 2-bit weights): numpy fp64 products of the rotated, quantized layer,
+  the chain rule through both rotations with the quantizer's rounding
+  passed straight through, and the C backward for each branch.
 * calib_loss_grad / adam / calib_step -- one calibration step for the
   angles (duidaima.com section "training and results": a reconstruction
   loss plus the KL divergence between the rotated activations' distribution
@@ -331,7 +337,8 @@ def _group_absmax(y: np.ndarray, group: int) -> np.ndarray:
     return np.repeat(a, group, axis=1)
 
 
-def calib_loss_grad(y: np.ndarray, bits: int, group: int, bins: int, lambda_kl: float):
+def calib_loss_grad(y: np.ndarray, bits: int, group: int, bins: int, lambda_kl: float,
+                    with_rec: bool = True):
     """Loss and dL/dy of one calibration step at Y (fp64 [rows][n]).
 
     Readings: the reconstruction term is the group quantizer's error,
@@ -342,6 +349,8 @@ def calib_loss_grad(y: np.ndarray, bits: int, group: int, bins: int, lambda_kl: 
     c_b = -1 + (b + 1/2) h, h = 2 / bins, each u giving linear-interpolation
     weights to its two nearest centres (u clamped to [c_0, c_{bins-1}];
     a clamped u has no gradient), p' = (p + 1e-6) / (1 + bins 1e-6).
+    with_rec=False leaves the reconstruction term out of loss and g (the
+    uniformity term alone, for the weight-side loss below).
     Returns dict(loss, rec, kl, g, t) with t = (u - c_0) / h (unclamped)."""
     y = np.asarray(y, dtype=np.float64)
     N = y.size
@@ -361,11 +370,11 @@ def calib_loss_grad(y: np.ndarray, bits: int, group: int, bins: int, lambda_kl: 
     ps = (p + CALIB_SMOOTH) / (1 + bins * CALIB_SMOOTH)
     lb = np.log(bins * ps)
     kl = float((ps * lb).sum())
-    g = 2.0 * (y - yhat) / N
+    g = 2.0 * (y - yhat) / N if with_rec else np.zeros_like(y)
     dkl = (lb[j + 1] - lb[j]) / (h * N * (1 + bins * CALIB_SMOOTH))
     g += lambda_kl * np.where(inside & (a > 0), dkl / np.where(a > 0, a, 1.0), 0.0)
-    return {"loss": rec + lambda_kl * kl, "rec": rec, "kl": kl, "g": g, "t": t, "p": p,
-            "yhat": yhat, "a": a}
+    return {"loss": (rec if with_rec else 0.0) + lambda_kl * kl, "rec": rec, "kl": kl, "g": g,
+            "t": t, "p": p, "yhat": yhat, "a": a}
 
 
 def adam(theta, m, v, g, step: int, lr: float, beta1: float, beta2: float, eps: float):
@@ -385,3 +394,62 @@ def calib_step(x, theta, m, v, step, bits, group, bins, lambda_kl, lr, beta1, be
     bw = backward(x, lg["g"].astype(np.float32), theta, want_y=False, want_dx=False)
     th2, m2, v2 = adam(theta, m, v, bw["dtheta"], step, lr, beta1, beta2, eps)
     return dict(lg, y=y, dtheta=bw["dtheta"], dabs=bw["dabs"], theta=th2, m=m2, v=v2)
+
+
+def calib_weight_loss_grad(x, w, theta, bits: int, group: int, mode: int, bins: int,
+                           lambda_kl: float, wq=None):
+    """Loss and dL/dtheta of one calibration step whose reconstruction term is
+    the layer's output (duidaima.com write-up, section "training and
+    results": the quantized model's output should match the original one;
+    ButterflyQuant abstract: computational invariance W x = (W Q^T)(Q x) and
+    2-bit weights).  fp64 throughout (x, w: float32 or bf16 bits).
+
+    Readings:
+      Xr = Q X (each row of X rotated), Wr = W Q^T (each row of W rotated),
+      What = the group quantizer's value of Wr (bits, group, mode; or the
+             codes, scales, zeros given as wq = (codes, scales, zeros)),
+      Y = X W^T,  Yhat = Xr What^T,
+      L_rec = sum (Yhat - Y)^2 / (rows * out),
+      L = L_rec + lambda KL(Xr), the uniformity term of calib_loss_grad on Xr.
+    The quantizer's rounding passes gradients straight through (What - Wr is
+    held constant), so by the chain rule
+      dL/dYhat = 2 (Yhat - Y) / (rows * out),
+      dL/dXr = dL/dYhat What,   dL/dWr = dL/dYhat^T Xr,
+    and dtheta is the butterfly backward of X with dL/dXr (plus the uniformity
+    term's dL/dXr) added to the backward of W's rows with dL/dWr.
+    Returns dict(loss, rec, kl, dtheta, dabs, gx, gw, r, e, xr, wr, what)."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    n = x.shape[1]
+    xr = forward(x, theta)
+    wr = forward(w, theta)
+    if wq is None:
+        q = quantize(wr, bits, group, mode)
+        wq = (q["codes"], q["scales"], q.get("zeros"))
+    what = dequantize(wq[0], wq[1], wq[2], bits, group, mode, n)
+    y = widen(x) @ widen(w).T
+    yhat = xr @ what.T
+    r = yhat - y
+    n_rec = r.size
+    rec = float((r * r).sum() / n_rec)
+    kl = calib_loss_grad(xr, 4, group, bins, lambda_kl, with_rec=False)
+    dyhat = 2.0 * r / n_rec
+    gx = dyhat @ what + kl["g"]
+    gw = dyhat.T @ xr
+    bx = backward(widen(x).astype(np.float32), gx.astype(np.float32), theta, want_y=False,
+                  want_dx=False)
+    bw = backward(widen(w).astype(np.float32), gw.astype(np.float32), theta, want_y=False,
+                  want_dx=False)
+    return {"loss": rec + lambda_kl * kl["kl"], "rec": rec, "kl": kl["kl"],
+            "dtheta": bx["dtheta"] + bw["dtheta"], "dabs": bx["dabs"] + bw["dabs"],
+            "gx": gx, "gw": gw, "r": r, "e": what - wr, "xr": xr, "wr": wr, "what": what,
+            "p": kl["p"], "a": kl["a"], "t": kl["t"]}
+
+
+def calib_weight_step(x, w, theta, m, v, step, bits, group, mode, bins, lambda_kl, lr, beta1,
+                      beta2, eps, wq=None):
+    """One calibration step with the layer-output loss: calib_weight_loss_grad,
+    then one Adam update of theta."""
+    out = calib_weight_loss_grad(x, w, theta, bits, group, mode, bins, lambda_kl, wq)
+    th2, m2, v2 = adam(theta, m, v, out["dtheta"], step, lr, beta1, beta2, eps)
+    return dict(out, theta=th2, m=m2, v=v2)

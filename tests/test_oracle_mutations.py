@@ -75,6 +75,12 @@ MUTATIONS = [
      "return np.where(parity == 1, 1.0, -1.0) / np.sqrt(float(n))"),
     ("Kronecker backward mixes with O, not its transpose", "__init__.py",
      'gz = np.einsum("ab,rai->rbi", mix64, g3)', 'gz = np.einsum("ab,rbi->rai", mix64, g3)'),
+    ("layer-output gradient through the unquantized weights", "__init__.py",
+     'gx = dyhat @ what + kl["g"]', 'gx = dyhat @ wr + kl["g"]'),
+    ("layer-output residual sign", "__init__.py", "    r = yhat - y\n", "    r = y - yhat\n"),
+    ("weight branch against the unrotated activations", "__init__.py",
+     "gw = dyhat.T @ xr", "gw = dyhat.T @ widen(x)"),
+    ("layer-output mean over rows only", "__init__.py", "n_rec = r.size", "n_rec = r.shape[0]"),
 ]
 
 

@@ -776,3 +776,115 @@ def test_calib_step_reduces_the_loss():
         first = o["loss"] if first is None else first
         th, m, v = o["theta"].astype(np.float32), o["m"], o["v"]
     assert o["loss"] < 0.9 * first
+
+
+# --- the layer-output (weight-side) calibration loss
+
+def _weight_case(seed, n=64, rows=6, out=5, bits=2, group=16, mode=oracle.ASYM):
+    rng = np.random.default_rng(seed)
+    th = rand_theta(n, rng) * 0.7
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    x[:, 5] *= 8.0
+    w = (rng.standard_normal((out, n)) * 0.3).astype(np.float32)
+    return th, x, w, bits, group, mode
+
+
+def test_calib_weight_grad_matches_finite_differences():
+    """dL/dtheta of the layer-output loss against central differences of
+    L(theta) = ||X_r(theta) (W_r(theta) + E)^T - X W^T||^2 / N with the
+    quantizer's error E = What - W_r frozen at theta_0 (the straight-through
+    reading), lambda = 0."""
+    th, x, w, bits, group, mode = _weight_case(90)
+    out = oracle.calib_weight_loss_grad(x, w, th, bits, group, mode, 8, 0.0)
+    e = out["e"]
+    y = x.astype(np.float64) @ w.astype(np.float64).T
+    q = oracle.dense_q  # dense Q built column by column from unit vectors
+
+    def loss(t):
+        Q = q(t)
+        xr = x.astype(np.float64) @ Q.T
+        wr = w.astype(np.float64) @ Q.T
+        return float(((xr @ (wr + e).T - y) ** 2).sum() / y.size)
+
+    assert abs(loss(th) - out["rec"]) < 1e-12 * (1 + out["rec"])
+    L = th.shape[0]
+    rng = np.random.default_rng(91)
+    checked = 0
+    for s in range(L):
+        for p in rng.choice(th.shape[1], 6, replace=False):
+            def fd(h):
+                tp, tm = th.copy(), th.copy()
+                tp[s, p] = np.float32(th[s, p] + h)
+                tm[s, p] = np.float32(th[s, p] - h)
+                return (loss(tp) - loss(tm)) / (float(tp[s, p]) - float(tm[s, p]))
+            rich = (4 * fd(2.0 ** -9) - fd(2.0 ** -8)) / 3
+            assert abs(rich - out["dtheta"][s, p]) < 1e-6 * (1 + abs(rich)), (s, p, rich, out["dtheta"][s, p])
+            checked += 1
+    assert checked == 6 * L
+
+
+def test_calib_weight_grad_single_backward_identity():
+    """Q orthogonal makes the two chain-rule branches collapse: d(X_r W_r^T)
+    = 0, so dL/dtheta equals the backward of X alone with dL/dX_r =
+    2 R E / N (+ the uniformity term), R = Yhat - Y and E = What - W_r.  A
+    sign or transpose slip in either branch breaks the equality."""
+    for seed, lam in ((92, 0.0), (93, 0.3)):
+        th, x, w, bits, group, mode = _weight_case(seed, n=128, rows=9, out=7, bits=4,
+                                                   group=32, mode=oracle.SYM)
+        out = oracle.calib_weight_loss_grad(x, w, th, bits, group, mode, 16, lam)
+        kl = oracle.calib_loss_grad(out["xr"], 4, group, 16, lam, with_rec=False)
+        g = 2.0 * out["r"] @ out["e"] / out["r"].size + kl["g"]
+        single = oracle.backward(x, g.astype(np.float32), th, want_y=False, want_dx=False)
+        scale = np.abs(out["dtheta"]).max()
+        assert np.abs(single["dtheta"] - out["dtheta"]).max() < 1e-6 * scale, lam
+
+
+def test_calib_weight_loss_identity_rotation_closed_form():
+    """theta = 0 (Q = I): L_rec = ||X (deq(quant(W)) - W)^T||^2 / N with the
+    quantizer applied to W itself, written out here from quantize and
+    dequantize; the uniformity term then sees X itself."""
+    th, x, w, bits, group, mode = _weight_case(94, n=64, rows=4, out=3)
+    th0 = np.zeros_like(th)
+    out = oracle.calib_weight_loss_grad(x, w, th0, bits, group, mode, 8, 0.2)
+    q = oracle.quantize(w.astype(np.float64), bits, group, mode)
+    what = oracle.dequantize(q["codes"], q["scales"], q.get("zeros"), bits, group, mode, 64)
+    r = x.astype(np.float64) @ (what - w.astype(np.float64)).T
+    assert abs(out["rec"] - (r * r).sum() / r.size) < 1e-12 * (1 + out["rec"])
+    kl = oracle.calib_loss_grad(x.astype(np.float64), 4, group, 8, 0.2, with_rec=False)
+    assert abs(out["kl"] - kl["kl"]) < 1e-15
+    assert abs(out["loss"] - (out["rec"] + 0.2 * kl["kl"])) < 1e-12
+
+
+def test_calib_uniformity_only_gradient_matches_finite_differences():
+    """with_rec=False: dL/dy of lambda KL alone against central differences
+    of the KL with the group max frozen."""
+    rng = np.random.default_rng(95)
+    rows, n, group, bins, lam = 2, 64, 16, 8, 0.5
+    y = rng.standard_normal((rows, n))
+    out = oracle.calib_loss_grad(y, 4, group, bins, lam, with_rec=False)
+    a, N, h = out["a"], y.size, 2.0 / bins
+    assert abs(out["loss"] - lam * out["kl"]) < 1e-15
+
+    def kl(yy):
+        t = np.clip((yy / a + 1.0) / h - 0.5, 0, bins - 1)
+        j = np.minimum(np.floor(t).astype(np.int64), bins - 2)
+        f = t - j
+        p = (np.bincount(j.ravel(), weights=(1 - f).ravel(), minlength=bins) +
+             np.bincount((j + 1).ravel(), weights=f.ravel(), minlength=bins)) / N
+        ps = (p + oracle.CALIB_SMOOTH) / (1 + bins * oracle.CALIB_SMOOTH)
+        return lam * (ps * np.log(bins * ps)).sum()
+
+    checked = 0
+    for r in range(rows):
+        for i in range(n):
+            ti = out["t"][r, i]
+            if not (0.02 < ti < bins - 1.02) or abs(ti - round(ti)) < 0.02 or abs(y[r, i]) == a[r, i]:
+                continue
+            eps = 1e-6 * a[r, i]
+            yp, ym = y.copy(), y.copy()
+            yp[r, i] += eps
+            ym[r, i] -= eps
+            fd = (kl(yp) - kl(ym)) / (2 * eps)
+            assert abs(fd - out["g"][r, i]) < 1e-6 * (abs(fd) + 1e-3), (r, i)
+            checked += 1
+    assert checked > 40
