@@ -26,7 +26,7 @@
  *   bfly_forward, bfly_forward_quant             Q x, fused group quantization
  *   bfly_kron_forward, bfly_kron_forward_wide    (O kron B) x for n = m * nb
  *   bfly_backward, bfly_kron_backward            dX and the angle gradients
- *   bfly_calib_step                              one step of learning the angles
+ *   bfly_calib_step, bfly_calib_step_weight      one step of learning the angles
  *   bfly_quant_matmul                            y = (Q x)(W Q^T)^T from the codes
  *   bfly_*_bytes, bfly_status_string, bfly_last_hip_error
  *   bfly_forward_quant_noalloc                   bfly_forward_quant with a fixed scratch
@@ -309,6 +309,51 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
                             void* hip_stream);
 
 size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n);
+
+/* Settings of bfly_calib_step_weight (readings: the pages name the loss
+ * terms, not these values). */
+typedef struct {
+    int32_t bits;       /* the weight quantizer: 2 or 4 bits */
+    int32_t group;      /* its group size: a power of two in [8, 512] dividing n; also the
+                           group whose max |y| normalises the uniformity term's histogram */
+    int32_t mode;       /* its bfly_qmode (BFLY_ASYM_MINMAX for W2A16) */
+    int32_t bins;       /* histogram bins of the uniformity term: a power of two in [2, 32] */
+    float lambda_kl;    /* weight of the uniformity term */
+    float lr, beta1, beta2, eps;  /* Adam */
+} bfly_calib_weight_config;
+
+/* One step of learning the angles with the layer's output as the
+ * reconstruction target (duidaima.com write-up, section "training and
+ * results": the quantized model's output should match the original one;
+ * ButterflyQuant abstract: computational invariance W x = (W Q^T)(Q x),
+ * 2-bit weights).  With Xr = Q(theta) X (rows of X), Wr = W Q^T (rows of
+ * W, quantized by the group quantizer of cfg to What):
+ *   L = ||Xr What^T - X W^T||^2 / (rows * out) + lambda_kl * KL(Xr),
+ * KL the uniformity term of bfly_calib_step on Xr.  The quantizer's
+ * rounding passes gradients straight through (What - Wr held constant); as
+ * Q is orthogonal, Xr What^T - X W^T = Xr (What - Wr)^T and dL/dtheta is the
+ * butterfly backward of X with dL/dXr = 2 (Xr E^T) E / (rows * out) plus the
+ * uniformity term's share, E = What - Wr.  The two products run on the
+ * matrix cores in fp32.  Then one Adam update of theta (as bfly_calib_step).
+ *   x     : device fp32 [rows][n] calibration activations (rows >= 1)
+ *   w     : device [out][n] weight rows, w_dt = BFLY_F32 or BFLY_BF16
+ *   out   : a multiple of 16 in [16, 65536], out * n * 4 < 4 GiB
+ *   n     : a power of two in [64, 4096]
+ *   theta, adam_m, adam_v, step, loss: as in bfly_calib_step (loss[0..2] =
+ *           L, the output term, KL at the angles before the update)
+ *   workspace: >= bfly_calib_step_weight_workspace_bytes(rows, out, n)
+ *           bytes of device scratch, 16-byte aligned; the call allocates
+ *           nothing.
+ * Errors: BFLY_ERR_NULL, BFLY_ERR_DTYPE, BFLY_ERR_SIZE, BFLY_ERR_QUANT
+ * (bits, group, mode or bins invalid), BFLY_ERR_UNSUPPORTED (sizes outside
+ * the ranges above), BFLY_ERR_WORKSPACE, BFLY_ERR_ALIGN, BFLY_ERR_HIP. */
+bfly_status bfly_calib_step_weight(const float* x, int64_t rows, const void* w, bfly_dtype w_dt,
+                                   int32_t out, int32_t n, float* theta, float* adam_m,
+                                   float* adam_v, int32_t step,
+                                   const bfly_calib_weight_config* cfg, float* loss,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+size_t bfly_calib_step_weight_workspace_bytes(int64_t rows, int32_t out, int32_t n);
 
 /* ---- consumer of the quantized weights ---------------------------------- */
 

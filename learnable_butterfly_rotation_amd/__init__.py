@@ -21,7 +21,8 @@ __all__ = [
     "bfly_kron_forward_wide_workspace_bytes", "bfly_quant_matmul",
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
     "bfly_kron_backward_workspace_bytes", "bfly_calib_config", "bfly_calib_step",
-    "bfly_calib_workspace_bytes", "bfly_status_string",
+    "bfly_calib_workspace_bytes", "bfly_calib_weight_config", "bfly_calib_step_weight",
+    "bfly_calib_step_weight_workspace_bytes", "bfly_status_string",
     "bfly_last_hip_error", "bfly_time_next_forward", "bfly_forward_quant_noalloc",
 ]
 
@@ -83,6 +84,11 @@ def lib():
                                       ctypes.POINTER(bfly_calib_config), vp, vp, sz, vp]
         L.bfly_calib_workspace_bytes.argtypes = [i64, i32]
         L.bfly_calib_workspace_bytes.restype = sz
+        L.bfly_calib_step_weight.argtypes = [vp, i64, vp, ctypes.c_int, i32, i32, vp, vp, vp, i32,
+                                             ctypes.POINTER(bfly_calib_weight_config), vp, vp, sz,
+                                             vp]
+        L.bfly_calib_step_weight_workspace_bytes.argtypes = [i64, i32, i32]
+        L.bfly_calib_step_weight_workspace_bytes.restype = sz
         L.bfly_kron_backward.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]
         L.bfly_kron_backward_workspace_bytes.argtypes = [i64, i32, i32]
         L.bfly_kron_backward_workspace_bytes.restype = sz
@@ -94,7 +100,8 @@ def lib():
                   L.bfly_forward_quant_noalloc,
                   L.bfly_kron_forward, L.bfly_kron_forward_wide, L.bfly_quant_matmul,
                   L.bfly_backward,
-                  L.bfly_kron_backward, L.bfly_calib_step, L.bfly_time_next_forward):
+                  L.bfly_kron_backward, L.bfly_calib_step, L.bfly_calib_step_weight,
+                  L.bfly_time_next_forward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -109,6 +116,13 @@ class bfly_calib_config(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("bins", ctypes.c_int32),
                 ("lambda_kl", ctypes.c_float), ("lr", ctypes.c_float), ("beta1", ctypes.c_float),
                 ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+class bfly_calib_weight_config(ctypes.Structure):
+    """Settings of bfly_calib_step_weight (include/bfly.h)."""
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("bins", ctypes.c_int32), ("lambda_kl", ctypes.c_float), ("lr", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
 def _ptr(t):
@@ -306,3 +320,20 @@ def bfly_calib_step(x, theta, adam_m, adam_v, step: int, cfg: bfly_calib_config,
                                  ctypes.byref(cfg), _ptr(loss), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "bfly_calib_step")
+
+
+def bfly_calib_step_weight_workspace_bytes(rows: int, out: int, n: int) -> int:
+    return lib().bfly_calib_step_weight_workspace_bytes(rows, out, n)
+
+
+def bfly_calib_step_weight(x, w, theta, adam_m, adam_v, step: int, cfg: bfly_calib_weight_config,
+                           loss, workspace, stream=None) -> None:
+    """One calibration step with the layer-output loss: x [rows, n] float32,
+    w [out, n] float32/bfloat16; theta, adam_m, adam_v updated in place."""
+    rows, n = x.shape
+    out = w.shape[0]
+    _check(lib().bfly_calib_step_weight(_ptr(x), rows, _ptr(w), _dt(w), out, n, _ptr(theta),
+                                        _ptr(adam_m), _ptr(adam_v), step, ctypes.byref(cfg),
+                                        _ptr(loss), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "bfly_calib_step_weight")

@@ -11,6 +11,7 @@
 #include "bfly_internal.h"
 #include "bfly_common.h"
 #include "bfly_calib.h"
+#include "bfly_calib_w.h"
 #include "bfly_qgemm.h"
 
 namespace bfly {
@@ -596,6 +597,144 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
   e = bfly::launch_adam(theta, adam_m, adam_v, dth, l * (n / 2), step, cfg->lr, cfg->beta1,
                         cfg->beta2, cfg->eps, s);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+// Workspace of the layer-output calibration step (every part 256-aligned):
+// the backward's own workspace (the coefficient table first), Xr = Q X,
+// E (first W Q^T, then the quantizer's error), the weight codes, scales and
+// zero points (sized for 4-bit codes and groups of 8), R = Xr E^T, G = dL/dXr,
+// the group maxima of Xr, the histogram partials and log-bins, the sums of
+// squares of R, dtheta.
+struct CalibWParts {
+  size_t bwd, xr, e, codes, scales, zeros, r, g, amax, hpart, lb, ss, dth, total;
+};
+static CalibWParts calib_w_parts(int64_t rows, int64_t out, int logn) {
+  const size_t n = (size_t)1 << logn;
+  CalibWParts o;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at = align_up(at + bytes, 256);
+    return here;
+  };
+  o.bwd = take(bfly_backward_workspace_bytes(rows, (int32_t)n));
+  o.xr = take((size_t)rows * n * sizeof(float));
+  o.e = take((size_t)out * n * sizeof(float));
+  o.codes = take((size_t)out * n / 2);
+  o.scales = take((size_t)out * (n / 8) * 2);
+  o.zeros = take((size_t)out * (n / 8) * 2);
+  o.r = take((size_t)rows * (size_t)out * sizeof(float));
+  o.g = take((size_t)rows * n * sizeof(float));
+  o.amax = take((size_t)rows * (n / 8) * sizeof(float));
+  o.hpart = take(sizeof(float) * (size_t)bfly::CALIB_MAX_BLOCKS * (bfly::CALIB_MAX_BINS + 1));
+  o.lb = take(sizeof(float) * bfly::CALIB_MAX_BINS);
+  o.ss = take(sizeof(float) * (size_t)bfly::gemm_f32_tiles(rows, (int32_t)out));
+  o.dth = take(sizeof(float) * (size_t)logn * (n / 2));
+  o.total = at;
+  return o;
+}
+
+static bool calib_w_sizes(int64_t rows, int32_t out, int32_t n, int* logn) {
+  if (rows < 1 || out < 16 || out % 16 != 0 || out > 65536) return false;
+  if (check_n(n, 12, logn) != BFLY_OK) return false;
+  // every matrix of the products stays below 4 GiB
+  if ((int64_t)out * n * 4 >= (int64_t(1) << 32)) return false;
+  return true;
+}
+
+size_t bfly_calib_step_weight_workspace_bytes(int64_t rows, int32_t out, int32_t n) {
+  int l = 0;
+  if (!calib_w_sizes(rows, out, n, &l)) return 0;
+  return calib_w_parts(rows, out, l).total;
+}
+
+bfly_status bfly_calib_step_weight(const float* x, int64_t rows, const void* w, bfly_dtype w_dt,
+                                   int32_t out, int32_t n, float* theta, float* adam_m,
+                                   float* adam_v, int32_t step,
+                                   const bfly_calib_weight_config* cfg, float* loss,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!x || !w || !theta || !adam_m || !adam_v || !cfg || !loss || !workspace) return BFLY_ERR_NULL;
+  if (!dtype_ok(w_dt)) return BFLY_ERR_DTYPE;
+  if (rows < 1 || step < 1 || out < 1) return BFLY_ERR_SIZE;
+  int l = 0;
+  const bfly_status sn = check_n(n, 12, &l);
+  if (sn != BFLY_OK) return sn;
+  if (!calib_w_sizes(rows, out, n, &l)) return BFLY_ERR_UNSUPPORTED;
+  const int lg = log2_pow2(cfg->group);
+  if ((cfg->bits != 2 && cfg->bits != 4) || lg < 3 || lg > 9 || cfg->group > n ||
+      (cfg->mode != BFLY_SYM_ABSMAX && cfg->mode != BFLY_ASYM_MINMAX) || cfg->bins < 2 ||
+      cfg->bins > bfly::CALIB_MAX_BINS || (cfg->bins & (cfg->bins - 1)) != 0)
+    return BFLY_ERR_QUANT;
+  const CalibWParts o = calib_w_parts(rows, out, l);
+  if (workspace_bytes < o.total) return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(workspace, 16) || !aligned(theta, 4) ||
+      !aligned(adam_m, 4) || !aligned(adam_v, 4) || !aligned(loss, 4))
+    return BFLY_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  char* wsb = ws + o.bwd;  // the backward's workspace; its table area holds the table
+  float* xr = reinterpret_cast<float*>(ws + o.xr);
+  float* e = reinterpret_cast<float*>(ws + o.e);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + o.codes);
+  uint16_t* scales = reinterpret_cast<uint16_t*>(ws + o.scales);
+  uint16_t* zeros = cfg->mode == BFLY_ASYM_MINMAX ? reinterpret_cast<uint16_t*>(ws + o.zeros)
+                                                  : nullptr;
+  float* r = reinterpret_cast<float*>(ws + o.r);
+  float* g = reinterpret_cast<float*>(ws + o.g);
+  float* dth = reinterpret_cast<float*>(ws + o.dth);
+  float* ss = reinterpret_cast<float*>(ws + o.ss);
+  hipError_t err = bfly::launch_prepare(theta, wsb, l, s);
+  if (err != hipSuccess) return hip_fail(err);
+  // Xr = Q X; Wr = W Q^T with its group codes; E = What - Wr in place
+  bfly_status st = bfly_forward(x, BFLY_F32, xr, BFLY_F32, rows, n, nullptr, wsb, nullptr, 0,
+                                hip_stream);
+  if (st != BFLY_OK) return st;
+  st = bfly_forward_quant(w, w_dt, e, BFLY_F32, codes, scales, zeros, out, n, nullptr, wsb,
+                          cfg->bits, cfg->group, (bfly_qmode)cfg->mode, nullptr, 0, hip_stream);
+  if (st != BFLY_OK) return st;
+  if ((err = bfly::launch_quant_residual(e, codes, scales, zeros, out, n, cfg->bits, cfg->group,
+                                         zeros != nullptr, s)) != hipSuccess)
+    return hip_fail(err);
+  // the uniformity term on Xr: group maxima, log-bins, KL into loss[2]
+  bfly::CalibLossParams p;
+  p.y = xr;
+  p.amax = reinterpret_cast<float*>(ws + o.amax);
+  p.rows = rows;
+  p.n = n;
+  p.group = cfg->group;
+  p.bits = 4;  // the histogram pass's own quantizer error is not used here
+  p.bins = cfg->bins;
+  p.lambda_kl = cfg->lambda_kl;
+  p.partials = reinterpret_cast<float*>(ws + o.hpart);
+  p.lb = reinterpret_cast<float*>(ws + o.lb);
+  p.loss = loss;
+  if ((err = bfly::launch_calib_hist(p, s)) != hipSuccess) return hip_fail(err);
+  if ((err = bfly::launch_calib_reduce(p, s)) != hipSuccess) return hip_fail(err);
+  // R = Xr E^T (= Yhat - Y), its sum of squares -> loss[0], loss[1]
+  const double n_rec = (double)rows * (double)out;
+  if ((err = bfly::launch_gemm_f32(xr, e, true, r, rows, out, n, 1.0f, ss, s)) != hipSuccess)
+    return hip_fail(err);
+  if ((err = bfly::launch_weight_loss(ss, bfly::gemm_f32_tiles(rows, out), n_rec, cfg->lambda_kl,
+                                      loss, s)) != hipSuccess)
+    return hip_fail(err);
+  // G = dL/dXr = 2 R E / N_rec + the uniformity term's share
+  if ((err = bfly::launch_gemm_f32(r, e, false, g, rows, n, out, (float)(2.0 / n_rec), nullptr,
+                                   s)) != hipSuccess)
+    return hip_fail(err);
+  const double nx = (double)rows * (double)n;
+  const float kl_scale =
+      (float)(cfg->lambda_kl / (nx * (1.0 + cfg->bins * (double)bfly::kCalibSmooth))) /
+      (2.f / cfg->bins);
+  if ((err = bfly::launch_kl_grad_add(xr, p.amax, p.lb, g, rows * (int64_t)n, cfg->group,
+                                      cfg->bins, kl_scale, s)) != hipSuccess)
+    return hip_fail(err);
+  // dtheta: the butterfly backward of X with G (dX written over G)
+  st = bfly_backward(x, g, nullptr, g, dth, rows, n, nullptr, wsb,
+                     wsb, bfly_backward_workspace_bytes(rows, n), hip_stream);
+  if (st != BFLY_OK) return st;
+  err = bfly::launch_adam(theta, adam_m, adam_v, dth, l * (n / 2), step, cfg->lr, cfg->beta1,
+                          cfg->beta2, cfg->eps, s);
+  return err == hipSuccess ? BFLY_OK : hip_fail(err);
 }
 
 bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* codes,

@@ -340,3 +340,35 @@ def test_calib_step_validation(L):
     assert cs(c=B.bfly_calib_config(4, 128, 33, 0.1, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
     assert cs(wsb=wsb - 1) == WORKSPACE
     assert cs(ws=ctypes.c_void_p(0x80008)) == ALIGN
+
+
+def test_calib_step_weight_validation(L):
+    cfg = B.bfly_calib_weight_config(2, 128, 1, 16, 0.05, 1e-3, 0.9, 0.999, 1e-8)
+    wsb = B.bfly_calib_step_weight_workspace_bytes(64, 256, 4096)
+    assert wsb > 64 * 4096 * 4 * 2 + 256 * 4096 * 4 + 64 * 256 * 4
+    assert B.bfly_calib_step_weight_workspace_bytes(0, 256, 4096) == 0
+    assert B.bfly_calib_step_weight_workspace_bytes(64, 250, 4096) == 0     # out % 16
+    assert B.bfly_calib_step_weight_workspace_bytes(64, 256, 8192) == 0
+    assert B.bfly_calib_step_weight_workspace_bytes(64, 65536 + 16, 1024) == 0
+
+    def cw(x=X, rows=64, w=Y, wd=1, out=256, n=4096, th=TH, m=C, v=S, step=1, c=cfg, loss=Z,
+           ws=WS, wsb=wsb):
+        return L.bfly_calib_step_weight(x, rows, w, wd, out, n, th, m, v, step,
+                                        ctypes.byref(c) if c else None, loss, ws, wsb, None)
+    assert cw(x=None) == NULL
+    assert cw(w=None) == NULL
+    assert cw(c=None) == NULL
+    assert cw(ws=None) == NULL
+    assert cw(wd=7) == DTYPE
+    assert cw(rows=0) == SIZE
+    assert cw(step=0) == SIZE
+    assert cw(n=100) == SIZE
+    assert cw(n=8192) == UNSUPPORTED
+    assert cw(out=100) == UNSUPPORTED                 # not a multiple of 16
+    assert cw(c=B.bfly_calib_weight_config(3, 128, 1, 16, 0.05, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cw(c=B.bfly_calib_weight_config(2, 96, 1, 16, 0.05, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cw(c=B.bfly_calib_weight_config(2, 128, 2, 16, 0.05, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cw(c=B.bfly_calib_weight_config(2, 128, 1, 12, 0.05, 1e-3, 0.9, 0.999, 1e-8)) == QUANT
+    assert cw(wsb=wsb - 1) == WORKSPACE
+    assert cw(ws=ctypes.c_void_p(0x80008)) == ALIGN
+    assert cw(w=ctypes.c_void_p(0x20004)) == ALIGN
