@@ -85,6 +85,11 @@
 extern "C" {
 #endif
 
+/* The two range markers of each enumeration here are no valid value: they
+ * make every 32-bit integer a value of the type, so that an out-of-range
+ * argument from a caller reaches the library's checks (a dtype or mode is
+ * rejected with BFLY_ERR_DTYPE or BFLY_ERR_QUANT) instead of being undefined
+ * in C++. */
 typedef enum {
     BFLY_OK = 0,
     BFLY_ERR_NULL = 1,        /* a required pointer is NULL                       */
@@ -94,10 +99,17 @@ typedef enum {
     BFLY_ERR_QUANT = 5,       /* bits / group / mode / zeros combination invalid   */
     BFLY_ERR_WORKSPACE = 6,   /* workspace or coefficient buffer too small         */
     BFLY_ERR_UNSUPPORTED = 7, /* a valid size the library does not handle         */
-    BFLY_ERR_HIP = 8          /* a HIP runtime call failed                         */
+    BFLY_ERR_HIP = 8,         /* a HIP runtime call failed                         */
+    BFLY_STATUS_RANGE_LOW_ = -2147483647 - 1,
+    BFLY_STATUS_RANGE_HIGH_ = 2147483647
 } bfly_status;
 
-typedef enum { BFLY_F32 = 0, BFLY_BF16 = 1 } bfly_dtype;
+typedef enum {
+    BFLY_F32 = 0,
+    BFLY_BF16 = 1,
+    BFLY_DTYPE_RANGE_LOW_ = -2147483647 - 1,
+    BFLY_DTYPE_RANGE_HIGH_ = 2147483647
+} bfly_dtype;
 
 /* Quantizer modes (WUSH page, technical summary section 2: round-to-nearest
  * with absmax block scaling; ButterflyQuant abstract: 2-bit weights).
@@ -111,7 +123,12 @@ typedef enum { BFLY_F32 = 0, BFLY_BF16 = 1 } bfly_dtype;
  *   A scale above 65504 saturates to 65504; a zero scale gives zero codes
  *   (and a zero point of 0).  rne = round to nearest, ties to even; the
  *   quantized value is the fp32 y before any bf16 rounding of the output. */
-typedef enum { BFLY_SYM_ABSMAX = 0, BFLY_ASYM_MINMAX = 1 } bfly_qmode;
+typedef enum {
+    BFLY_SYM_ABSMAX = 0,
+    BFLY_ASYM_MINMAX = 1,
+    BFLY_QMODE_RANGE_LOW_ = -2147483647 - 1,
+    BFLY_QMODE_RANGE_HIGH_ = 2147483647
+} bfly_qmode;
 
 /* ---- angle preparation ------------------------------------------------- */
 

@@ -132,6 +132,12 @@ int log2_pow2(int64_t n) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Row counts beyond what any device holds are a valid size the library does
+// not handle: below 2^46 elements per matrix every byte count and grid size
+// in this file stays far from overflow.
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+bool rows_fit(int64_t rows, int64_t width) { return width > 0 && rows <= kMaxElems / width; }
+
 // Butterfly length: power of two in [64, 8192] (smaller powers of two are
 // valid sizes the library does not handle).
 bfly_status check_n(int64_t n, int max_log, int* logn) {
@@ -259,7 +265,7 @@ static bfly_status forward_args(const void* x, bfly_dtype x_dt, void* y, bfly_dt
   bfly_status st = check_n(nb, 13, &lognb);
   if (st != BFLY_OK) return st;
   const int64_t n = (int64_t)m * nb;
-  if (n > 8192) return BFLY_ERR_UNSUPPORTED;
+  if (n > 8192 || !rows_fit(rows, n)) return BFLY_ERR_UNSUPPORTED;
   if (quant) {
     st = check_quant(codes, scales, zeros, rows, n, nb, lognb, bits, group, mode);
     if (st != BFLY_OK) return st;
@@ -352,7 +358,7 @@ bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtyp
 
 size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n) {
   int l = 0;
-  if (rows < 0 || check_n(n, 12, &l) != BFLY_OK) return 0;
+  if (rows < 0 || check_n(n, 12, &l) != BFLY_OK || !rows_fit(rows, n)) return 0;
   const size_t slots = (size_t)bfly::backward_blocks(rows, l) * bwd_rows_per_block(l);
   return align_up(coeff_bytes_l(l), 256) + slots * ((size_t)l << (l - 1)) * sizeof(float);
 }
@@ -366,6 +372,7 @@ bfly_status bfly_backward(const float* x, const float* g, float* y, float* dx, f
   int l = 0;
   const bfly_status st = check_n(n, 12, &l);
   if (st != BFLY_OK) return st;
+  if (!rows_fit(rows, n)) return BFLY_ERR_UNSUPPORTED;
   if (workspace_bytes < bfly_backward_workspace_bytes(rows, n)) return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(dx, 16) || !aligned(y, 16) ||
       !aligned(workspace, 16) || !aligned(dtheta, 4) || (coeffs && !aligned(coeffs, 16)) ||
@@ -411,7 +418,7 @@ static size_t kron_wide_parts(int64_t rows, int32_t m, int lognb, size_t* o_v) {
 
 size_t bfly_kron_forward_wide_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
   int l = 0;
-  if (rows < 0 || !kron_wide_sizes(m, nb, &l)) return 0;
+  if (rows < 0 || !kron_wide_sizes(m, nb, &l) || !rows_fit(rows, (int64_t)m * nb)) return 0;
   return kron_wide_parts(rows, m, l, nullptr);
 }
 
@@ -431,7 +438,7 @@ bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly
   int l = 0;
   const bfly_status sn = check_n(nb, 13, &l);
   if (sn != BFLY_OK) return sn;
-  if (!kron_wide_sizes(m, nb, &l)) return BFLY_ERR_UNSUPPORTED;
+  if (!kron_wide_sizes(m, nb, &l) || !rows_fit(rows, (int64_t)m * nb)) return BFLY_ERR_UNSUPPORTED;
   size_t o_v = 0;
   if (workspace_bytes < kron_wide_parts(rows, m, l, &o_v)) return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(workspace, 16) || !aligned(mix, 4)) return BFLY_ERR_ALIGN;
@@ -462,7 +469,7 @@ static size_t kron_bwd_parts(int64_t rows, int32_t m, int lognb, size_t* off_bwd
 
 size_t bfly_kron_backward_workspace_bytes(int64_t rows, int32_t m, int32_t nb) {
   int l = 0;
-  if (rows < 0 || !kron_wide_sizes(m, nb, &l)) return 0;
+  if (rows < 0 || !kron_wide_sizes(m, nb, &l) || !rows_fit(rows, (int64_t)m * nb)) return 0;
   return kron_bwd_parts(rows, m, l, nullptr);
 }
 
@@ -478,7 +485,8 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   const bfly_status st = check_n(nb, 12, &l);
   if (st != BFLY_OK) return st;
   // m = 1 is the plain butterfly (bfly_backward)
-  if (m == 1 || !kron_wide_sizes(m, nb, &l)) return BFLY_ERR_UNSUPPORTED;
+  if (m == 1 || !kron_wide_sizes(m, nb, &l) || !rows_fit(rows, (int64_t)m * nb))
+    return BFLY_ERR_UNSUPPORTED;
   size_t o_bwd = 0;
   if (workspace_bytes < kron_bwd_parts(rows, m, l, &o_bwd)) return BFLY_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(dx, 16) || !aligned(workspace, 16) ||
@@ -524,7 +532,7 @@ static size_t calib_parts(int64_t rows, int logn, size_t* o_amax, size_t* o_dth,
 
 size_t bfly_calib_workspace_bytes(int64_t rows, int32_t n) {
   int l = 0;
-  if (rows < 1 || check_n(n, 12, &l) != BFLY_OK) return 0;
+  if (rows < 1 || check_n(n, 12, &l) != BFLY_OK || !rows_fit(rows, n)) return 0;
   return calib_parts(rows, l, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
@@ -537,6 +545,7 @@ bfly_status bfly_calib_step(const float* x, int64_t rows, int32_t n, float* thet
   int l = 0;
   const bfly_status sn = check_n(n, 12, &l);
   if (sn != BFLY_OK) return sn;
+  if (!rows_fit(rows, n)) return BFLY_ERR_UNSUPPORTED;
   const int lg = log2_pow2(cfg->group);
   if ((cfg->bits != 2 && cfg->bits != 4) || lg < 3 || lg > 9 || cfg->group > n ||
       cfg->bins < 2 || cfg->bins > bfly::CALIB_MAX_BINS)
@@ -637,6 +646,7 @@ static CalibWParts calib_w_parts(int64_t rows, int64_t out, int logn) {
 static bool calib_w_sizes(int64_t rows, int32_t out, int32_t n, int* logn) {
   if (rows < 1 || out < 16 || out % 16 != 0 || out > 65536) return false;
   if (check_n(n, 12, logn) != BFLY_OK) return false;
+  if (!rows_fit(rows, n) || !rows_fit(rows, out)) return false;
   // every matrix of the products stays below 4 GiB
   if ((int64_t)out * n * 4 >= (int64_t(1) << 32)) return false;
   return true;
@@ -752,6 +762,7 @@ bfly_status bfly_quant_matmul(const void* a, bfly_dtype a_dt, const uint8_t* cod
   if (k % group != 0) return BFLY_ERR_QUANT;
   if (n_out % bfly::QG_BN != 0 || n_out > (1 << 20) || k % bfly::QG_BK != 0 || k > 65536)
     return BFLY_ERR_UNSUPPORTED;
+  if (!rows_fit(rows, k) || !rows_fit(rows, n_out)) return BFLY_ERR_UNSUPPORTED;
   const int64_t tiles = (rows + bfly::QG_BM - 1) / bfly::QG_BM * (n_out / bfly::QG_BN);
   if (tiles >= (int64_t(1) << 31)) return BFLY_ERR_UNSUPPORTED;
   if ((a && !aligned(a, 16)) || !aligned(codes, 16) || !aligned(scales, 2) ||
@@ -806,6 +817,7 @@ const char* bfly_status_string(bfly_status s) {
     case BFLY_ERR_WORKSPACE: return "workspace or coefficient buffer too small";
     case BFLY_ERR_UNSUPPORTED: return "size not supported by the library";
     case BFLY_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }
