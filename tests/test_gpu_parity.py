@@ -341,6 +341,100 @@ def test_timed_forward_launch_is_the_same_kernel():
         assert np.array_equal(a, b)
 
 
+def _fq(x, th, ws=None, coeffs=None, noalloc=False):
+    rows, n = x.shape
+    y = empty((rows, n), torch.bfloat16)
+    codes = torch.zeros((rows, n // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+    if noalloc:
+        B.bfly_forward_quant_noalloc(x, y, codes, scales, theta=th, bits=4, group=128, mode=0)
+    elif coeffs is not None:
+        B.bfly_forward_quant(x, y, codes, scales, coeffs=coeffs, bits=4, group=128, mode=0)
+    else:
+        B.bfly_forward_quant(x, y, codes, scales, theta=th, bits=4, group=128, mode=0,
+                             workspace=ws)
+    return y, codes, scales
+
+
+@pytest.mark.parametrize("n,rows", [(4096, 512), (4096, 383), (1024, 640), (256, 300)])
+def test_forward_from_angles_with_a_reused_workspace(n, rows):
+    """From angles, the call prepares its table into the caller's workspace.
+    One workspace, whatever it held before (zeros, ones, an earlier call's
+    table), serves calls with different angles in turn; each matches the
+    call on the table bfly_prepare made, bit for bit (and so does the entry
+    point without allocation), and the oracle."""
+    rng = np.random.default_rng(4000 + n + rows)
+    x = dev(inputs.f32_to_bf16_bits(rng.standard_normal((rows, n)).astype(np.float32)))
+    thetas = [dev(rand_theta(rng, n)) for _ in range(2)]
+    refs = []
+    for th in thetas:
+        tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+        B.bfly_prepare(th, n, tab)
+        refs.append([host(t) for t in _fq(x, th, coeffs=tab)])
+    ws = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    for fill in (0, 255):
+        ws.fill_(fill)
+        for k in (0, 1, 0, 0, 1):
+            got = [host(t) for t in _fq(x, thetas[k], ws=ws)]
+            for a, b in zip(got, refs[k]):
+                assert np.array_equal(a, b), (fill, k)
+    got = [host(t) for t in _fq(x, thetas[1], noalloc=True)]
+    for a, b in zip(got, refs[1]):
+        assert np.array_equal(a, b)
+    th64 = host(thetas[0])
+    xb = host(x)
+    y64 = oracle.forward(xb, th64)
+    assert_forward(refs[0][0], y64, xb, n)
+
+
+def test_forward_from_angles_under_stream_capture():
+    """A captured forward from angles (the prepare kernel, then the fused
+    kernel) is replayed with the angles changed in place between replays,
+    with eager work and synchronisations in between; every replay matches
+    the eager call with those angles.  Both the workspace entry point and
+    the one without allocation are captured."""
+    rng = np.random.default_rng(4100)
+    n, rows = 4096, 512
+    x = dev(inputs.f32_to_bf16_bits(rng.standard_normal((rows, n)).astype(np.float32)))
+    th = dev(rand_theta(rng, n))
+    ws = torch.zeros(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    y = empty((rows, n), torch.bfloat16)
+    codes = torch.zeros((rows, n // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((rows, n // 128), dtype=torch.float16, device="cuda")
+    for noalloc in (False, True):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm-up outside the capture
+            if noalloc:
+                B.bfly_forward_quant_noalloc(x, y, codes, scales, theta=th, bits=4, group=128,
+                                             mode=0)
+            else:
+                B.bfly_forward_quant(x, y, codes, scales, theta=th, bits=4, group=128, mode=0,
+                                     workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            if noalloc:
+                B.bfly_forward_quant_noalloc(x, y, codes, scales, theta=th, bits=4, group=128,
+                                             mode=0)
+            else:
+                B.bfly_forward_quant(x, y, codes, scales, theta=th, bits=4, group=128, mode=0,
+                                     workspace=ws)
+        for rep in range(4):
+            th.copy_(dev(rand_theta(rng, n)))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = (host(y), host(codes), host(scales))
+            tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+            B.bfly_prepare(th, n, tab)
+            want = [host(t) for t in _fq(x, th, coeffs=tab)]
+            for a, b in zip(got, want):
+                assert np.array_equal(a, b), (noalloc, rep)
+        del g
+
+
 def test_zero_angles_identity_bit_exact():
     rng = np.random.default_rng(4)
     x = inputs.f32_to_bf16_bits(rng.standard_normal((20, 512)).astype(np.float32))
