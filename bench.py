@@ -25,7 +25,7 @@ host's cores (all threads; one-thread timings of three workloads beside it).
 --workload picks one of the other workloads for a secondary line:
 tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
 kron_n11008_bf16_int4, kron_bwd_n5120_fp32, calib_n4096_fp32_fwd_bwd,
-calib_step_n4096_fp32, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
+calib_step_n4096_fp32, calib_step_weight_n4096_out4096, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
 w2a16_m1_k4096_n11008, w2a16_m16_k4096_n11008.  --copy-probe runs a plain
 device copy of known size (for calibrating the byte counters).
 """
@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "butterfly+quant GB/s (% of HBM roofline), n=4096, 8192 rows bf16"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
+MFMA_FP32_PEAK_TFLOPS = 157.3   # dense fp32 matrix-core peak of the MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bfly_fwd_quant_n4096_bf16_int4_traffic.txt")
 NSETS = 5
 
@@ -542,6 +543,34 @@ def bench_secondary(args, torch, B, inputs):
         passes = c.rows * c.n * 4 * 4  # X and Y (forward), Y (histogram), X (backward)
         res.update(us_per_step=t * 1e6, rows_per_s=c.rows / t, bytes_moved=passes,
                    GBs_moved=passes / t / 1e9, loss=[float(z) for z in loss.cpu()])
+    elif name == "calib_step_weight_n4096_out4096":
+        # One layer-output calibration step on the 262144 calibration rows of
+        # n = 4096 against the 4096 x 4096 weight of the weight workload (a
+        # LLaMA-2-7B attention projection's shape), asym INT2 g128 (W2A16):
+        # forward of X and of W's rows, the two fp32 products on the matrix
+        # cores, the uniformity term, one backward, Adam.
+        c = inputs.CalibFP32()
+        X = torch.empty((c.rows, c.n), device="cuda")
+        for r0, xb, _ in c.blocks(threads=16):
+            X[r0:r0 + xb.shape[0]].copy_(torch.from_numpy(xb))
+        ww = inputs.weight_int2()
+        W = to_dev(ww["w1"], torch)
+        out = W.shape[0]
+        th = to_dev(c.theta, torch)
+        m, v = torch.zeros_like(th), torch.zeros_like(th)
+        loss = torch.zeros(3, device="cuda")
+        ws = torch.empty(B.bfly_calib_step_weight_workspace_bytes(c.rows, out, c.n),
+                         dtype=torch.uint8, device="cuda")
+        cfg = B.bfly_calib_weight_config(2, 128, B.BFLY_ASYM_MINMAX, 16, 0.05, 1e-3, 0.9, 0.999,
+                                         1e-8)
+        t = time_loop(torch, lambda i: B.bfly_calib_step_weight(X, W, th, m, v, i + 1, cfg, loss,
+                                                                 ws), args.steps, args.warmup)
+        flops = 4.0 * c.rows * out * c.n  # R = Xr E^T and G = R E, 2 flops per multiply-add
+        res.update(us_per_step=t * 1e6, rows_per_s=c.rows / t, out=out, product_flops=flops,
+                   product_TFLOPs_at_step=flops / t / 1e12,
+                   mfma_fp32_peak_TFLOPs=MFMA_FP32_PEAK_TFLOPS,
+                   frac_of_fp32_mfma_peak_at_step=flops / t / 1e12 / MFMA_FP32_PEAK_TFLOPS,
+                   loss=[float(z) for z in loss.cpu()])
     elif name == "calib_n4096_fp32_fwd_bwd":
         c = inputs.CalibFP32()
         X = torch.empty((c.rows, c.n), device="cuda")
@@ -557,6 +586,20 @@ def bench_secondary(args, torch, B, inputs):
                       args.steps, args.warmup)
         b = c.rows * c.n * 16
         res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=c.rows / t)
+        if not args.no_cpu_baseline:
+            # the oracle's forward + backward (Y, dX, dtheta) on the first
+            # block of rows with all host threads, median of 3: a bounded
+            # sample of the workload, scaled to its rows
+            import oracle
+            xb = X[:4096].cpu().numpy()
+            gb = G[:4096].cpu().numpy()
+            thh = c.theta
+            tc = _median_time(lambda: oracle.backward(xb, gb, thh), 3)
+            res["cpu_baseline"] = {
+                "kind": "oracle", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+                "nproc": os.cpu_count(), "sample_rows": 4096, "s_per_sample": round(tc, 3),
+                "rows_per_s": round(4096 / tc), "GBs": round(4096 * c.n * 16 / tc / 1e9, 4),
+                "full_workload_s_estimate": round(tc * c.rows / 4096, 1)}
     else:
         raise SystemExit("unknown workload %s" % name)
     if "GBs" in res:
