@@ -25,7 +25,8 @@ host's cores (all threads; one-thread timings of three workloads beside it).
 --workload picks one of the other workloads for a secondary line:
 tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
 kron_n11008_bf16_int4, kron_bwd_n5120_fp32, calib_n4096_fp32_fwd_bwd,
-calib_step_n4096_fp32, calib_step_weight_n4096_out4096, hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
+calib_step_n4096_fp32, calib_step_weight_n4096_out4096, act_n8192_bf16_int4,
+hadamard_n4096_bf16_int4, w2a16_m8192_k4096_n11008,
 w2a16_m1_k4096_n11008, w2a16_m16_k4096_n11008.  --copy-probe runs a plain
 device copy of known size (for calibrating the byte counters).
 """
@@ -543,6 +544,30 @@ def bench_secondary(args, torch, B, inputs):
         passes = c.rows * c.n * 4 * 4  # X and Y (forward), Y (histogram), X (backward)
         res.update(us_per_step=t * 1e6, rows_per_s=c.rows / t, bytes_moved=passes,
                    GBs_moved=passes / t / 1e9, loss=[float(z) for z in loss.cpu()])
+    elif name == "act_n8192_bf16_int4":
+        # n = 8192 (two passes: the halves' 12 stages into an fp32 workspace,
+        # then stage 12 with the bf16 output and the INT4 g128 quantizer) on
+        # 4096 bf16 rows with outlier channels: the headline's bytes at twice
+        # the width.  One step = one bfly_forward_quant call from the angles.
+        rng = np.random.default_rng(7)
+        n, rows = 8192, 4096
+        th = to_dev(inputs.angles(rng, n), torch)
+        cols = inputs.outlier_columns(rng, n)
+        xh = inputs.activations(rng, rows, n, cols, "bf16")
+        sets = []
+        for _ in range(NSETS):
+            x = to_dev(xh, torch)
+            sets.append((x, torch.empty_like(x), torch.empty((rows, n // 2), dtype=torch.uint8, device="cuda"),
+                         torch.empty((rows, n // 128), dtype=torch.float16, device="cuda")))
+        ws = torch.empty(B.bfly_forward_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            x, y, c, sc = sets[i % NSETS]
+            B.bfly_forward_quant(x, y, c, sc, theta=th, bits=4, group=128, mode=0, workspace=ws)
+        t = time_loop(torch, fn, args.steps, args.warmup)
+        b = rows * (2 * n + 2 * n + n // 2 + 2 * (n // 128))
+        res.update(us_per_step=t * 1e6, bytes=b, GBs=b / t / 1e9, rows_per_s=rows / t,
+                   fp32_intermediate_bytes=rows * n * 8)
     elif name == "calib_step_weight_n4096_out4096":
         # One layer-output calibration step on the 262144 calibration rows of
         # n = 4096 against the 4096 x 4096 weight of the weight workload (a

@@ -165,11 +165,21 @@ bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, v
  * bf16 outputs are rounded to nearest even from fp32.  workspace: with
  * coeffs == NULL, >= bfly_coeff_bytes(n) bytes of device scratch that
  * receives the table (BFLY_ERR_NULL if missing, BFLY_ERR_WORKSPACE if
- * smaller); ignored with coeffs.  Passage: ButterflyQuant abstract (Q x and
- * W Q^T). */
+ * smaller); ignored with coeffs.  Its contents on entry do not matter.
+ * n = 8192 runs in two passes (stages 0..11 on each half of the row, then
+ * stage 12 with the output and quantizer) and always needs a workspace of
+ * >= bfly_forward_workspace_bytes(rows, 8192) bytes: the table area, then
+ * the rows in fp32 between the passes.  Passage: ButterflyQuant abstract
+ * (Q x and W Q^T). */
 bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
                          int64_t rows, int32_t n, const float* theta, const void* coeffs,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes of a forward call (bfly_forward, bfly_forward_quant) of
+ * `rows` rows of length n: bfly_coeff_bytes(n) for n <= 4096 (needed when
+ * the table comes from theta), the table area rounded up to 256 bytes plus
+ * rows * 8192 * 4 for n = 8192; 0 for sizes the library does not handle. */
+size_t bfly_forward_workspace_bytes(int64_t rows, int32_t n);
 
 /* The forward, fused with per-group round-to-nearest quantization of y.
  *   y      : may be NULL (codes only); else [rows][n] of y_dt

@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "BflyError", "lib", "library_path", "BFLY_F32", "BFLY_BF16", "BFLY_SYM_ABSMAX",
-    "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_prepare", "bfly_prepare_hadamard",
+    "BFLY_ASYM_MINMAX", "bfly_coeff_bytes", "bfly_forward_workspace_bytes", "bfly_prepare",
+    "bfly_prepare_hadamard",
     "bfly_forward", "bfly_forward_quant", "bfly_kron_forward", "bfly_kron_forward_wide",
     "bfly_kron_forward_wide_workspace_bytes", "bfly_quant_matmul",
     "bfly_backward", "bfly_backward_workspace_bytes", "bfly_kron_backward",
@@ -60,6 +61,8 @@ def lib():
         vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         L.bfly_coeff_bytes.argtypes = [i32]
         L.bfly_coeff_bytes.restype = sz
+        L.bfly_forward_workspace_bytes.argtypes = [i64, i32]
+        L.bfly_forward_workspace_bytes.restype = sz
         L.bfly_prepare.argtypes = [vp, i32, vp, sz, vp]
         L.bfly_prepare_hadamard.argtypes = [i32, vp, sz, vp]
         L.bfly_forward.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, vp, sz,
@@ -159,15 +162,16 @@ def _nbytes(t):
 
 
 def _table_ws(n, theta, coeffs, workspace, like):
-    """The workspace a forward call prepares its table into: the caller's,
-    or -- when angles are given without a table or a workspace -- a fresh
-    uint8 tensor of bfly_coeff_bytes(n) from torch's allocator on the
-    device of `like` (torch supplies the device memory; the library
-    allocates none)."""
-    if coeffs is not None or workspace is not None or theta is None:
+    """The workspace of a forward call: the caller's, or -- when the call
+    needs one (angles without a table; n = 8192 always) and none is given --
+    a fresh uint8 tensor of bfly_forward_workspace_bytes(rows, n) from
+    torch's allocator on the device of `like` (torch supplies the device
+    memory; the library allocates none)."""
+    if workspace is not None or (n != 8192 and (coeffs is not None or theta is None)):
         return workspace
     import torch
-    return torch.empty(max(1, bfly_coeff_bytes(n)), dtype=torch.uint8, device=like.device)
+    nbytes = bfly_forward_workspace_bytes(like.shape[0], n)
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=like.device)
 
 
 # ---------------------------------------------------------------------------
@@ -176,6 +180,10 @@ def _table_ws(n, theta, coeffs, workspace, like):
 
 def bfly_coeff_bytes(n: int) -> int:
     return lib().bfly_coeff_bytes(n)
+
+
+def bfly_forward_workspace_bytes(rows: int, n: int) -> int:
+    return lib().bfly_forward_workspace_bytes(rows, n)
 
 
 def bfly_prepare(theta, n: int, coeffs, stream=None) -> None:

@@ -150,7 +150,8 @@ bfly_status check_n(int64_t n, int max_log, int* logn) {
 
 bool dtype_ok(int d) { return d == BFLY_F32 || d == BFLY_BF16; }
 
-size_t coeff_bytes_l(int logn) { return bfly::table_bytes(logn); }
+// n = 8192 keeps the two half tables of its two-pass forward (bfly_fwd8k.hip).
+size_t coeff_bytes_l(int logn) { return logn == 13 ? bfly::table8k_bytes() : bfly::table_bytes(logn); }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -172,8 +173,6 @@ bfly_status check_quant(const uint8_t* codes, const uint16_t* scales, const uint
   const int lg = log2_pow2(group);
   if (lg < 3 || lg > 9 || group > seg || seg % group != 0 || n % group != 0) return BFLY_ERR_QUANT;
   if ((group * bits) % 8 != 0) return BFLY_ERR_QUANT;
-  // a thread holds 16 elements at length 8192 (8 elsewhere): groups of 8 would split it
-  if (logseg >= 13 && group < 16) return BFLY_ERR_UNSUPPORTED;
   if (!aligned(codes, 16)) return BFLY_ERR_ALIGN;
   if (!aligned(scales, 2) || (zeros && !aligned(zeros, 2))) return BFLY_ERR_ALIGN;
   return BFLY_OK;
@@ -226,7 +225,8 @@ bfly_status bfly_prepare(const float* theta, int32_t n, void* coeffs, size_t coe
   if (st != BFLY_OK) return st;
   if (coeff_bytes < coeff_bytes_l(l)) return BFLY_ERR_WORKSPACE;
   if (!aligned(coeffs, 16) || !aligned(theta, 4)) return BFLY_ERR_ALIGN;
-  const hipError_t e = bfly::launch_prepare(theta, coeffs, l, (hipStream_t)hip_stream);
+  const hipError_t e = l == 13 ? bfly::launch_prepare_8192(theta, coeffs, false, (hipStream_t)hip_stream)
+                               : bfly::launch_prepare(theta, coeffs, l, (hipStream_t)hip_stream);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
@@ -243,7 +243,8 @@ bfly_status bfly_prepare_hadamard(int32_t n, void* coeffs, size_t coeff_bytes, v
   if (st != BFLY_OK) return st;
   if (coeff_bytes < coeff_bytes_l(l)) return BFLY_ERR_WORKSPACE;
   if (!aligned(coeffs, 16)) return BFLY_ERR_ALIGN;
-  const hipError_t e = bfly::launch_prepare(nullptr, coeffs, l, (hipStream_t)hip_stream, true);
+  const hipError_t e = l == 13 ? bfly::launch_prepare_8192(nullptr, coeffs, true, (hipStream_t)hip_stream)
+                               : bfly::launch_prepare(nullptr, coeffs, l, (hipStream_t)hip_stream, true);
   return e == hipSuccess ? BFLY_OK : hip_fail(e);
 }
 
@@ -324,10 +325,72 @@ static bfly_status forward_common(const void* x, bfly_dtype x_dt, void* y, bfly_
   return forward_run(p, theta, coeffs, workspace, (hipStream_t)hip_stream);
 }
 
+// n = 8192 (two passes): the workspace always holds the fp32 rows between
+// the passes, after the table area (used when the table comes from theta).
+static size_t fwd8k_v_offset() { return align_up(coeff_bytes_l(13), 256); }
+
+static bfly_status forward_8192(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt,
+                                uint8_t* codes, uint16_t* scales, uint16_t* zeros, int64_t rows,
+                                const float* theta, const void* coeffs, int32_t bits,
+                                int32_t group, bfly_qmode mode, bool quant, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+  if (rows > 0 && !x) return BFLY_ERR_NULL;
+  if (!coeffs && !theta) return BFLY_ERR_NULL;
+  if (rows > 0 && !y && !quant) return BFLY_ERR_NULL;
+  if (!workspace) return BFLY_ERR_NULL;
+  if (!dtype_ok(x_dt) || (y && !dtype_ok(y_dt))) return BFLY_ERR_DTYPE;
+  if (rows < 0) return BFLY_ERR_SIZE;
+  if (!rows_fit(rows, 8192)) return BFLY_ERR_UNSUPPORTED;
+  if (quant) {
+    const bfly_status st = check_quant(codes, scales, zeros, rows, 8192, 8192, 13, bits, group, mode);
+    if (st != BFLY_OK) return st;
+  }
+  if (workspace_bytes < fwd8k_v_offset() + (size_t)rows * 8192 * sizeof(float))
+    return BFLY_ERR_WORKSPACE;
+  if (!aligned(x, 16) || (y && !aligned(y, 16)) || !aligned(workspace, 16) ||
+      (coeffs && !aligned(coeffs, 16)) || (theta && !aligned(theta, 4)))
+    return BFLY_ERR_ALIGN;
+  if (rows == 0) return BFLY_OK;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  const void* tab = coeffs;
+  if (!tab) {
+    const hipError_t e = bfly::launch_prepare_8192(theta, ws, false, s);
+    if (e != hipSuccess) return hip_fail(e);
+    tab = ws;
+  }
+  bfly::Fwd8kParams p;
+  p.x = x;
+  p.x_bf16 = x_dt == BFLY_BF16;
+  p.y = y;
+  p.y_kind = !y ? bfly::Y_NONE : (y_dt == BFLY_BF16 ? bfly::Y_BF16 : bfly::Y_F32);
+  p.codes = quant ? codes : nullptr;
+  p.scales = quant ? scales : nullptr;
+  p.zeros = quant ? zeros : nullptr;
+  p.bits = quant ? bits : 0;
+  p.group = quant ? group : 0;
+  p.asym = quant && mode == BFLY_ASYM_MINMAX;
+  p.rows = rows;
+  p.table = tab;
+  p.v = reinterpret_cast<float*>(ws + fwd8k_v_offset());
+  const hipError_t e = bfly::launch_forward_8192(p, s);
+  return e == hipSuccess ? BFLY_OK : hip_fail(e);
+}
+
+size_t bfly_forward_workspace_bytes(int64_t rows, int32_t n) {
+  int l = 0;
+  if (rows < 0 || check_n(n, 13, &l) != BFLY_OK || !rows_fit(rows, n)) return 0;
+  if (l == 13) return fwd8k_v_offset() + (size_t)rows * 8192 * sizeof(float);
+  return coeff_bytes_l(l);
+}
+
 bfly_status bfly_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtype y_dt, int64_t rows,
                          int32_t n, const float* theta, const void* coeffs, void* workspace,
                          size_t workspace_bytes, void* hip_stream) {
   if (rows > 0 && !y) return BFLY_ERR_NULL;
+  if (n == 8192)
+    return forward_8192(x, x_dt, y, y_dt, nullptr, nullptr, nullptr, rows, theta, coeffs, 0, 0,
+                        BFLY_SYM_ABSMAX, false, workspace, workspace_bytes, hip_stream);
   return forward_common(x, x_dt, y, y_dt, nullptr, nullptr, nullptr, rows, 1, n, theta, coeffs,
                         nullptr, 0, 0, BFLY_SYM_ABSMAX, false, workspace, workspace_bytes,
                         hip_stream);
@@ -338,6 +401,9 @@ bfly_status bfly_forward_quant(const void* x, bfly_dtype x_dt, void* y, bfly_dty
                                int32_t n, const float* theta, const void* coeffs, int32_t bits,
                                int32_t group, bfly_qmode mode, void* workspace,
                                size_t workspace_bytes, void* hip_stream) {
+  if (n == 8192)
+    return forward_8192(x, x_dt, y, y_dt, codes, scales, zeros, rows, theta, coeffs, bits, group,
+                        mode, true, workspace, workspace_bytes, hip_stream);
   return forward_common(x, x_dt, y, y_dt, codes, scales, zeros, rows, 1, n, theta, coeffs,
                         nullptr, bits, group, mode, true, workspace, workspace_bytes, hip_stream);
 }

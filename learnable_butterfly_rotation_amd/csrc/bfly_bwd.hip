@@ -362,10 +362,17 @@ constexpr int PREP_LANES = 4;
 // shear form) and scale d_i (scaled form).  The forward calls then compute
 // H_n x, H_n the orthonormal Sylvester-ordered Walsh-Hadamard matrix
 // (Q(pi/4) D = H_n).  theta is not read.
+//
+// tstride: floats from one stage's angles to the next (n/2 for a table of
+// its own; the halves of a longer butterfly read strided slices of its
+// angles).  par0: the sign every element's history starts with (HAD only;
+// the upper half of a longer Hadamard starts negated).  gid: the lane's
+// index among the table's PREP_LANES * L * n/2 lanes.
 template <bool HAD>
-__global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
+__device__ __forceinline__ void prepare_entry(const float* __restrict__ theta,
+                                              char* __restrict__ table, int logn, int tstride,
+                                              int par0, int64_t gid) {
   const int half = 1 << (logn - 1);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int q = (int)(gid % PREP_LANES);
   const int64_t k = gid / PREP_LANES;
   // a pair's lanes leave together (the reductions below need all of them)
@@ -375,10 +382,11 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
   const int j = i | (1 << s);
   const double halfpi = 1.5707963267948966;
   const double r2 = 0.70710678118654752;  // cos and sin of pi/4
-  const double t = HAD ? 0.78539816339744831 : (double)theta[k];
+  const int64_t ka = (int64_t)s * tstride + p;  // this pair's angle
+  const double t = HAD ? 0.78539816339744831 : (double)theta[ka];
   double sn, cn;
   if (HAD) sn = cn = r2;
-  else sincos_of_float(theta[k], sn, cn);
+  else sincos_of_float(theta[ka], sn, cn);
   const Table tab = table_at(table, logn);
   float2* cs = const_cast<float2*>(tab.cs);
   float* fgt = reinterpret_cast<float*>(const_cast<float4*>(tab.fgt));
@@ -394,12 +402,12 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
     const int s2 = q + PREP_LANES * m;
-    ti[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * half + pair_rank(i, s2) : k];
-    tj[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * half + pair_rank(j, s2) : k];
+    ti[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * tstride + pair_rank(i, s2) : ka];
+    tj[m] = HAD ? 0.f : theta[s2 < s ? (int64_t)s2 * tstride + pair_rank(j, s2) : ka];
   }
   // the input side's diagonal (identity unless HAD), taken by one lane
-  int par_i = (HAD && q == 0) ? (__builtin_popcount(i) & 1) : 0;
-  int par_j = (HAD && q == 0) ? (__builtin_popcount(j) & 1) : 0;
+  int par_i = (HAD && q == 0) ? ((__builtin_popcount(i) + par0) & 1) : 0;
+  int par_j = (HAD && q == 0) ? ((__builtin_popcount(j) + par0) & 1) : 0;
   double sig_i = par_i ? -1.0 : 1.0, sig_j = par_j ? -1.0 : 1.0;
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
@@ -469,6 +477,51 @@ __global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict
       else *reinterpret_cast<float2*>(fgt + fwd_last_index(j, logn)) = make_float2(kj, kji);
     }
   }
+}
+
+template <bool HAD>
+__global__ void prepare_kernel(const float* __restrict__ theta, char* __restrict__ table, int logn) {
+  prepare_entry<HAD>(theta, table, logn, 1 << (logn - 1), 0,
+                     (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// (cos, sin) of one angle in fp64, rounded to fp32 (theta nullptr: pi/4).
+__device__ __forceinline__ void last_stage_entry(const float* __restrict__ theta,
+                                                 float2* __restrict__ cs, int i) {
+  double sn = 0.70710678118654752, cn = 0.70710678118654752;  // pi/4 without angles
+  if (theta != nullptr) sincos_of_float(theta[i], sn, cn);
+  cs[i] = make_float2((float)cn, (float)sn);
+}
+
+// The whole table of n = 8192 in one launch: the lanes of the two half
+// tables (length 4096, stage stride 4096 in theta, the upper half from
+// column 2048; for H_8192 the upper half's diagonal starts with one more
+// sign), then one lane per angle of stage 12.
+template <bool HAD>
+__global__ void prepare8k_kernel(const float* __restrict__ theta, char* __restrict__ table) {
+  constexpr int64_t lanes = (int64_t)12 * 2048 * PREP_LANES;  // one half table
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid < 2 * lanes) {
+    const int h = gid >= lanes ? 1 : 0;  // whole PREP_LANES groups per half
+    prepare_entry<HAD>(HAD ? nullptr : theta + h * 2048, table + h * table_bytes(12), 12, 4096,
+                       HAD ? h : 0, gid - h * lanes);
+  } else if (gid < 2 * lanes + 4096) {
+    last_stage_entry(HAD ? nullptr : theta + 12 * 4096,
+                     reinterpret_cast<float2*>(table + 2 * table_bytes(12)), (int)(gid - 2 * lanes));
+  }
+}
+
+hipError_t launch_prepare_8192(const float* theta, void* table, bool hadamard, hipStream_t s) {
+  const int threads = 64;
+  const int64_t count = (int64_t)2 * 12 * 2048 * PREP_LANES + 4096;
+  const unsigned blocks = (unsigned)((count + threads - 1) / threads);
+  if (hadamard)
+    hipLaunchKernelGGL(prepare8k_kernel<true>, dim3(blocks), dim3(threads), 0, s, nullptr,
+                       static_cast<char*>(table));
+  else
+    hipLaunchKernelGGL(prepare8k_kernel<false>, dim3(blocks), dim3(threads), 0, s, theta,
+                       static_cast<char*>(table));
+  return hipGetLastError();
 }
 
 hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t s, bool hadamard) {

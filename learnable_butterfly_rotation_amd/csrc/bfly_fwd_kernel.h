@@ -352,18 +352,20 @@ struct InRegs {
 // resource covering exactly the group's valid rows (none past the end).
 // elem0: the element of the thread's register 0 within its row segment.
 // Non-temporal: every input line is read once (-0.7 us at n = 4096, 8192
-// rows).
-template <class S, bool XBF16>
+// rows).  XS: rows lie XS * n elements apart (XS = 2: one half of each row of
+// twice the length).
+template <class S, bool XBF16, int XS = 1>
 __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t rows, const int64_t grp,
                                            InRegs<S, XBF16>& in, const int d, const int team,
                                            const int elem0) {
-  constexpr int N = S::N, NB = S::NB, E = S::E, RPP = S::ROWS_PER_PASS;
+  constexpr int N = S::N, NB = S::NB, RPP = S::ROWS_PER_PASS;
   constexpr int RPT = S::ROWS_PER_PASS / S::R, M = S::SEGS / RPT;
   constexpr int RAW = InRegs<S, XBF16>::RAW, ESZ = XBF16 ? 2 : 4;
+  constexpr int LD = XS * N;  // row stride in elements
   const uint32_t valid = (uint32_t)group_rows(rows, grp, RPP);
-  const auto rs = buffer_range32(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * N) * ESZ,
-                                 valid * (uint32_t)(N * ESZ));
-  const int thr_elem = team * RPT * N + elem0;
+  const auto rs = buffer_range32(reinterpret_cast<const char*>(P.x) + grp * ((int64_t)RPP * LD) * ESZ,
+                                 valid * (uint32_t)(LD * ESZ));
+  const int thr_elem = team * RPT * LD + elem0;
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr)
 #pragma unroll
@@ -371,7 +373,7 @@ __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t row
 #pragma unroll
       for (int c = 0; c < RAW; ++c)
         in.r[d][rr * M + a][c] =
-            buf_ld16<kNonTemporal>(rs, (uint32_t)(thr_elem + rr * N + a * NB) * ESZ + 16 * c);
+            buf_ld16<kNonTemporal>(rs, (uint32_t)(thr_elem + rr * LD + a * NB) * ESZ + 16 * c);
 }
 
 // PRE: the caller has already issued the prologue's loads (slot d holds row
@@ -384,7 +386,7 @@ __device__ __forceinline__ void load_group(const FwdParams& P, const int64_t row
 // false, and the caller must redo every row.  The early stop only shortens
 // the loop: a separate exit path would put the two forms' loops on two arms
 // of a branch, where the register allocator does far worse.
-template <class S, bool XBF16, int YK, int QM, bool FAST, bool PRE, bool CHECK>
+template <class S, bool XBF16, int YK, int QM, bool FAST, bool PRE, bool CHECK, int XS = 1>
 __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows, float* lds, int team,
                                          int t, const Coeffs<S>& C, InRegs<S, XBF16>& in) {
   constexpr int LOGE = S::LOGE, E = S::E, NB = S::NB, N = S::N, M = S::SEGS / (S::ROWS_PER_PASS / S::R);
@@ -393,6 +395,8 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   constexpr int L = S::L, NPH = S::NPH;
   constexpr int RAW = XBF16 ? E / 8 : E / 4;  // 16-byte vectors per segment
   constexpr bool QUANT = QM != Q_NONE;
+  constexpr int LD = XS * N;  // row stride of x and y in elements
+  static_assert(XS == 1 || (!QUANT && M == 1), "strided rows: plain butterfly, rows only");
   static_assert(global_transposes<S>() % 2 == 0, "buffer alternation assumes an even count");
 
   float* const lbuf = lds + team * (SEGS * SEGW);          // wave-local transposes
@@ -416,16 +420,16 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
   // groups past the end and lanes with nothing to store fall outside the
   // ranges, so no memory instruction sits under a branch and the compiler
   // can keep every prefetch in flight.
-  constexpr int64_t GRP_ELEMS = (int64_t)RPP * N;
+  constexpr int64_t GRP_ELEMS = (int64_t)RPP * LD;
   // Element of the thread's register 0 within a row segment: the two-phase
   // plan's layout A for the scaled form, register-contiguous blocks for the
   // three-shear form.
   const int elem0 = FAST ? fwd_elem_a(t, 0, S::PL) : t * E;
-  const int thr_elem = team * RPT * N + elem0;  // element offset of (team, t) in a group
+  const int thr_elem = team * RPT * LD + elem0;  // element offset of (team, t) in a group
 
   constexpr int PD = S::PD;
   auto& cur = in.r;
-  auto load = [&](int64_t grp, int d) { load_group<S, XBF16>(P, rows, grp, in, d, team, elem0); };
+  auto load = [&](int64_t grp, int d) { load_group<S, XBF16, XS>(P, rows, grp, in, d, team, elem0); };
 
   // The previous row group's outputs: bf16 rows, codes and scales (and, for
   // fp32 output, its rows), stored only once the next group's input has
@@ -445,8 +449,8 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
     if (YK == Y_NONE && !QUANT) return;
     const int64_t hg = held_grp;
     const uint32_t vr = (uint32_t)group_rows(rows, hg, RPP);  // at most RPP rows: 32-bit sizes
-    const auto ry = buffer_range32(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * (N * 2));
-    const auto ry4 = buffer_range32(reinterpret_cast<const float*>(P.y) + hg * GRP_ELEMS, vr * (N * 4));
+    const auto ry = buffer_range32(reinterpret_cast<const uint16_t*>(P.y) + hg * GRP_ELEMS, vr * (LD * 2));
+    const auto ry4 = buffer_range32(reinterpret_cast<const float*>(P.y) + hg * GRP_ELEMS, vr * (LD * 4));
     const auto rc = buffer_range32(P.codes + hg * (GRP_ELEMS * bits / 8), vr * (uint32_t)(N * bits / 8));
     const auto rsc = buffer_range32(P.scales + hg * RPP * ngroups_row, vr * (uint32_t)(ngroups_row * 2));
     const auto rz = buffer_range32(P.zeros + hg * RPP * ngroups_row, vr * (uint32_t)(ngroups_row * 2));
@@ -455,7 +459,7 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
 #pragma unroll
       for (int a = 0; a < M; ++a) {
         const int sg = rr * M + a;
-        const uint32_t el = (uint32_t)(thr_elem + rr * N + a * NB);
+        const uint32_t el = (uint32_t)(thr_elem + rr * LD + a * NB);
         if (YK == Y_BF16) {
 #pragma unroll
           for (int c = 0; c < E / 8; ++c)
@@ -827,11 +831,19 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
 // One kernel per (input type, output kind, quantizer format): the host picks
 // the variant, so each kernel holds just the two row loops below and the
 // register allocator sees one loop nest at a time.
-template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM>
+template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM, int XS = 1>
 __global__ void __launch_bounds__((FwdShape<LOGNB, M, RPT>::NT))
 fwd_kernel(FwdParams P) {
   using S = FwdShape<LOGNB, M, RPT>;
   constexpr int LOGE = S::LOGE, E = S::E, T = S::T, NB = S::NB, L = S::L;
+  if constexpr (XS != 1) {
+    // Halves of rows XS times longer (fp32 out): blockIdx.y picks the half,
+    // its columns and its table (the half tables lie one after the other).
+    const int h = blockIdx.y;
+    P.x = static_cast<const char*>(P.x) + (size_t)h * NB * (XBF16 ? 2 : 4);
+    P.y = static_cast<float*>(P.y) + (size_t)h * NB;
+    P.tab = table_at(reinterpret_cast<const char*>(P.tab.cs) + (size_t)h * table_bytes(LOGNB), LOGNB);
+  }
   extern __shared__ float4 lds_raw[];
   float* const lds = reinterpret_cast<float*>(lds_raw);
   const int tid = threadIdx.x;
@@ -887,7 +899,7 @@ fwd_kernel(FwdParams P) {
   InRegs<S, XBF16> in;
 #pragma unroll
   for (int d = 0; d < S::PD; ++d)
-    load_group<S, XBF16>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team,
+    load_group<S, XBF16, XS>(P, P.rows, (int64_t)blockIdx.x + (int64_t)d * gridDim.x, in, d, team,
                          fwd_elem_a(t, 0, S::PL));  // the scaled form's layout A
   load_fast(P.tab.fgt);
   __builtin_amdgcn_sched_barrier(0);
@@ -910,34 +922,36 @@ fwd_kernel(FwdParams P) {
   scale_last();
   // The two forms run as consecutive loops, not as two arms of a branch:
   // the register allocator then never holds both coefficient sets at once.
-  const bool usable = row_loop<S, XBF16, YK, QM, true, true, true>(P, P.rows, lds, team, t, C, in);
+  const bool usable = row_loop<S, XBF16, YK, QM, true, true, true, XS>(P, P.rows, lds, team, t, C, in);
   if (!usable) {
     // Three-shear form, with the general quantizer for every format.
     load_coeffs(P.tab.lift, P.tab.last);
     scale_last();
-    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false, false>(P, P.rows, lds, team, t, C, in);
+    row_loop<S, XBF16, YK, (QM == Q_NONE ? Q_NONE : Q_ANY), false, false, false, XS>(P, P.rows, lds, team, t,
+                                                                                    C, in);
   }
 }
 
 // Host-side launch: pick the variant, size the persistent grid (cached per
 // variant on first use).
-template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM>
+template <int LOGNB, int M, int RPT, bool XBF16, int YK, int QM, int XS = 1>
 hipError_t launch_fwd_variant(const FwdParams& p, hipStream_t stream) {
   using S = FwdShape<LOGNB, M, RPT>;
-  auto kern = fwd_kernel<LOGNB, M, RPT, XBF16, YK, QM>;
+  auto kern = fwd_kernel<LOGNB, M, RPT, XBF16, YK, QM, XS>;
   int blocks_per_cu = 0, num_cu = 0;
   const hipError_t e =
       kernel_setup(reinterpret_cast<const void*>(kern), S::NT, S::LDS_BYTES, &blocks_per_cu, &num_cu);
   if (e != hipSuccess) return e;
   const int64_t ngrp = (p.rows + S::ROWS_PER_PASS - 1) / S::ROWS_PER_PASS;
-  const int64_t cap = (int64_t)blocks_per_cu * num_cu;
+  // XS halves run side by side (grid y): together they fill the device once
+  const int64_t cap = ((int64_t)blocks_per_cu * num_cu + XS - 1) / XS;
   const int grid = (int)(ngrp < cap ? ngrp : cap);
+  const dim3 g3((unsigned)grid, (unsigned)XS);
   const LaunchEvents ev = take_forward_events();
   if (ev.start != nullptr || ev.stop != nullptr)  // timestamps of this dispatch itself
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, ev.start, ev.stop,
-                          0u, p);
+    hipExtLaunchKernelGGL(kern, g3, dim3(S::NT), S::LDS_BYTES, stream, ev.start, ev.stop, 0u, p);
   else
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), S::LDS_BYTES, stream, p);
+    hipLaunchKernelGGL(kern, g3, dim3(S::NT), S::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

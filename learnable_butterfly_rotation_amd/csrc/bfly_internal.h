@@ -196,6 +196,27 @@ hipError_t launch_prepare(const float* theta, void* table, int logn, hipStream_t
                           bool hadamard = false);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);
 
+// The butterfly of length 8192 (two passes, bfly_fwd8k.hip).  Its table:
+// the two half tables (n = 4096 layout), then (cos, sin) of stage 12's
+// 4096 angles, table8k_bytes() in all.
+struct Fwd8kParams {
+  const void* x;      // [rows][8192], bf16 (x_bf16) or fp32
+  int32_t x_bf16;
+  void* y;            // [rows][8192] of y_kind, or nullptr
+  int32_t y_kind;     // YKind
+  uint8_t* codes;     // nullptr: no quantization
+  uint16_t* scales;
+  uint16_t* zeros;
+  int32_t bits, group, asym;
+  int64_t rows;
+  const void* table;  // table8k_bytes()
+  float* v;           // [rows][8192] fp32 scratch between the passes
+};
+size_t table8k_bytes();
+// The table of n = 8192 from theta (or of H_8192), in one launch.
+hipError_t launch_prepare_8192(const float* theta, void* table, bool hadamard, hipStream_t s);
+hipError_t launch_forward_8192(const Fwd8kParams& p, hipStream_t s);
+
 // Events attached to the next forward-kernel dispatch (kernel-only timing):
 // returns the pair armed by bfly_time_next_forward and disarms it (both null
 // when nothing is armed).

@@ -92,8 +92,20 @@ def test_forward_validation(L):
     assert fwd(L, n=100) == SIZE
     assert fwd(L, n=0) == SIZE
     assert fwd(L, n=32) == UNSUPPORTED
-    assert fwd(L, n=8192) == UNSUPPORTED
     assert fwd(L, n=16384) == UNSUPPORTED
+    # n = 8192 always needs its workspace: the table area, then the fp32 rows
+    # between its two passes
+    w8 = B.bfly_forward_workspace_bytes(4, 8192)
+    assert w8 == (B.bfly_coeff_bytes(8192) + 255) // 256 * 256 + 4 * 8192 * 4
+    assert B.bfly_coeff_bytes(8192) == 2 * B.bfly_coeff_bytes(4096) + 4096 * 8
+    assert B.bfly_forward_workspace_bytes(4, 4096) == B.bfly_coeff_bytes(4096)
+    assert B.bfly_forward_workspace_bytes(-1, 8192) == 0
+    assert B.bfly_forward_workspace_bytes(4, 100) == 0
+    assert fwd(L, n=8192, rows=0, wsb=w8) == OK
+    assert fwd(L, n=8192, rows=0, co=CO, th=None, ws=None, wsb=0) == NULL
+    assert fwd(L, n=8192, rows=4, wsb=w8 - 1) == WORKSPACE
+    assert fwd(L, n=8192, rows=-1, wsb=w8) == SIZE
+    assert fwd(L, n=8192, rows=0, x=ctypes.c_void_p(0x10008), wsb=w8) == ALIGN
     assert fwd(L, x=ctypes.c_void_p(0x10008)) == ALIGN
     assert fwd(L, y=ctypes.c_void_p(0x20004)) == ALIGN
     assert fwd(L, co=ctypes.c_void_p(0x90008), rows=0) == ALIGN
@@ -131,6 +143,8 @@ def test_forward_quant_validation(L):
     assert fq(L, group=512, n=256) == QUANT           # group larger than the row
     for g in (8, 16, 32, 64, 128, 256, 512):
         assert fq(L, group=g) == OK
+        assert fq(L, group=g, n=8192, wsb=B.bfly_forward_workspace_bytes(0, 8192)) == OK
+    assert fq(L, group=1024, n=8192, wsb=1 << 30) == QUANT
     assert fq(L, c=ctypes.c_void_p(0x30004)) == ALIGN
     assert fq(L, s=ctypes.c_void_p(0x40001)) == ALIGN
     assert fq(L, ws=None) == NULL

@@ -435,6 +435,86 @@ def test_forward_from_angles_under_stream_capture():
         del g
 
 
+# ---------------------------------------------------------------------------
+# n = 8192: two passes (stages 0..11 on each half, then stage 12 with the
+# output and the quantizer)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows", [1, 37, 300])
+@pytest.mark.parametrize("x_dt,y_dt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_forward_8192(rows, x_dt, y_dt):
+    """Every row against the oracle; the call from angles and the call on the
+    table bfly_prepare made agree bit for bit."""
+    rng = np.random.default_rng(5000 + rows)
+    n = 8192
+    th = rand_theta(rng, n)
+    cols = inputs.outlier_columns(rng, n)
+    x = inputs.activations(rng, rows, n, cols, x_dt)
+    tdt = torch.float32 if y_dt == "f32" else torch.bfloat16
+    y = empty((rows, n), tdt)
+    B.bfly_forward(dev(x), y, theta=dev(th))
+    got = host(y)
+    y64 = oracle.forward(x, th)
+    print("n=8192 forward", x_dt, y_dt, rows, assert_forward(got, y64, x, n))
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare(dev(th), n, tab)
+    y2 = empty((rows, n), tdt)
+    B.bfly_forward(dev(x), y2, coeffs=tab)
+    assert np.array_equal(got, host(y2))
+
+
+@pytest.mark.parametrize("bits,group,mode", [(4, 128, 0), (2, 128, 1), (4, 8, 1), (2, 512, 0),
+                                             (4, 64, 0)])
+def test_forward_quant_8192(bits, group, mode):
+    rng = np.random.default_rng(5100 + bits * 1000 + group + mode)
+    n, rows = 8192, 301
+    th = rand_theta(rng, n)
+    cols = inputs.outlier_columns(rng, n)
+    x = inputs.activations(rng, rows, n, cols, "bf16")
+    out = run_quant(x, th, bits, group, mode)
+    y64 = oracle.forward(x, th)
+    rf = assert_forward(out["y"], y64, x, n)
+    rq = assert_quant(out, y64, bits, group, mode)
+    print("n=8192 quant", bits, group, mode, rf, rq)
+    codes_only = run_quant(x, th, bits, group, mode, with_y=False)
+    for k in codes_only:
+        assert np.array_equal(codes_only[k], out[k]), k
+
+
+def test_forward_quant_8192_batch():
+    """2048 bf16 rows of n = 8192 with outlier channels, sym INT4 g128: every
+    row, element by element (the headline's format at twice the width)."""
+    rng = np.random.default_rng(5200)
+    n, rows = 8192, 2048
+    th = rand_theta(rng, n)
+    cols = inputs.outlier_columns(rng, n)
+    x = inputs.activations(rng, rows, n, cols, "bf16")
+    out = run_quant(x, th, 4, 128, 0)
+    y64 = oracle.forward(x, th)
+    print("n=8192 batch:", assert_forward(out["y"], y64, x, n), assert_quant(out, y64, 4, 128, 0))
+    part = run_quant(x[:5], th, 4, 128, 0)
+    for k in part:
+        assert np.array_equal(out[k][:5], part[k]), k
+
+
+def test_forward_8192_in_place_and_hadamard():
+    rng = np.random.default_rng(5300)
+    n, rows = 8192, 64
+    th = rand_theta(rng, n)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    xd = dev(x)
+    B.bfly_forward(xd, xd, theta=dev(th))
+    assert_forward(host(xd), oracle.forward(x, th), x, n)
+    # H_8192 from its table: the halves' tables start with the diagonal's
+    # signs, the last stage is pi/4 from exact constants
+    tab = torch.empty(B.bfly_coeff_bytes(n), dtype=torch.uint8, device="cuda")
+    B.bfly_prepare_hadamard(n, tab)
+    xs = x[:8]
+    y = empty((8, n), torch.float32)
+    B.bfly_forward(dev(xs), y, coeffs=tab)
+    assert_forward(host(y), oracle.hadamard(xs), xs, n)
+
+
 def test_zero_angles_identity_bit_exact():
     rng = np.random.default_rng(4)
     x = inputs.f32_to_bf16_bits(rng.standard_normal((20, 512)).astype(np.float32))

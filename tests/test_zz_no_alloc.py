@@ -75,7 +75,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     L = B.lib()
-    # n = 8192 is beyond the scratch (and the forward); nothing is launched
+    # n = 8192 is beyond the scratch; nothing is launched
     st = L.bfly_forward_quant_noalloc(0x10000, 1, 0x20000, 1, 0x30000, 0x40000, None, 4, 8192,
                                       0x60000, 4, 128, 0, None)
     assert st == 7, st   # BFLY_ERR_UNSUPPORTED
