@@ -236,9 +236,12 @@ bfly_status bfly_kron_forward(const void* x, bfly_dtype x_dt, void* y, bfly_dtyp
 /* Kronecker composites with more segments: the same y[r] = (O kron
  * B(theta_b)) x[r] and optional quantization as bfly_kron_forward, for
  * m in [2, 64] (e.g. 11008 = 43 * 256), nb a power of two in [256, 4096],
- * m * nb <= 65536.  Two passes: v = (O kron I) x in fp32 into `workspace`,
- * then the butterfly with its fused quantizer on the rows * m segments of v
- * ((O kron B) = (I kron B)(O kron I)).  workspace: >=
+ * m * nb <= 65536.  bf16 rows with nb = 256 (e.g. 11008) run in one pass
+ * (per row: the mix on the matrix cores into LDS, then the butterfly and
+ * the quantizer on each segment); otherwise two passes: v = (O kron I) x in
+ * fp32 into `workspace`, then the butterfly with its fused quantizer on the
+ * rows * m segments of v ((O kron B) = (I kron B)(O kron I)).  y == x is
+ * allowed.  workspace (either way): >=
  * bfly_kron_forward_wide_workspace_bytes(rows, m, nb) bytes of device
  * memory (the table's bytes rounded up to 256, then rows * m * nb * 4),
  * 16-byte aligned, caller-owned.  codes == NULL => no quantization

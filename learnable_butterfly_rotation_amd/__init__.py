@@ -250,8 +250,9 @@ def bfly_kron_forward_wide_workspace_bytes(rows: int, m: int, nb: int) -> int:
 def bfly_kron_forward_wide(x, y, mix, workspace, codes=None, scales=None, zeros=None,
                            theta_b=None, coeffs_b=None, bits=4, group=128,
                            mode=BFLY_SYM_ABSMAX, stream=None) -> None:
-    """(O kron B) on rows of n = m * nb for m up to 64 (two passes through
-    `workspace`, a uint8 tensor of bfly_kron_forward_wide_workspace_bytes)."""
+    """(O kron B) on rows of n = m * nb for m up to 64 (`workspace`: a uint8
+    tensor of bfly_kron_forward_wide_workspace_bytes; bf16 rows with nb = 256
+    run in one pass, others in two through the workspace)."""
     rows, n = x.shape
     m = mix.shape[0]
     _check(lib().bfly_kron_forward_wide(

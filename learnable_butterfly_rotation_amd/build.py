@@ -25,7 +25,8 @@ SOURCES = [("bfly_api.hip", "bfly_api.o", []), ("bfly_bwd.hip", "bfly_bwd.o", []
            ("bfly_kron_mix.hip", "bfly_kron_mix.o", []),
            ("bfly_calib.hip", "bfly_calib.o", []),
            ("bfly_calib_w.hip", "bfly_calib_w.o", []),
-           ("bfly_fwd8k.hip", "bfly_fwd8k.o", [])] + \
+           ("bfly_fwd8k.hip", "bfly_fwd8k.o", []),
+           ("bfly_kron_fused.hip", "bfly_kron_fused.o", [])] + \
           [("bfly_fwd_kron.hip", "bfly_fwd_kron_m%d.o" % m, ["-DKRON_M=%d" % m]) for m in range(2, 9)]
 
 FLAGS = [

@@ -520,6 +520,32 @@ bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly
   if (st != BFLY_OK) return st;
   if (rows == 0) return BFLY_OK;
   const hipStream_t s = (hipStream_t)hip_stream;
+  if (bfly::kron_fused_supported(m, nb, x_dt == BFLY_BF16)) {
+    // one pass: the mix, the butterfly and the quantizer per row (the
+    // workspace holds only the table, when it comes from theta_b)
+    const void* tab = coeffs_b;
+    if (!tab) {
+      const hipError_t e = bfly::launch_prepare(theta_b, ws, l, s);
+      if (e != hipSuccess) return hip_fail(e);
+      tab = ws;
+    }
+    bfly::KronFusedParams f;
+    f.x = x;
+    f.y = y;
+    f.y_bf16 = y_dt == BFLY_BF16;
+    f.codes = quant ? codes : nullptr;
+    f.scales = quant ? scales : nullptr;
+    f.zeros = quant ? zeros : nullptr;
+    f.bits = quant ? bits : 0;
+    f.group = quant ? group : 0;
+    f.asym = quant && mode == BFLY_ASYM_MINMAX;
+    f.mix = mix;
+    f.cs = bfly::table_at(tab, l).cs;
+    f.rows = rows;
+    f.m = m;
+    const hipError_t e = bfly::launch_kron_fused(f, s);
+    return e == hipSuccess ? BFLY_OK : hip_fail(e);
+  }
   const hipError_t e = bfly::launch_kron_mix(x, x_dt == BFLY_BF16, v, mix, rows, m, nb, s);
   if (e != hipSuccess) return hip_fail(e);
   return forward_run(p, theta_b, coeffs_b, ws, s);

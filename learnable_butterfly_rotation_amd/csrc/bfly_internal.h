@@ -217,6 +217,24 @@ size_t table8k_bytes();
 hipError_t launch_prepare_8192(const float* theta, void* table, bool hadamard, hipStream_t s);
 hipError_t launch_forward_8192(const Fwd8kParams& p, hipStream_t s);
 
+// The wide Kronecker composite in one pass (bfly_kron_fused.hip): segments
+// of 256, bf16 rows, m in [2, 64].
+struct KronFusedParams {
+  const void* x;       // [rows][m * 256] bf16
+  void* y;             // [rows][m * 256] bf16 (y_bf16) or fp32, or nullptr
+  int32_t y_bf16;
+  uint8_t* codes;      // nullptr: no quantization
+  uint16_t* scales;
+  uint16_t* zeros;
+  int32_t bits, group, asym;
+  const float* mix;    // [m][m] fp32
+  const float2* cs;    // the table's (cos, sin) of B's 8 x 128 pairs
+  int64_t rows;
+  int32_t m;
+};
+bool kron_fused_supported(int m, int nb, bool xbf16);
+hipError_t launch_kron_fused(const KronFusedParams& p, hipStream_t s);
+
 // Events attached to the next forward-kernel dispatch (kernel-only timing):
 // returns the pair armed by bfly_time_next_forward and disarms it (both null
 // when nothing is armed).

@@ -886,10 +886,10 @@ def test_kron_backward(m, nb, rows):
 # ---------------------------------------------------------------------------
 
 def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=torch.bfloat16,
-                  coeffs=False):
+                  coeffs=False, with_y=True):
     rows, n = x.shape
     m = mix.shape[0]
-    y = empty((rows, n), y_dtype)
+    y = empty((rows, n), y_dtype) if with_y else None
     ws = torch.empty(B.bfly_kron_forward_wide_workspace_bytes(rows, m, n // m), dtype=torch.uint8,
                      device="cuda")
     args = {}
@@ -905,7 +905,7 @@ def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=tor
     else:
         args["theta_b"] = dev(th)
     B.bfly_kron_forward_wide(dev(x), y, dev(mix), ws, bits=bits, group=group, mode=mode, **args)
-    out = {"y": host(y)}
+    out = {"y": host(y)} if with_y else {}
     if quant:
         out["codes"] = host(args["codes"])
         out["scales"] = host(args["scales"])
@@ -918,7 +918,7 @@ def run_kron_wide(x, th, mix, quant=True, bits=4, group=128, mode=0, y_dtype=tor
 # tiles; one to four 16-deep k steps) and its edges (17, 32, 33, 48, 49).
 @pytest.mark.parametrize("m,nb", [(43, 256), (9, 512), (16, 1024), (64, 256), (2, 4096),
                                   (5, 1024), (16, 4096), (17, 256), (32, 512), (33, 256),
-                                  (48, 256), (49, 512)])
+                                  (48, 256), (49, 512), (2, 256), (16, 256)])
 def test_kron_wide_shapes(m, nb):
     rng = np.random.default_rng(7000 + 10 * m + nb)
     th = rand_theta(rng, nb)
@@ -934,6 +934,36 @@ def test_kron_wide_shapes(m, nb):
     xf = rng.standard_normal((5, m * nb)).astype(np.float32)
     out = run_kron_wide(xf, th, mix, quant=False, y_dtype=torch.float32, coeffs=True)
     assert_forward(out["y"], oracle.kron_forward(xf, th, mix), xf, m * nb)
+
+
+@pytest.mark.parametrize("m", [2, 16, 43, 64])
+def test_kron_wide_one_pass(m):
+    """bf16 rows with nb = 256 take the one-pass kernel (mix on the matrix
+    cores into LDS, butterfly and quantizer per segment): fp32, bf16 and no
+    output, groups of 8 to 256, both modes and widths, in place."""
+    rng = np.random.default_rng(7500 + m)
+    nb, rows = 256, 45
+    th = rand_theta(rng, nb)
+    mix = inputs.mixing_factor(rng, m)
+    cols = inputs.outlier_columns(rng, m * nb)
+    x = inputs.activations(rng, rows, m * nb, cols, "bf16")
+    y64 = oracle.kron_forward(x, th, mix)
+    out = run_kron_wide(x, th, mix, quant=False, y_dtype=torch.float32)
+    print("one pass m=%d fp32:" % m, assert_forward(out["y"], y64, x, m * nb))
+    for bits, group, mode in ((4, 8, 1), (2, 64, 0), (2, 256, 1), (4, 128, 0)):
+        out = run_kron_wide(x, th, mix, bits=bits, group=group, mode=mode)
+        assert_forward(out["y"], y64, x, m * nb)
+        print("one pass m=%d" % m, bits, group, mode, assert_quant(out, y64, bits, group, mode))
+        only = run_kron_wide(x, th, mix, bits=bits, group=group, mode=mode, with_y=False)
+        for k in only:
+            assert np.array_equal(only[k], out[k]), k
+    # in place
+    xd = dev(x)
+    ws = torch.empty(B.bfly_kron_forward_wide_workspace_bytes(rows, m, nb), dtype=torch.uint8,
+                     device="cuda")
+    B.bfly_kron_forward_wide(xd, xd, dev(mix), ws, theta_b=dev(th))
+    ref = run_kron_wide(x, th, mix, quant=False)
+    assert np.array_equal(host(xd), ref["y"])
 
 
 def test_kron_wide_workload_full():
