@@ -541,6 +541,7 @@ bfly_status bfly_kron_forward_wide(const void* x, bfly_dtype x_dt, void* y, bfly
     f.asym = quant && mode == BFLY_ASYM_MINMAX;
     f.mix = mix;
     f.cs = bfly::table_at(tab, l).cs;
+    f.fgt = reinterpret_cast<const float*>(bfly::table_at(tab, l).fgt);
     f.rows = rows;
     f.m = m;
     const hipError_t e = bfly::launch_kron_fused(f, s);

@@ -229,6 +229,7 @@ struct KronFusedParams {
   int32_t bits, group, asym;
   const float* mix;    // [m][m] fp32
   const float2* cs;    // the table's (cos, sin) of B's 8 x 128 pairs
+  const float* fgt;    // the table's scaled form (forward layout)
   int64_t rows;
   int32_t m;
 };
