@@ -405,8 +405,10 @@ size_t bfly_calib_step_weight_workspace_bytes(int64_t rows, int32_t out, int32_t
  *            the inputs
  *   w[o][k] = scale * q (symmetric) or scale * (q - zero) (asymmetric).
  * Arithmetic: sums of a * (q - zero) in fp32 (exact products) over one
- * group (or over 16 codes when rows <= 64), each times its group's scale
- * and added in fp32.
+ * group, each times its group's scale and added in fp32.  With rows <= 64
+ * the group sum is formed as C - zero * S from the fp32 sums C of a * q
+ * (q the code as offset binary: a symmetric code plus 2^(bits-1), with
+ * that as its zero point) and S of a, over the group.
  * Sizes: bits 2 or 4; k a multiple of 64 in [64, 65536]; group one of 64,
  * 128, 256, 512 dividing k; n_out a positive multiple of 128 with
  * n_out <= 1048576.  rows == 0 is a no-op.  Errors: BFLY_ERR_NULL,

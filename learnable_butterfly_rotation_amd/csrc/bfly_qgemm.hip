@@ -18,6 +18,7 @@
 // v_mfma_f32_32x32x16_bf16 tiles (64 x 64 outputs).  Each weight code is
 // decoded once per workgroup (by one thread) and then read by the four
 // waves of its output columns.
+#include <algorithm>
 #include <type_traits>
 
 #include "bfly_common.h"
@@ -287,192 +288,385 @@ __global__ __launch_bounds__(QTile<BM>::THREADS, BM == 128 ? 2 : 1) void qgemm_k
       }
 }
 
-// Few rows (decode time: one to a few dozen tokens): the product is bound by
-// reading and decoding the codes once, and MFMA tiles of 256 rows would be
-// mostly padding.  One wave per QV_OPW weight rows; lane l takes QV_KU
-// consecutive codes per step (k = QV_KU l + 64 QV_KU i, inside one group:
-// group >= 64); with QV_KU = 64 a row of 4096 codes is one step with every
-// load in flight at once.  The codes are decoded to
-// exact bf16 pairs as above; for each of the MR activation rows the 64-term
-// sum is formed with v_dot2c_f32_bf16 (exact products), scaled by the
-// group's scale and accumulated in fp32.  The 64 lanes' sums are then added
-// by an xor-shuffle tree (fixed order) and lane m * QV_OPW + r stores y[m][r].
-constexpr int QV_OPW = 4;   // weight rows per wave
+// Few rows on the matrix cores.  Codes are decoded by the chip's format
+// converters: a 2-bit code masked into a nibble is the fp4 (e2m1) number
+// q / 2, a 4-bit code masked into a byte the fp8 (e4m3) number q 2^-9, and
+// v_cvt_scalef32_pk_bf16_fp4 / _fp8 with the scale 2 (2^9) give two of
+// them as the bf16 pair of the integers q, exactly.  Masking a 16-code word
+// (2-bit) into its even and odd nibbles, or an 8-code word (4-bit) into its
+// even and odd bytes, gives the pairs (q0, q2) (q1, q3) (q4, q6) (q5, q7) of
+// every eight codes: 11 vector operations per 16 two-bit codes.  Symmetric
+// codes have their sign bit flipped in the same masking (offset binary,
+// z = 2^(bits-1)).
+// The products run on v_mfma_f32_16x16x32_bf16: up to 16 activation rows
+// are A (rows past the end read as zero, or repeat the last row), 16 weight
+// rows are B; lane l holds eight k of block l / 16 of row l % 16 in both
+// operands (the activations re-paired to the codes' pair order), and
+// C[4 (l / 16) + i][l % 16].
+// Zero points: per group the codes give C = sum a q, a second product
+// against ones gives S = sum a, and the group adds s (C - z S).  Each
+// product a q is exact; the sums are fp32.
+// Work split: a workgroup per 16 weight rows with one wave per 1024 codes
+// of k (up to MAXW waves; each takes a run of whole groups, in passes of
+// 1024), the waves' sums added through LDS in fixed order.  A wave reads
+// its codes in segments of 256 per row: lane l loads 16 (4-bit: 32)
+// contiguous bytes of row l % 16, four lanes 64 (128) contiguous bytes.  A
+// 4 x 4 transpose of dwords across the four 16-lane rows
+// (v_permlane32_swap, then v_permlane16_swap) leaves lane l with codes
+// 16 (l / 16) .. + 15 (4-bit: 8 (l / 16) .. + 7 and 32 + 8 (l / 16) .. + 7)
+// of each 64-code chunk, so that the 32 codes of a step lie in one chunk,
+// inside one group.  Each wave stages the scales and zero points of its
+// groups, and (up to four rows) its activations, in its own part of LDS:
+// those loads are issued before the codes, so waiting for them leaves the
+// codes in flight (loads complete in issue order), and no workgroup
+// barrier comes before the k loop.
+constexpr int QV_PASS = 16;       // 64-code chunks per wave and pass (1024 codes)
+constexpr int QV_LDS_ROWS = 4;    // activation rows staged in LDS at most
+constexpr int QV_AW = 4;          // chunks of activations in flight (rows read from memory)
+// waves per workgroup at most (the launch bound: more waves leave fewer
+// registers per lane)
+__host__ __device__ constexpr int qv_maxw(int bits, int q, int ni) {
+  return (bits == 2 && q >= 2 && ni <= 2) ? 16 : 8;
+}
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 2.0f, SEL));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 512.0f, HI));
+}
 
-template <int BITS, bool ASYM, bool YBF16, int MR, int QV_KU>
-__global__ __launch_bounds__(256) void qgemv_kernel(const QgemmParams P) {
-  static_assert(MR * QV_OPW <= 64, "one lane per output");
-  constexpr int NW = QV_KU * BITS / 32;  // code words per lane per row and step
-  const int lane = threadIdx.x & 63;
-  const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * QV_OPW;  // n_out % 16 == 0
-  const int K = P.k, G = P.group, N = P.n_out, NG = K / G;
-  const int KB = K * BITS / 8;
-  const int64_t m0 = (int64_t)blockIdx.y * MR;
-  const int mrows = group_rows(P.rows, blockIdx.y, MR);
-  const auto ra = buffer_range32(P.a + m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
-  const auto rc = buffer_range32(P.codes + (int64_t)o0 * KB, (uint32_t)(QV_OPW * KB));
-  const auto rs = buffer_range32(P.scales + (int64_t)o0 * NG, (uint32_t)(QV_OPW * NG * 2));
-  const auto rz = buffer_range32(ASYM ? P.zeros + (int64_t)o0 * NG : P.scales,
-                                 ASYM ? (uint32_t)(QV_OPW * NG * 2) : 0u);
-  float acc[MR][QV_OPW];
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int r = 0; r < QV_OPW; ++r) acc[m][r] = 0.f;
-  for (int k0 = lane * QV_KU; k0 < K; k0 += 64 * QV_KU) {
-    const int g = k0 / G;
-    uint32_t cw[QV_OPW][NW];
-    uint16_t sb[QV_OPW], zb[QV_OPW];
-#pragma unroll
-    for (int r = 0; r < QV_OPW; ++r) {
-      const uint32_t off = (uint32_t)(r * KB + k0 * BITS / 8);
-      if (NW == 1) {
-        cw[r][0] = buf_ld4(rc, off);
-      } else if (NW == 2) {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)off, 0, 0);
-        cw[r][0] = v.x;
-        cw[r][NW - 1] = v.y;
-      } else {
-#pragma unroll
-        for (int h = 0; h < NW / 4; ++h) {
-          const uint4 v = buf_ld16(rc, off + 16 * h);
-          cw[r][4 * h] = v.x;
-          cw[r][(4 * h + 1) % NW] = v.y;
-          cw[r][(4 * h + 2) % NW] = v.z;
-          cw[r][(4 * h + 3) % NW] = v.w;
-        }
-      }
-      const uint32_t so = (uint32_t)((r * NG + g) * 2);
-      sb[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
-      zb[r] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(rz, (int)so, 0, 0) : (uint16_t)0;
-    }
-    if constexpr (BITS == 2 && MR == 1) {
-      // One activation row, 2-bit codes: decode through a byte permute.  The
-      // four values q - z of the row's group are bf16 entries of an 8-byte
-      // table (exact small integers); codes i and i + 8 of a 16-code word sit
-      // 16 bits apart, so one shift and mask put them in the two halves of
-      // t, t * 0x202 + 0x01000100 is the byte selector of their table
-      // entries, and v_perm_b32 gives the pair (w_i, w_i+8).  The activations
-      // are re-paired the same way once, for all the weight rows.
-      uint32_t pa[QV_KU / 2];
-      {
-        const uint32_t ao = (uint32_t)k0 * 2u;
-#pragma unroll
-        for (int u = 0; u < QV_KU / 16; ++u) {
-          const uint4 v0 = buf_ld16(ra, ao + 32 * u), v1 = buf_ld16(ra, ao + 32 * u + 16);
-          const uint32_t av[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            pa[8 * u + i] = __builtin_amdgcn_perm(av[4 + i / 2], av[i / 2],
-                                                  (i & 1) ? 0x07060302u : 0x05040100u);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < QV_OPW; ++r) {
-        uint32_t lut_lo, lut_hi;
-        if (ASYM) {
-          const float z = half_to_float(zb[r]);
-          lut_lo = pack_exact(-z, 1.f - z);
-          lut_hi = pack_exact(2.f - z, 3.f - z);
-        } else {  // two's complement: 0, 1, -2, -1
-          lut_lo = 0x3F800000u;  // (0, 1)
-          lut_hi = 0xBF80C000u;              // (-2, -1)
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int u = 0; u < QV_KU / 16; ++u) {
-          const uint32_t x = cw[r][u];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t tq = (x >> (2 * i)) & 0x00030003u;
-            const uint32_t w = __builtin_amdgcn_perm(lut_hi, lut_lo, tq * 0x202u + 0x01000100u);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pa[8 * u + i]),
-                                                   __builtin_bit_cast(bf16x2_t, w), part, false);
-          }
-        }
-        acc[0][r] = fmaf(half_to_float(sb[r]), part, acc[0][r]);
-      }
-      continue;
-    }
-    // one weight row at a time (its 32 decoded words), against every
-    // activation row (re-read from the cache for each weight row)
-#pragma unroll
-    for (int r = 0; r < QV_OPW; ++r) {
-      const float z = ASYM ? half_to_float(zb[r]) : (float)(1 << (BITS - 1));
-      uint32_t w[QV_KU / 2];
-#pragma unroll
-      for (int u = 0; u < QV_KU / 16; ++u) {
-        uint32_t x[BITS / 2];
-#pragma unroll
-        for (int h = 0; h < BITS / 2; ++h) {
-          const uint32_t v = cw[r][u * (BITS / 2) + h];
-          x[h] = ASYM ? v : v ^ (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);
-        }
-        uint32_t wu[8];
-        decode16<BITS>(x, z, wu);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[8 * u + i] = wu[i];
-      }
-      const float sr = half_to_float(sb[r]);
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const uint32_t ao = (uint32_t)(m * K + k0) * 2u;
-        float part = 0.f;
-#pragma unroll
-        for (int q = 0; q < QV_KU / 8; ++q) {
-          const uint4 v = buf_ld16(ra, ao + 16 * q);
-          const uint32_t av[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[i]),
-                                                   __builtin_bit_cast(bf16x2_t, w[4 * q + i]),
-                                                   part, false);
-        }
-        acc[m][r] = fmaf(sr, part, acc[m][r]);
-      }
-    }
-  }
-  // lane sums, fixed-order tree; every lane ends with every total
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int r = 0; r < QV_OPW; ++r) acc[m][r] += __shfl_xor(acc[m][r], off, 64);
-  float mine = 0.f;
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int r = 0; r < QV_OPW; ++r)
-      if (lane == m * QV_OPW + r) mine = acc[m][r];
-  if (lane < MR * QV_OPW) {  // rows past the end fall outside the range
-    constexpr int YSZ = YBF16 ? 2 : 4;
-    const auto ry = buffer_range32(static_cast<char*>(P.y) + m0 * N * YSZ,
-                                   (uint32_t)mrows * (uint32_t)N * YSZ);
-    const uint32_t off = (uint32_t)((lane / QV_OPW) * N + o0 + lane % QV_OPW) * YSZ;
-    if (YBF16) buf_st2(ry, off, (uint16_t)pack_bf16(mine, 0.f));
-    else buf_st4(ry, off, __float_as_uint(mine));
+// Activations (a0 .. a7) of one step in the codes' pair order:
+// (a0, a2) (a1, a3) (a4, a6) (a5, a7).
+__device__ __forceinline__ bf16x8_t pair_order(uint4 w) {
+  u32x4_t r;
+  r.x = __builtin_amdgcn_perm(w.y, w.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(w.y, w.x, 0x07060302u);
+  r.z = __builtin_amdgcn_perm(w.w, w.z, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(w.w, w.z, 0x07060302u);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// After the call v[d] of lane-row r (lanes 16 r .. 16 r + 15) holds what
+// v[r] of lane-row d held.
+__device__ __forceinline__ void transpose4_rows(uint32_t& v0, uint32_t& v1, uint32_t& v2,
+                                                uint32_t& v3) {
+  const auto p0 = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+  const auto p1 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+  const auto q0 = __builtin_amdgcn_permlane16_swap(p0[0], p1[0], false, false);
+  const auto q1 = __builtin_amdgcn_permlane16_swap(p0[1], p1[1], false, false);
+  v0 = q0[0];
+  v1 = q0[1];
+  v2 = q1[0];
+  v3 = q1[1];
+}
+
+// Calls f(integral_constant<int, i>) for i = I .. COUNT-1, in order.
+template <int I, int COUNT, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < COUNT) {
+    f(std::integral_constant<int, I>());
+    static_for_from<I + 1, COUNT>(f);
   }
 }
 
-template <int BITS, bool ASYM, bool YBF16, int MR, int KU>
-hipError_t launch_gemv(const QgemmParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.n_out / (4 * QV_OPW)), (unsigned)((p.rows + MR - 1) / MR));
-  hipLaunchKernelGGL((qgemv_kernel<BITS, ASYM, YBF16, MR, KU>), grid, dim3(256), 0, s, p);
+// Q: 64-code chunks per group (group / 64); NI: rows of C used per lane;
+// AL: activations staged in LDS (at most QV_LDS_ROWS rows) or read from
+// memory; MAXW: waves per workgroup at most.  Workgroup (x, y) takes the
+// weight rows 16 x .. + 15 and the activation rows 16 y .. + 15.
+template <int BITS, int Q, int NI, bool AL, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void qmv_kernel(const QgemmParams P) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  static_assert(QV_PASS % Q == 0, "shape");
+  constexpr int MT = 1;
+  constexpr int LPS = BITS / 2;       // b128 loads per lane and 256-code segment
+  constexpr int GP = QV_PASS / Q;     // groups per pass
+  constexpr int RS = GP >= 4 ? GP / 4 : 1;  // scale (zero) halves staged per lane and pass
+  const int nw = (int)(blockDim.x >> 6);
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar control
+  const int n = lane & 15, j = lane >> 4;
+  const int o0 = blockIdx.x * 16;
+  const int K = P.k, N = P.n_out, NG = K / (64 * Q);
+  const int KB = K * BITS / 8;
+  const int mrows = group_rows(P.rows, blockIdx.y, 16);  // at most QV_LDS_ROWS with AL
+  const uint16_t* A = P.a + (int64_t)blockIdx.y * 16 * P.k;
+  const bool asym = P.asym;
+  const int gpw = (NG + nw - 1) / nw;
+  const int gbeg = min(NG, wave * gpw);
+  const int T = (min(NG, gbeg + gpw) - gbeg) * Q;  // chunks of this wave
+  // LDS: per wave [scales, zeros: 16 x GP fp16] [activations (AL): mrows x 1024
+  // bf16]; after the k loop, the waves' sums [nw][16 MT][16] fp32
+  extern __shared__ __align__(16) uint8_t qv_lds[];
+  constexpr int WSZ = 64 * GP;
+  const int wbytes = WSZ + (AL ? mrows * 2048 : 0);
+  uint16_t* ls = reinterpret_cast<uint16_t*>(qv_lds + wave * wbytes);
+  uint16_t* lz = ls + 16 * GP;
+  uint8_t* la = qv_lds + wave * wbytes + WSZ;
+
+  const uint32_t szbytes = (uint32_t)(32 * NG);
+  const auto rs = buffer_range32(P.scales + (int64_t)o0 * NG, szbytes);
+  const auto rz = buffer_range32(asym ? P.zeros + (int64_t)o0 * NG : P.scales, asym ? szbytes : 0u);
+  const auto ra = buffer_range32(A, (uint32_t)mrows * (uint32_t)K * 2u);
+  const uint32_t cl = (uint32_t)(n * KB + j * 16 * LPS);  // lane part of a code offset
+  const uint32_t kx = asym ? 0u : (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);  // sign flip
+
+  uint16_t sst[RS], zst[RS];
+  uint4 ast[AL ? 2 * QV_LDS_ROWS : 1];
+  uint32_t cw[4][4 * LPS];
+  // the loads of a pass starting at chunk c0 (group gbeg + c0 / Q), in the
+  // order they are used: scales and zeros, activations, codes
+  auto issue = [&](const int c0) {
+    const int g0 = gbeg + c0 / Q;
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int gl = j + 4 * r;  // this lane's group of the pass
+      const bool ok = gl < GP && c0 + gl * Q < T;
+      const uint32_t off = ok ? (uint32_t)(2 * (n * NG + g0 + gl)) : 0xFFFFFFF0u;
+      sst[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0);
+      zst[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)off, 0, 0);
+    }
+    if constexpr (AL) {
+      // rows 0 .. 3 (zero past the end) x the pass's 1024 codes: lane l
+      // takes 32 bytes of row l / 16
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 64 * c0 + 16 * (lane & 15) + 8 * h;  // element of the wave's k run
+        const bool ok = (lane >> 4) < mrows && e < 64 * T;
+        const uint32_t off = ok ? (uint32_t)(2 * ((lane >> 4) * K + 64 * Q * gbeg + e)) : 0xFFFFFFF0u;
+        ast[h] = buf_ld16(ra, off);
+      }
+#pragma unroll
+      for (int h = 2; h < 2 * QV_LDS_ROWS; ++h) {
+        // pieces 2 .. 7: the same rows, the next 256 elements each
+        const int e = 64 * c0 + 256 * (h / 2) + 16 * (lane & 15) + 8 * (h & 1);
+        const bool ok = (lane >> 4) < mrows && e < 64 * T;
+        const uint32_t off = ok ? (uint32_t)(2 * ((lane >> 4) * K + 64 * Q * gbeg + e)) : 0xFFFFFFF0u;
+        ast[h] = buf_ld16(ra, off);
+      }
+    }
+    static_for_from<0, 4>([&](auto sc) {
+      constexpr int sg = decltype(sc)::value;
+      const bool live = c0 + 4 * sg < T;
+      // all of the offset in the range-checked (vector) part: a segment
+      // may run past the end of the row (its chunks past T are not used)
+      const auto rc = buffer_range32(P.codes + (int64_t)o0 * KB, live ? (uint32_t)(16 * KB) : 0u);
+      const uint32_t su = live ? (uint32_t)((64 * Q * gbeg + 64 * (c0 + 4 * sg)) * BITS / 8) : 0u;
+#pragma unroll
+      for (int h = 0; h < LPS; ++h) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(cl + su + 16u * h), 0, 0);
+        cw[sg][4 * h + 0] = v.x;
+        cw[sg][4 * h + 1] = v.y;
+        cw[sg][4 * h + 2] = v.z;
+        cw[sg][4 * h + 3] = v.w;
+      }
+    });
+  };
+  // staged values into this wave's LDS (waits for them, not for the codes)
+  auto stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int gl = j + 4 * r;
+      if (gl < GP) {
+        ls[n * GP + gl] = sst[r];
+        lz[n * GP + gl] = zst[r];
+      }
+    }
+    if constexpr (AL) {
+      // piece h of lane l: row l / 16, elements 256 (h / 2) + 16 (l % 16) + 8 (h % 2),
+      // stored in the codes' pair order (re-paired once here, not per step)
+      if ((lane >> 4) < mrows) {
+#pragma unroll
+        for (int h = 0; h < 2 * QV_LDS_ROWS; ++h)
+          *reinterpret_cast<bf16x8_t*>(la + 2 * ((lane >> 4) * 1024 + 256 * (h / 2) +
+                                                 16 * (lane & 15) + 8 * (h & 1))) = pair_order(ast[h]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // activations read from memory (MT tiles of 16 rows), QV_AW chunks ahead
+  const int arow = AL ? min(n, mrows - 1) : n;
+  const int ak0 = BITS == 2 ? 16 * j : 8 * j;  // lane's elements of a chunk's steps
+  const int ak1 = ak0 + (BITS == 2 ? 8 : 32);
+  uint4 aw[AL ? 1 : QV_AW][MT][2];
+  auto issue_a = [&](const int t, auto slot_c) {
+    if constexpr (!AL) {
+      constexpr int sl = decltype(slot_c)::value;
+      const bool live = t < T;
+      const auto ral = buffer_range32(A, live ? (uint32_t)mrows * (uint32_t)K * 2u : 0u);
+      const int kc = 64 * Q * gbeg + 64 * t;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int e = (arow + 16 * mt) * K + kc;
+        aw[sl][mt][0] = buf_ld16(ral, (uint32_t)(2 * (e + ak0)));
+        aw[sl][mt][1] = buf_ld16(ral, (uint32_t)(2 * (e + ak1)));
+      }
+    }
+  };
+  const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_w);
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  // two sets of group sums (even and odd groups), so that a group's
+  // scaling can overlap the next group's products
+  f32x4_t C[2][MT], S[2][MT], acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = zero4;
+  const float zsym = (float)(1 << (BITS - 1));
+  const uint8_t* la_lane = la + 2 * (arow * 1024 + ak0);
+
+  auto pass = [&](const int c0) {
+    static_for_from<0, QV_AW>([&](auto pc) { issue_a(c0 + (int)decltype(pc)::value, pc); });
+    static_for_from<0, 4>([&](auto sc) {
+      constexpr int sg = decltype(sc)::value;
+      uint32_t y[4 * LPS];
+#pragma unroll
+      for (int w = 0; w < 4 * LPS; ++w) y[w] = cw[sg][w];
+      if (c0 + 4 * sg >= T) return;
+      transpose4_rows(y[0], y[1], y[2], y[3]);
+      if constexpr (LPS == 2) transpose4_rows(y[4], y[5], y[6], y[7]);
+      static_for_from<0, 4>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int tl = 4 * sg + d;       // chunk within the pass
+        constexpr int gl = tl / Q, ps = gl & 1;  // group within the pass, its set of sums
+        const int t = c0 + tl;
+        uint4 ar[MT][2];
+        if constexpr (!AL) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            ar[mt][0] = aw[tl % QV_AW][mt][0];
+            ar[mt][1] = aw[tl % QV_AW][mt][1];
+          }
+          if constexpr (tl + QV_AW < QV_PASS) issue_a(t + QV_AW, std::integral_constant<int, tl % QV_AW>());
+        }
+        if (t >= T) return;
+        u32x4_t b[2];
+        if constexpr (BITS == 2) {
+          const uint32_t x = y[d], xs = x >> 2;
+          const uint32_t lo = (x ^ kx) & 0x33333333u, hi = (xs ^ (kx >> 2)) & 0x33333333u;
+          b[0] = u32x4_t{fp4_pair<0>(lo), fp4_pair<0>(hi), fp4_pair<1>(lo), fp4_pair<1>(hi)};
+          b[1] = u32x4_t{fp4_pair<2>(lo), fp4_pair<2>(hi), fp4_pair<3>(lo), fp4_pair<3>(hi)};
+        } else {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t x = y[d + 4 * w], xs = x >> 4;
+            const uint32_t lo = (x ^ kx) & 0x0F0F0F0Fu, hi = (xs ^ (kx >> 4)) & 0x0F0F0F0Fu;
+            b[w] = u32x4_t{fp8_pair<false>(lo), fp8_pair<false>(hi), fp8_pair<true>(lo),
+                           fp8_pair<true>(hi)};
+          }
+        }
+        bf16x8_t a[MT][2];
+        if constexpr (AL) {
+          a[0][0] = *reinterpret_cast<const bf16x8_t*>(la_lane + 128 * tl);
+          a[0][1] = *reinterpret_cast<const bf16x8_t*>(la_lane + 128 * tl + 2 * (ak1 - ak0));
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            a[mt][0] = pair_order(ar[mt][0]);
+            a[mt][1] = pair_order(ar[mt][1]);
+          }
+        }
+        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, b[0]);
+        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, b[1]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          C[ps][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][0], b0, tl % Q == 0 ? zero4 : C[ps][mt], 0, 0, 0);
+          S[ps][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][0], ones, tl % Q == 0 ? zero4 : S[ps][mt], 0, 0, 0);
+          C[ps][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][1], b1, C[ps][mt], 0, 0, 0);
+          S[ps][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][1], ones, S[ps][mt], 0, 0, 0);
+        }
+        if constexpr (tl % Q == Q - 1) {  // the group's last chunk: add s (C - z S)
+          const float sc = half_to_float(ls[n * GP + gl]);
+          const float z = asym ? half_to_float(lz[n * GP + gl]) : zsym;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+              acc[mt][i] = fmaf(sc, fmaf(-z, S[ps][mt][i], C[ps][mt][i]), acc[mt][i]);
+        }
+      });
+    });
+  };
+  // One pass (k up to 1024 per wave): straight code, no loop, so that the
+  // compiler tracks every load in flight exactly.  Longer runs loop.
+  issue(0);
+  stage();
+  if (T <= QV_PASS) {
+    pass(0);
+  } else {
+    pass(0);
+    for (int c0 = QV_PASS; c0 < T; c0 += QV_PASS) {
+      issue(c0);
+      stage();
+      pass(c0);
+    }
+  }
+
+  // --- the waves' sums, added in wave order ---
+  __syncthreads();  // every wave is done with its staged values
+  float* red = reinterpret_cast<float*>(qv_lds);  // [nw][16 MT][16]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) red[(wave * MT * 16 + mt * 16 + 4 * j + i) * 16 + n] = acc[mt][i];
+  __syncthreads();
+  const int ysz = P.y_bf16 ? 2 : 4;
+  const auto ry = buffer_range32(static_cast<char*>(P.y) + (int64_t)blockIdx.y * 16 * N * ysz,
+                                 (uint32_t)mrows * (uint32_t)N * (uint32_t)ysz);
+  for (int e = tid; e < MT * 256; e += 64 * nw) {
+    const int m = e >> 4, c = e & 15;
+    if (m < mrows) {
+      float v = red[m * 16 + c];
+      for (int w = 1; w < nw; ++w) v += red[(w * MT * 16 + m) * 16 + c];
+      const uint32_t off = (uint32_t)(m * N + o0 + c) * (uint32_t)ysz;
+      if (P.y_bf16) buf_st2(ry, off, (uint16_t)pack_bf16(v, 0.f));
+      else buf_st4(ry, off, __float_as_uint(v));
+    }
+  }
+}
+
+template <int BITS, int Q, int NI, bool AL>
+hipError_t launch_mv(const QgemmParams& p, hipStream_t s) {
+  constexpr int MT = 1;
+  constexpr int MAXW = qv_maxw(BITS, Q, NI);
+  constexpr int GP = QV_PASS / Q;
+  const int nw = std::min(MAXW, (p.k + 1023) / 1024);
+  const size_t wbytes = (size_t)64 * GP + (AL ? (size_t)p.rows * 2048 : 0);
+  const size_t lds = std::max((size_t)nw * wbytes, (size_t)nw * MT * 1024);
+  const void* fn = reinterpret_cast<const void*>(qmv_kernel<BITS, Q, NI, AL, MAXW>);
+  const hipError_t e = allow_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((qmv_kernel<BITS, Q, NI, AL, MAXW>),
+                     dim3((unsigned)(p.n_out / 16), (unsigned)((p.rows + 15) / 16)), dim3(64 * nw),
+                     lds, s, p);
   return hipGetLastError();
+}
+
+template <int BITS, int Q>
+hipError_t launch_mv_rows(const QgemmParams& p, hipStream_t s) {
+  if (p.rows == 1) return launch_mv<BITS, Q, 1, true>(p, s);
+  if (p.rows == 2) return launch_mv<BITS, Q, 2, true>(p, s);
+  if (p.rows <= QV_LDS_ROWS) return launch_mv<BITS, Q, 4, true>(p, s);
+  return launch_mv<BITS, Q, 4, false>(p, s);  // 16 rows per workgroup row
+}
+
+template <int BITS>
+hipError_t launch_mv_group(const QgemmParams& p, hipStream_t s) {
+  switch (p.group) {
+    case 64: return launch_mv_rows<BITS, 1>(p, s);
+    case 128: return launch_mv_rows<BITS, 2>(p, s);
+    case 256: return launch_mv_rows<BITS, 4>(p, s);
+    default: return launch_mv_rows<BITS, 8>(p, s);
+  }
 }
 
 template <int BITS, bool ASYM, bool YBF16>
 hipError_t launch_one(const QgemmParams& p, hipStream_t s) {
-  if (p.rows <= QG_GEMV_ROWS) {
-    // one row: 64 codes per lane (a 4096-code row in one step, the decode
-    // dominates); more rows: 16 per lane, the dot products dominate
-    if (p.rows == 1) return launch_gemv<BITS, ASYM, YBF16, 1, 64>(p, s);
-    if (p.rows <= 4) return launch_gemv<BITS, ASYM, YBF16, 4, 16>(p, s);
-    return launch_gemv<BITS, ASYM, YBF16, 16, 16>(p, s);
-  }
+  if (p.rows <= QG_GEMV_ROWS) return launch_mv_group<BITS>(p, s);
   constexpr int BM = QG_BM;
   using T = QTile<BM>;
   const void* fn = reinterpret_cast<const void*>(qgemm_kernel<BM, BITS, ASYM, YBF16>);

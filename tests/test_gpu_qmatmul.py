@@ -5,14 +5,18 @@ against the 11008 x 4096 weight) on sampled rows.
 
 Tolerance (derived from each kernel's arithmetic; a sum whose terms pass
 through at most D fp32 roundings is within D * 2^-24 * sum |terms| of the
-exact sum): every product a * (q - zero) is exact in fp32.
-* MFMA tiles (more than 64 rows): one group's products summed in fp32
-  (at most `group` roundings), times the group's scale (1), added over the
-  k / group groups:  D = group + k / group + 2.
-* few-row kernel (64 rows or fewer): each lane sums KU codes with v_dot2
-  (counted as one rounding per product: KU), scales the chunk (1), adds
-  its k / (64 KU) chunks, and the 64 lanes are added by a 6-level tree:
-  D = KU + k / (64 KU) + 9, with KU = 64 for one row and 16 otherwise.
+exact sum):
+* MFMA tiles (more than 64 rows): every product a * (q - zero) is exact in
+  fp32; one group's products summed in fp32 (at most `group` roundings),
+  times the group's scale (1), added over the k / group groups:
+  D = group + k / group + 2, on the terms |a| |w|.
+* few-row kernel (64 rows or fewer): per group the matrix cores sum the
+  exact products a q' (q' the code as offset binary, q' - z = w / s; at most
+  `group` roundings) and, alongside, the activations S = sum a; the group
+  adds s (C - z S) (one rounding for the zero point, one for the
+  accumulation over at most k / group groups), and at most 16 waves' sums
+  are added: D = group + k / group + 18, on the terms |a| s (q' + z), which
+  bound both sums (s (q' + z) <= |w| + 2 s |z|).
 bf16 outputs add half a bf16 ulp of the result."""
 import math
 
@@ -78,8 +82,19 @@ def rounding_depth(call_rows, k, group):
     """D of the kernel that a call with `call_rows` rows runs (see above)."""
     if call_rows > 64:
         return group + k // group + 2
-    ku = 64 if call_rows == 1 else 16
-    return ku + max(1, k // (64 * ku)) + 9
+    return group + k // group + 18
+
+
+def term_bound(w, scales, zeros, bits, group, mode, call_rows):
+    """Per-element weight magnitude of the bound's terms (see above)."""
+    if call_rows > 64:
+        return np.abs(w)
+    s = np.repeat(np.asarray(scales, dtype=np.uint16).view(np.float16).astype(np.float64), group, 1)
+    if mode == oracle.ASYM:
+        z = np.repeat(np.asarray(zeros, dtype=np.uint16).view(np.float16).astype(np.float64), group, 1)
+    else:
+        z = float(1 << (bits - 1))
+    return np.abs(w) + 2.0 * np.abs(s) * np.abs(z)
 
 
 def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=None):
@@ -91,7 +106,8 @@ def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=N
     w = oracle.dequantize(codes, scales, zeros, bits, group, mode, a.shape[1])
     y64 = a @ w.T
     k = a.shape[1]
-    bound = rounding_depth(call_rows, k, group) * U * (np.abs(a) @ np.abs(w).T)
+    wt = term_bound(w, scales, zeros, bits, group, mode, call_rows)
+    bound = rounding_depth(call_rows, k, group) * U * (np.abs(a) @ wt.T)
     if bf16_out:
         mag = np.maximum(np.abs(got), np.abs(y64))
         e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
@@ -107,9 +123,15 @@ def check(got, a_bits, codes, scales, zeros, bits, group, mode, bf16_out, rows=N
 @pytest.mark.parametrize("y_dt", ["f32", "bf16"])
 def test_small_shapes(bits, mode, y_dt):
     rng = np.random.default_rng(100 + 10 * bits + mode + (5 if y_dt == "bf16" else 0))
+    # few-row kernel: 1, 2, 3-4 rows (activations staged in LDS), 5-16 and
+    # more (16-row slices); one pass per wave (k up to 1024 per wave), a
+    # partial last segment (k = 64, 2112), several passes (k = 11008 at
+    # group 64 with eight waves); every group size
     for rows, n_out, k, group in [(1, 128, 64, 64), (37, 256, 128, 128), (300, 384, 640, 64),
                                   (257, 128, 1024, 256), (513, 256, 512, 512), (4, 384, 2112, 64),
-                                  (16, 128, 1024, 512), (64, 256, 4096, 128), (65, 128, 256, 128)]:
+                                  (16, 128, 1024, 512), (64, 256, 4096, 128), (65, 128, 256, 128),
+                                  (2, 128, 4096, 256), (3, 256, 11008, 128), (5, 128, 16384, 64),
+                                  (20, 128, 3072, 256), (1, 256, 11008, 64)]:
         a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, k)).astype(np.float32) * 3)
         codes, scales, zeros = rand_codes(rng, n_out, k, bits, group, mode)
         got = run(a, codes, scales, zeros, bits, group, mode,
@@ -171,7 +193,7 @@ def test_w2a16_decode_full_width(rows):
 @pytest.mark.parametrize("rows,bits,mode", [(1, 2, oracle.ASYM), (300, 4, oracle.SYM)])
 def test_longest_k(rows, bits, mode):
     """k = 65536 (the largest accepted): 1024 chunks through the MFMA tiles,
-    16 steps per lane in the few-row kernel."""
+    four passes per wave in the few-row kernel."""
     rng = np.random.default_rng(21 + rows)
     k, n_out, group = 65536, 128, 512
     a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, k)).astype(np.float32))
