@@ -172,8 +172,9 @@ __device__ __forceinline__ void kf_segment(float (&w)[8], const KfPlain& C) {
   kf_plain_lane<4>(w, C);
 }
 
-// The row loop over rows blockIdx.x, + gridDim.x, ... below nrun: mix into
-// LDS, one barrier, the segments.  QM fixes the two common quantizer formats
+// The row loop over rows blockIdx.x, + gridDim.x, ... below nrun: one
+// barrier per row, then the next row's mix (matrix cores, into the other LDS
+// buffer) alongside this row's segments (vector units).  QM fixes the two common quantizer formats
 // at compile time (no group-size branches).
 template <int KS, int YK, int QM, class Coef>
 __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, const uint16_t* opart,
@@ -211,32 +212,22 @@ __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, c
         d[ks][u] = buf_ld4(rx, ((uint32_t)(16 * ks + 8 * kh + u) * KF_NB + c0) * 2u);
   };
 
-  uint32_t d[KS][8];
-  int64_t r = blockIdx.x;
-  load(r, d);
-  int buf = 0;
-  for (; r < nrun; r += gridDim.x, buf ^= 1) {
-    float* const V = vbuf + buf * KF_VBUF;
-    // 1. the mix on the matrix cores (the next row's loads go out once the
-    // operands are repacked)
+  // the mix of one row from the X words in d (on the matrix cores): the
+  // MFMAs are issued here, their results written to V by mix_store
+  kf_f32x16_t acc[2];
+  auto mix_issue = [&](const uint32_t (&dd)[KS][8]) {
     kf_bf16x8_t b[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        lo[u] = __builtin_amdgcn_perm(d[ks][2 * u + 1], d[ks][2 * u], 0x05040100u);
-        hi[u] = __builtin_amdgcn_perm(d[ks][2 * u + 1], d[ks][2 * u], 0x07060302u);
+        lo[u] = __builtin_amdgcn_perm(dd[ks][2 * u + 1], dd[ks][2 * u], 0x05040100u);
+        hi[u] = __builtin_amdgcn_perm(dd[ks][2 * u + 1], dd[ks][2 * u], 0x07060302u);
       }
       b[ks][0] = kf_frag(lo[0], lo[1], lo[2], lo[3]);
       b[ks][1] = kf_frag(hi[0], hi[1], hi[2], hi[3]);
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(b[ks][h])::"memory");
-    load(r + gridDim.x, d);
-    kf_f32x16_t acc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -248,18 +239,42 @@ __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, c
         // A operand: O part q, row 32 mt + col, k = 16 ks + 8 kh .. + 7
         const uint4 av = *reinterpret_cast<const uint4*>(opart + q * KF_OPART + (32 * mt + col) * KF_OS +
                                                          16 * ks + 8 * kh);
-        const kf_bf16x8_t a = kf_frag(av.x, av.y, av.z, av.w);
+        const kf_bf16x8_t aq = kf_frag(av.x, av.y, av.z, av.w);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[ks][h], acc[h], 0, 0, 0);
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, b[ks][h], acc[h], 0, 0, 0);
       }
-    // V rows 32 mt + 8 (e / 4) + 4 kh + e % 4, columns 64 blk + 2 col + h
+  };
+  // V rows 32 mt + 8 (e / 4) + 4 kh + e % 4, columns 64 blk + 2 col + h
+  auto mix_store = [&](float* Vw) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = 32 * mt + 8 * (e >> 2) + 4 * kh + (e & 3);
-      *reinterpret_cast<float2*>(V + i * KF_VS + 64 * blk + 2 * col) = make_float2(acc[0][e], acc[1][e]);
+      *reinterpret_cast<float2*>(Vw + i * KF_VS + 64 * blk + 2 * col) = make_float2(acc[0][e], acc[1][e]);
     }
-    __syncthreads();
+  };
+
+  // Software pipeline over rows: the mix of the next row runs on the matrix
+  // cores while this row's butterfly runs on the vector units.  Row r's V
+  // sits in buffer buf; the next row's goes to the other one, last read by
+  // the row before r (finished by every wave at this iteration's barrier).
+  uint32_t d[KS][8];
+  int64_t r = blockIdx.x;
+  load(r, d);
+  int buf = 0;
+  if (r < nrun) {
+    mix_issue(d);
+    load(r + gridDim.x, d);
+    mix_store(vbuf);
+  }
+  for (; r < nrun; r += gridDim.x, buf ^= 1) {
+    float* const V = vbuf + buf * KF_VBUF;
+    __syncthreads();  // V of row r is complete; the other buffer is free
+    const bool next = r + gridDim.x < nrun;
+    if (next) {
+      mix_issue(d);
+      load(r + 2 * gridDim.x, d);
+    }
 
     // 2. the butterfly on each segment, then the outputs
     const auto ry = buffer_range32(static_cast<uint16_t*>(P.y) + (YK == Y_BF16 ? r * (int64_t)n : 0),
@@ -303,6 +318,7 @@ __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, c
         if (asym) buf_st2<kNonTemporal>(rz, off, (uint16_t)(qp.sz >> 16));
       }
     }
+    if (next) mix_store(vbuf + (buf ^ 1) * KF_VBUF);
   }
 }
 
