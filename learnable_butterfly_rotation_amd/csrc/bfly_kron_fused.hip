@@ -215,6 +215,22 @@ __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, c
   // the mix of one row from the X words in d (on the matrix cores): the
   // MFMAs are issued here, their results written to V by mix_store
   kf_f32x16_t acc[2];
+  // this wave's A operands (O's parts at rows 32 mt + col), the same for
+  // every row: held in registers up to KS = 3 (m <= 48; four k steps would
+  // spill), read from LDS at each use above that
+  constexpr bool AREG = KS <= 3;
+  kf_bf16x8_t aop[3][AREG ? KS : 1];
+  auto a_frag = [&](int q, int ks) {
+    const uint4 av = *reinterpret_cast<const uint4*>(opart + q * KF_OPART + (32 * mt + col) * KF_OS +
+                                                     16 * ks + 8 * kh);
+    return kf_frag(av.x, av.y, av.z, av.w);
+  };
+  if constexpr (AREG) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aop[q][ks] = a_frag(q, ks);
+  }
   auto mix_issue = [&](const uint32_t (&dd)[KS][8]) {
     kf_bf16x8_t b[KS][2];
 #pragma unroll
@@ -237,9 +253,7 @@ __device__ __forceinline__ void kf_rows(const KronFusedParams& P, float* vbuf, c
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         // A operand: O part q, row 32 mt + col, k = 16 ks + 8 kh .. + 7
-        const uint4 av = *reinterpret_cast<const uint4*>(opart + q * KF_OPART + (32 * mt + col) * KF_OS +
-                                                         16 * ks + 8 * kh);
-        const kf_bf16x8_t aq = kf_frag(av.x, av.y, av.z, av.w);
+        const kf_bf16x8_t aq = AREG ? aop[q][AREG ? ks : 0] : a_frag(q, ks);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, b[ks][h], acc[h], 0, 0, 0);
