@@ -414,7 +414,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_kernel(const QgemmParams P) {
   const uint32_t kx = asym ? 0u : (BITS == 2 ? 0xAAAAAAAAu : 0x88888888u);  // sign flip
 
   uint16_t sst[RS], zst[RS];
-  uint4 ast[AL ? 2 * QV_LDS_ROWS : 1];
+  uint4 ast[AL ? (NI == 1 ? 2 : 2 * QV_LDS_ROWS) : 1];
   uint32_t cw[4][4 * LPS];
   // the loads of a pass starting at chunk c0 (group gbeg + c0 / Q), in the
   // order they are used: scales and zeros, activations, codes
@@ -428,7 +428,15 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_kernel(const QgemmParams P) {
       sst[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0);
       zst[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)off, 0, 0);
     }
-    if constexpr (AL) {
+    if constexpr (AL && NI == 1) {
+      // one row: lane l takes elements 8 l and 8 (l + 64) of the pass's 1024
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 64 * c0 + 8 * (lane + 64 * h);
+        const uint32_t off = e < 64 * T ? (uint32_t)(2 * (64 * Q * gbeg + e)) : 0xFFFFFFF0u;
+        ast[h] = buf_ld16(ra, off);
+      }
+    } else if constexpr (AL) {
       // rows 0 .. 3 (zero past the end) x the pass's 1024 codes: lane l
       // takes 32 bytes of row l / 16
 #pragma unroll
@@ -474,7 +482,11 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_kernel(const QgemmParams P) {
         lz[n * GP + gl] = zst[r];
       }
     }
-    if constexpr (AL) {
+    if constexpr (AL && NI == 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<bf16x8_t*>(la + 16 * (lane + 64 * h)) = pair_order(ast[h]);
+    } else if constexpr (AL) {
       // piece h of lane l: row l / 16, elements 256 (h / 2) + 16 (l % 16) + 8 (h % 2),
       // stored in the codes' pair order (re-paired once here, not per step)
       if ((lane >> 4) < mrows) {
