@@ -190,12 +190,16 @@ def test_w2a16_decode_full_width(rows):
     check(got, a, q["codes"], q["scales"], q["zeros"], 2, 128, oracle.ASYM, True)
 
 
-@pytest.mark.parametrize("rows,bits,mode", [(1, 2, oracle.ASYM), (300, 4, oracle.SYM)])
-def test_longest_k(rows, bits, mode):
-    """k = 65536 (the largest accepted): 1024 chunks through the MFMA tiles,
-    four passes per wave in the few-row kernel."""
+@pytest.mark.parametrize("rows,bits,mode,k,group",
+                         [(1, 2, oracle.ASYM, 65536, 512), (300, 4, oracle.SYM, 65536, 512),
+                          (16, 4, oracle.ASYM, 65536, 512), (3, 2, oracle.SYM, 16384, 128)])
+def test_longest_k(rows, bits, mode, k, group):
+    """k = 65536 (the largest accepted): 1024 chunks through the MFMA tiles;
+    in the few-row kernel four passes per wave for one row (16 waves), eight
+    for 16 rows (8 waves, activations read from memory), and several passes
+    with the activations staged in LDS (3 rows, k = 16384, 8 waves)."""
     rng = np.random.default_rng(21 + rows)
-    k, n_out, group = 65536, 128, 512
+    n_out = 128
     a = inputs.f32_to_bf16_bits(rng.standard_normal((rows, k)).astype(np.float32))
     codes, scales, zeros = rand_codes(rng, n_out, k, bits, group, mode)
     got = run(a, codes, scales, zeros, bits, group, mode, torch.float32)
