@@ -238,10 +238,13 @@ __device__ __forceinline__ float group_min(float v, int gt) {
 // integer, ties to even, and the low bits of the result's encoding are
 // q + bias.  Clamping y to [qlo*s16, qhi*s16] (products exact in fp32) is the
 // same as clamping q afterwards.  The clamp changes a code only when some
-// y * r of the group rounds outside [qlo, qhi], which needs a scale that
-// lost precision (fp16 subnormal, or saturated at 65504): near_edge flags a
-// group within 1/4 of that (room to spare for the fp32 rounding of the
-// extremes' products), and callers may skip the clamp where no group is.
+// y * r of the group rounds outside [qlo, qhi].  With the symmetric scale
+// that needs a scale that lost precision (fp16 subnormal, or saturated at
+// 65504): near_edge flags a group within 1/4 of that (room to spare for the
+// fp32 rounding of the extremes' products), and callers may skip the clamp
+// where no group is.  With the asymmetric one the zero point's own rounding
+// can push the top code one past qhi as well, and near_edge fires for about
+// half the groups: callers clamp those always.
 struct QParams {
   float r, clo, chi, z;
   uint32_t sz;  // fp16 scale bits (low half), zero-point bits (high half)
@@ -268,18 +271,14 @@ __device__ __forceinline__ QParams quant_params(const float (&v)[8], int gt, boo
   const _Float16 s16 = (_Float16)s_pre;
   const float sc = (float)s16;
   QParams q;
-  q.r = q.z = 0.f;
-  q.clo = -top * sc;  // symmetric bounds; zero with the scale
-  q.chi = top * sc;
-  if (sc != 0.f) {
-    q.r = __builtin_amdgcn_rcpf(sc);
-    q.r = fmaf(fmaf(-sc, q.r, 1.0f), q.r, q.r);
-    if (asym) {
-      q.z = __builtin_amdgcn_fmed3f(rintf(-lo * q.r), 0.f, top);
-      q.clo = -q.z * sc;
-      q.chi = (top - q.z) * sc;
-    }
-  }
+  // Branch-free: a zero scale (all-zero group, or max = min) selects r = 0,
+  // so every code, the zero point and both bounds come out zero.
+  q.r = __builtin_amdgcn_rcpf(sc);
+  q.r = fmaf(fmaf(-sc, q.r, 1.0f), q.r, q.r);
+  q.r = sc != 0.f ? q.r : 0.f;
+  q.z = asym ? __builtin_amdgcn_fmed3f(rintf(-lo * q.r), 0.f, top) : 0.f;
+  q.clo = asym ? -q.z * sc : -top * sc;
+  q.chi = (top - q.z) * sc;
   q.sz = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q.z) << 16);
   // z and top are small integers: the bounds are exact.
@@ -303,6 +302,27 @@ __device__ __forceinline__ uint32_t quant_pack(const float (&v)[8], const QParam
     const uint32_t w01 = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
     const uint32_t w23 = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
     packed = (w01 | w23) ^ 0x88888888u;
+  } else if (asym) {
+    // The bits of fma(y, r, 1.5*2^23) are 0x4B400000 + q as an integer, so
+    // sum_e (q_e + z) << (bits*e), whose fields cannot carry once the codes
+    // are clamped to [0, 2^bits - 1], is sum_e bits_e << (bits*e) plus one
+    // constant per group, in wrapping 32-bit arithmetic.
+    // z in every field: z * 0x5555 or z * 0x1111 (twice) is exact in fp32
+    const uint32_t rep = bits == 2 ? 0x5555u : 0x11111111u;  // sum_e 2^(bits*e)
+    const uint32_t zr = (uint32_t)(q.z * (bits == 2 ? 21845.0f : 4369.0f));
+    const uint32_t zrep = bits == 2 ? zr : (zr | (zr << 16));
+    // Horner form, one v_lshl_add_u32 per element (the compiler otherwise
+    // splits the sum into separate shifts and three-input adds)
+    packed = __float_as_uint(fmaf(v[7], q.r, 12582912.0f));
+#pragma unroll
+    for (int e = 6; e >= 0; --e) {
+      const uint32_t f = __float_as_uint(fmaf(v[e], q.r, 12582912.0f));
+      if (bits == 2)  // the only asymmetric widths are 2 and 4
+        asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(packed) : "v"(packed), "v"(f));
+      else
+        asm("v_lshl_add_u32 %0, %1, 4, %2" : "=v"(packed) : "v"(packed), "v"(f));
+    }
+    packed += zrep - 0x4B400000u * rep;
   } else {
     const uint32_t off = (uint32_t)q.z - 0x4B400000u;
     const uint32_t mask = (1u << bits) - 1u;
@@ -628,7 +648,9 @@ __device__ __forceinline__ bool row_loop(const FwdParams& P, const int64_t rows,
           held_c[sg] = quant_pack(c, qp[sg], bits, asym);
         }
       } else {  // one wave-uniform test for every segment, the clamp in place
-        if (__builtin_amdgcn_ballot_w64(near_edge) != 0) {
+        // (asymmetric groups put an extreme past the test's margin in about
+        // half the cases, so a wave of them always clamps)
+        if (asym || __builtin_amdgcn_ballot_w64(near_edge) != 0) {
 #pragma unroll
           for (int sg = 0; sg < SEGS; ++sg) quant_clamp(w[sg], qp[sg]);
         }
