@@ -66,8 +66,12 @@
  *     returns its code and enqueues nothing.  A failed HIP call returns
  *     BFLY_ERR_HIP; the HIP error code is then available from
  *     bfly_last_hip_error() on the calling thread.
- *   - Supported sizes: n a power of two in [64, 4096] (smaller powers of
- *     two and 8192 return BFLY_ERR_UNSUPPORTED); for bfly_kron_forward
+ *   - Supported sizes: n a power of two in [64, 8192] for bfly_forward,
+ *     bfly_forward_quant (n = 8192 in two passes), bfly_coeff_bytes,
+ *     bfly_prepare and bfly_prepare_hadamard; in [64, 4096] for
+ *     bfly_forward_quant_noalloc, bfly_backward and the calibration steps.
+ *     Smaller powers of two, and 8192 where it is not listed, return
+ *     BFLY_ERR_UNSUPPORTED; for bfly_kron_forward
  *     m in [1, 8] and nb a power of two with m * nb <= 8192, nb in
  *     [256, 4096] for m >= 2 and in [64, 4096] for m = 1; for the wide
  *     forward and the Kronecker backward m in [2, 64], nb in [256, 4096],
