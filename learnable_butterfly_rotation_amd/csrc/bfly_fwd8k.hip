@@ -60,19 +60,31 @@ __global__ void __launch_bounds__(FS_THREADS) final_stage_kernel(FinalParams P) 
   const int ngr = quant ? N8K / P.group : 0;
   const bool scale_lane = quant && (t & (gt - 1)) == 0;
   // Per row, buffer resources covering exactly that row of each array; a
-  // lane with no scale to store aims outside its range.
-  for (int64_t r = blockIdx.x; r < P.rows; r += gridDim.x) {
-    const auto rv = buffer_range32(P.v + r * N8K, N8K * 4);
+  // lane with no scale to store aims outside its range.  The next row's
+  // input is loaded before this row's arithmetic and stores (a row past the
+  // end has an empty range: its loads return zeros and move no data).
+  const int64_t G = gridDim.x;
+  uint4 in[2][2];
+  auto load_row = [&](const int64_t r) {
+    const auto rv = buffer_range32(P.v + (r < P.rows ? r : 0) * N8K, r < P.rows ? N8K * 4 : 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      in[0][k] = buf_ld16<kNonTemporal>(rv, (uint32_t)(c0 + 4 * k) * 4);
+      in[1][k] = buf_ld16<kNonTemporal>(rv, (uint32_t)(H8K + c0 + 4 * k) * 4);
+    }
+  };
+  load_row(blockIdx.x);
+  for (int64_t r = blockIdx.x; r < P.rows; r += G) {
     float lo[8], hi[8];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint4 a = buf_ld16<kNonTemporal>(rv, (uint32_t)(c0 + 4 * k) * 4);
-      const uint4 b = buf_ld16<kNonTemporal>(rv, (uint32_t)(H8K + c0 + 4 * k) * 4);
+      const uint4 a = in[0][k], b = in[1][k];
       lo[4 * k] = __uint_as_float(a.x); lo[4 * k + 1] = __uint_as_float(a.y);
       lo[4 * k + 2] = __uint_as_float(a.z); lo[4 * k + 3] = __uint_as_float(a.w);
       hi[4 * k] = __uint_as_float(b.x); hi[4 * k + 1] = __uint_as_float(b.y);
       hi[4 * k + 2] = __uint_as_float(b.z); hi[4 * k + 3] = __uint_as_float(b.w);
     }
+    load_row(r + G);
     float w[2][8];  // stage 12: (v_i, v_j) -> (c v_i - s v_j, s v_i + c v_j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
