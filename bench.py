@@ -21,8 +21,10 @@ launches on their stream gives its average launch duration
 peak.  Then 240 launches with events attached to each dispatch
 (bfly_time_next_forward) give the median and spread beside it.  `traffic` comes from
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded for the current kernel
-sources (null if they changed).  `cpu_baseline` times the fp64 oracle on the
-host's cores (all threads; one-thread timings of three workloads beside it).
+sources (null if they changed).  `roofline.copy_context` is a plain device
+copy of the same bytes (half read, half written) timed the same way, as
+context only.  `cpu_baseline` times the fp64 oracle on the host's cores (all
+threads; one-thread timings of three workloads beside it).
 
 --workload picks one of the other workloads for a secondary line:
 tiny_n256_fp32, weight_n4096_bf16_int2, kron_n5120_bf16_int4,
@@ -184,6 +186,25 @@ def warm_up(torch, fn, steps, min_seconds=0.3):
     return time.perf_counter() - t0
 
 
+def copy_context(torch, stream, nbytes, reps=200, sets=5):
+    """GB/s of a plain device copy moving `nbytes` (half read, half written)
+    per call, rotating buffer pairs so no copy finds its source in cache."""
+    n = nbytes // 8  # fp32 elements per buffer
+    bufs = [(torch.ones(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(sets)]
+    for i in range(20):
+        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev[0].record(stream)
+    for i in range(reps):
+        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    s = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+    del bufs
+    return 8 * n / s / 1e9
+
+
 def bench_act(args, torch, B, inputs):
     w = inputs.act_int4()
     x, th = w["x"], w["theta"]
@@ -287,6 +308,7 @@ def bench_act(args, torch, B, inputs):
     kern_ms = kernel_times(False)
     kern_med_s = float(np.median(kern_ms)) / 1e3
     achieved = kernel_bytes / kern_avg_s / 1e9
+    copy_gbs = copy_context(torch, stream, kernel_bytes)
     traffic = recorded_traffic()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -315,7 +337,12 @@ def bench_act(args, torch, B, inputs):
                          "median_us": round(kern_med_s * 1e6, 3),
                          "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                          "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
-                     "algorithmic_bytes_per_launch": kernel_bytes},
+                     "algorithmic_bytes_per_launch": kernel_bytes,
+                     "copy_context": {"GBs": round(copy_gbs, 2),
+                                      "kernel_frac_of_copy": round(achieved / copy_gbs, 4),
+                                      "what": "torch device copy of the same bytes (half read, half "
+                                              "written), 5 rotating buffer pairs, 200 copies "
+                                              "between one event pair; context only"}},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_act(w, bytes_per_row, inputs)
