@@ -291,7 +291,10 @@ size_t bfly_backward_workspace_bytes(int64_t rows, int32_t n);
  *              [log2 nb][nb/2], OVERWRITTEN (zeros when rows == 0)
  * Computed as dL/dz = (O^T kron I) G, then the butterfly backward on the
  * rows * m segments of length nb (z = (I kron B) x per segment), with the
- * same fixed-order reduction as bfly_backward.  Sizes: m in [2, 64] (m = 1
+ * same fixed-order reduction as bfly_backward.  For m <= 5 and dx != g the
+ * backward kernel forms dL/dz from G's m segments as it loads them (one
+ * pass); otherwise a mixing pass writes dL/dz into dx first.  Both give the
+ * same bits (dx and dtheta_b).  Sizes: m in [2, 64] (m = 1
  * is the plain butterfly: bfly_backward), nb a power of two in [256, 4096],
  * m * nb <= 65536.  workspace: >= bfly_kron_backward_workspace_bytes(rows, m,
  * nb) bytes of device scratch, 16-byte aligned; the call allocates nothing.

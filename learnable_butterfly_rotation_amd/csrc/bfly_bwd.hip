@@ -62,7 +62,14 @@ struct BwdShape {
 // CALIB: dL/dY is not read but formed from the recomputed Y (calib_grad,
 // with each group's max |y| loaded like g and the log-bins in LDS), and dX
 // is not stored -- the loss of one calibration step.
-template <int LOGN, bool CALIB>
+// KM > 0: the backward of a Kronecker composite (O kron B) with m = KM
+// segments; each row of length N is segment a of row r of g, and its dL/dz
+// = sum_b O[b][a] g[r][b N + .] is formed from the m segments of g as they
+// are loaded (duidaima.com write-up, section "butterfly": the Kronecker
+// composite; the mix is the transpose of the forward's).  The segments'
+// loads are issued at the start of the row group, ahead of the next group's
+// prefetch, and consumed after the forward recompute.
+template <int LOGN, bool CALIB, int KM = 0>
 __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, CalibGradArgs C) {
   using S = BwdShape<LOGN>;
   constexpr int LOGE = S::LOGE, E = S::E, T = S::T, N = S::N, R = S::R, L = S::L;
@@ -132,10 +139,45 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
 #pragma unroll
       for (int e = 0; e < E; ++e)
         gc[e] = buf_ld4(ra, (uint32_t)(team * ngr + ((el0 + (e << BL)) >> lg_group)) * 4);
-    } else {
+    } else if (KM == 0) {
       const auto rg = group_range(P.g, grp);
 #pragma unroll
       for (int e = 0; e < E; ++e) gc[e] = buf_ld4(rg, offl + ((uint32_t)e << BL) * 4);
+    }
+  };
+  // KM > 0: the m = KM segments of g for this team's segment row (row
+  // r = sr / m, segment a = sr % m) and the column a of O, through a
+  // resource over the rows the group's teams touch (from r0 = its first
+  // segment row's row); segment rows past the end read as zeros.  A group's
+  // segments are requested once the previous group's are mixed.
+  uint32_t gm[KM > 0 ? KM : 1][E], om[KM > 0 ? KM : 1];
+  // The group's first segment row is row r0, segment a0 (uniform), tracked
+  // from group to group by adding the stride's quotient and remainder: one
+  // 64-bit division before the loop instead of several per group.
+  constexpr int km = KM > 0 ? KM : 1;
+  const int64_t stride_sr = (int64_t)gridDim.x * R;
+  const int64_t q_stride = stride_sr / km;
+  const int r_stride = (int)(stride_sr - q_stride * km);
+  int64_t r0 = ((int64_t)blockIdx.x * R) / km;
+  int a0 = (int)((int64_t)blockIdx.x * R - r0 * km);
+  auto load_gm = [&]() {
+    if constexpr (KM > 0) {
+      constexpr int m = km;
+      const int64_t avail = rows / m - r0;  // whole rows from r0 on
+      const uint32_t nr = (uint32_t)(avail <= 0 ? 0 : (avail < R + 1 ? avail : R + 1));
+      const auto rg = buffer_range32(P.g + r0 * ((int64_t)m * N), nr * (uint32_t)(m * N * 4));
+      const auto ro = buffer_range32(P.mixt, (uint32_t)(m * m * 4));
+      const uint32_t at = (uint32_t)(a0 + team);  // < m + R
+      const int rrel = (int)(at / (uint32_t)m), a = (int)(at - (uint32_t)rrel * (uint32_t)m);
+      const uint32_t el = (uint32_t)lay<LOGE>(t, 0, BL);
+      const uint32_t base = ((uint32_t)(rrel * m * N) + el) * 4u;
+#pragma unroll
+      for (int b = 0; b < KM; ++b) {
+        om[b] = buf_ld4(ro, (uint32_t)(a * m + b) * 4u);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          gm[b][e] = buf_ld4(rg, base + (((uint32_t)(b * N) + ((uint32_t)e << BL)) * 4u));
+      }
     }
   };
   __shared__ float lbs[CALIB ? CALIB_MAX_BINS : 1];
@@ -147,6 +189,7 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
   const float inv_qmax = CALIB ? 1.f / qmax : 0.f;
 
   load(blockIdx.x);
+  load_gm();  // KM > 0: the first group's g segments
   for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
     float v[E], g[E];
 #pragma unroll
@@ -157,7 +200,7 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
       v[4 * c + 3] = __uint_as_float(xc[c].w);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) g[e] = __uint_as_float(gc[e]);
+    for (int e = 0; e < E; ++e) g[e] = KM > 0 ? 0.f : __uint_as_float(gc[e]);
     // the registers are free once copied: pin the copies so the refill is
     // issued after them and reuses the registers
 #pragma unroll
@@ -203,6 +246,23 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
 #pragma unroll
       for (int e = 0; e < E; ++e)
         g[e] = calib_grad(v[e], g[e], qmax, inv_qmax, C.bins, lbs, C.two_n, C.kl_scale);
+    }
+    if constexpr (KM > 0) {
+      // dL/dz of segment a: the sum over b from 0, in the order of the
+      // mixing kernel (the same fp32 value as its (O^T kron I) g pass)
+#pragma unroll
+      for (int b = 0; b < KM; ++b)
+#pragma unroll
+        for (int e = 0; e < E; ++e) g[e] = fmaf(__uint_as_float(om[b]), __uint_as_float(gm[b][e]), g[e]);
+      // then the next group's segments into the same registers: they have
+      // this group's reverse sweep and the next forward to arrive
+      a0 += r_stride;
+      r0 += q_stride;
+      if (a0 >= km) {
+        a0 -= km;
+        ++r0;
+      }
+      load_gm();
     }
 
     // reverse sweep: for each stage from the last, accumulate the angle
@@ -271,11 +331,14 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
   }
 }
 
-// Pass 2.  A block covers 32 consecutive angles with 8 lanes each: lane q
-// sums slots q, q + 8, q + 16, ... in that order (fp64), then lane 0 adds
-// the eight sums in order q = 0 .. 7.  The order depends only on the slot
-// count, so the result is bit-identical from run to run.
-constexpr int RED_PARTS = 8, RED_COLS = 32;
+// Pass 2.  A block covers 8 consecutive angles with 32 lanes each: lane q
+// sums slots q, q + 32, q + 64, ... in that order (fp64), then lane 0 adds
+// the 32 sums in order q = 0 .. 31.  The order depends only on the slot
+// count, so the result is bit-identical from run to run.  Each lane keeps
+// four loads in flight (count / 8 blocks: 640 at n = 1024, 3072 at 4096);
+// with 8 lanes per angle and 160 blocks the pass was latency-bound (39.5 us
+// for 1024 slots of 5120 angles, 21 MB).
+constexpr int RED_PARTS = 32, RED_COLS = 8;
 
 __global__ void __launch_bounds__(RED_PARTS * RED_COLS)
 reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ dtheta, int nslots,
@@ -284,8 +347,21 @@ reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ d
   const int c = threadIdx.x % RED_COLS, q = threadIdx.x / RED_COLS;
   const int k = blockIdx.x * RED_COLS + c;
   double sum = 0.0;
-  if (k < count)
-    for (int sl = q; sl < nslots; sl += RED_PARTS) sum += (double)partials[(int64_t)sl * count + k];
+  if (k < count) {
+    const float* const col = partials + k;
+    int sl = q;
+    for (; sl + 3 * RED_PARTS < nslots; sl += 4 * RED_PARTS) {
+      const float a0 = col[(int64_t)sl * count];
+      const float a1 = col[(int64_t)(sl + RED_PARTS) * count];
+      const float a2 = col[(int64_t)(sl + 2 * RED_PARTS) * count];
+      const float a3 = col[(int64_t)(sl + 3 * RED_PARTS) * count];
+      sum += (double)a0;
+      sum += (double)a1;
+      sum += (double)a2;
+      sum += (double)a3;
+    }
+    for (; sl < nslots; sl += RED_PARTS) sum += (double)col[(int64_t)sl * count];
+  }
   part[q][c] = sum;
   __syncthreads();
   if (q == 0 && k < count) {
@@ -547,16 +623,16 @@ int backward_blocks(int64_t rows, int logn) {
   return (int)(ngrp < cap ? (ngrp > 0 ? ngrp : 1) : cap);
 }
 
-template <int LOGN, bool CALIB = false>
+template <int LOGN, bool CALIB = false, int KM = 0>
 static hipError_t launch_bwd_inst(const BwdParams& p, float* dtheta, hipStream_t s,
                                   const CalibGradArgs& c = CalibGradArgs{}) {
   using S = BwdShape<LOGN>;
   const hipError_t lds_ok =
-      kernel_setup(reinterpret_cast<const void*>(bwd_kernel<LOGN, CALIB>), S::NT, S::LDS_BYTES,
+      kernel_setup(reinterpret_cast<const void*>(bwd_kernel<LOGN, CALIB, KM>), S::NT, S::LDS_BYTES,
                    nullptr, nullptr);
   if (lds_ok != hipSuccess) return lds_ok;
   if (p.nblk > 0) {
-    hipLaunchKernelGGL((bwd_kernel<LOGN, CALIB>), dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p, c);
+    hipLaunchKernelGGL((bwd_kernel<LOGN, CALIB, KM>), dim3(p.nblk), dim3(S::NT), S::LDS_BYTES, s, p, c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -577,6 +653,30 @@ hipError_t launch_backward_calib(const BwdParams& p, const CalibGradArgs& c, flo
     case 10: return launch_bwd_inst<10, true>(p, dtheta, s, c);
     case 11: return launch_bwd_inst<11, true>(p, dtheta, s, c);
     case 12: return launch_bwd_inst<12, true>(p, dtheta, s, c);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KM>
+static hipError_t launch_bwd_kron_m(const BwdParams& p, float* dtheta, hipStream_t s) {
+  switch (p.logn) {  // segment lengths of the Kronecker composites: 256 .. 4096
+    case 8: return launch_bwd_inst<8, false, KM>(p, dtheta, s);
+    case 9: return launch_bwd_inst<9, false, KM>(p, dtheta, s);
+    case 10: return launch_bwd_inst<10, false, KM>(p, dtheta, s);
+    case 11: return launch_bwd_inst<11, false, KM>(p, dtheta, s);
+    case 12: return launch_bwd_inst<12, false, KM>(p, dtheta, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_backward_kron(const BwdParams& p, float* dtheta, hipStream_t s) {
+  if (p.mixt == nullptr) return hipErrorInvalidValue;
+  static_assert(kKronBwdFusedM == 5, "one kernel per segment count 2 .. 5");
+  switch (p.m) {  // the segment count is a compile-time constant of each kernel
+    case 2: return launch_bwd_kron_m<2>(p, dtheta, s);
+    case 3: return launch_bwd_kron_m<3>(p, dtheta, s);
+    case 4: return launch_bwd_kron_m<4>(p, dtheta, s);
+    case 5: return launch_bwd_kron_m<5>(p, dtheta, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -188,6 +188,11 @@ struct BwdParams {
   int64_t rows;
   int32_t logn;
   int32_t nblk;       // number of partial slots = grid size
+  // Kronecker composites (launch_backward_kron): g is [rows / m][m n] and
+  // the kernel forms each segment's dL/dz = (O^T kron I) g as it loads it;
+  // mixt = O^T, [m][m] row-major.  m = 0 otherwise.
+  const float* mixt;
+  int32_t m;
 };
 
 // Kernel-launch helpers; each returns the hipError_t of the launch.
@@ -245,6 +250,11 @@ struct LaunchEvents {
 LaunchEvents take_forward_events();
 void arm_forward_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_backward(const BwdParams& p, float* dtheta, hipStream_t s);
+// The backward of (O kron B) over rows / m rows of m segments (p.rows counts
+// segments), the O^T mix folded into the gradient loads: m <= kKronBwdFusedM,
+// g not aliased by dx.
+constexpr int kKronBwdFusedM = 5;
+hipError_t launch_backward_kron(const BwdParams& p, float* dtheta, hipStream_t s);
 
 // Whether a forward instantiation exists for (lognb, m); validation uses it.
 bool forward_supported(int lognb, int m);

@@ -855,8 +855,11 @@ def test_calibration_workload_full():
 # Kronecker backward
 # ---------------------------------------------------------------------------
 
+# m <= 5 out of place: one pass (the O^T mix formed in the backward's loads);
+# in place and m > 5: the mixing pass, then the backward.  Both give the same bits.
 @pytest.mark.parametrize("m,nb,rows", [(5, 1024, 37), (2, 256, 300), (3, 2048, 9), (8, 1024, 64),
-                                       (43, 256, 21), (9, 512, 40), (16, 1024, 7), (64, 256, 5)])
+                                       (43, 256, 21), (9, 512, 40), (16, 1024, 7), (64, 256, 5),
+                                       (4, 512, 50), (2, 4096, 11), (5, 256, 3), (3, 1024, 1)])
 def test_kron_backward(m, nb, rows):
     rng = np.random.default_rng(5000 + 10 * m + nb + rows)
     th = rand_theta(rng, nb)
@@ -876,9 +879,12 @@ def test_kron_backward(m, nb, rows):
     assert r["ok"], r
     r = check_dtheta(host(dth), ref["dtheta"], ref["dabs"], nb)
     assert r["ok"], r
-    # in place on g gives the same bits; a second call (same workspace) too
+    # in place on g gives the same bits, dx and dtheta; a second call (same
+    # workspace) too
+    dth1 = host(dth)
     B.bfly_kron_backward(xd, gd, gd, dth, dev(mix), ws, theta_b=dev(th))
     assert np.array_equal(host(gd), host(dx))
+    assert np.array_equal(host(dth), dth1)
 
 
 # ---------------------------------------------------------------------------
