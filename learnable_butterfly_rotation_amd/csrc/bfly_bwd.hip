@@ -331,14 +331,14 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
   }
 }
 
-// Pass 2.  A block covers 8 consecutive angles with 32 lanes each: lane q
-// sums slots q, q + 32, q + 64, ... in that order (fp64), then lane 0 adds
-// the 32 sums in order q = 0 .. 31.  The order depends only on the slot
+// Pass 2.  A block covers 32 consecutive angles with 8 lanes each: lane q
+// sums slots q, q + 8, q + 16, ... in that order (fp64), then lane 0 adds
+// the eight sums in order q = 0 .. 7.  The order depends only on the slot
 // count, so the result is bit-identical from run to run.  Each lane keeps
-// four loads in flight (count / 8 blocks: 640 at n = 1024, 3072 at 4096);
-// with 8 lanes per angle and 160 blocks the pass was latency-bound (39.5 us
-// for 1024 slots of 5120 angles, 21 MB).
-constexpr int RED_PARTS = 32, RED_COLS = 8;
+// four loads in flight: with one at a time the pass was latency-bound
+// (1024 slots of 5120 angles, 21 MB: 39.5 us, now 14.4 us; 256 slots of
+// 24576 angles: 15 us, now 7.5 us).  32 lanes per angle was no faster.
+constexpr int RED_PARTS = 8, RED_COLS = 32;
 
 __global__ void __launch_bounds__(RED_PARTS * RED_COLS)
 reduce_partials_kernel(const float* __restrict__ partials, float* __restrict__ dtheta, int nslots,
