@@ -120,6 +120,7 @@ __global__ __launch_bounds__(CALIB_SLICES*(CALIB_MAX_BINS + 1)) void calib_reduc
     const CalibLossParams P, int nblk) {
   __shared__ double part[CALIB_SLICES][CALIB_MAX_BINS + 1];
   __shared__ double p[CALIB_MAX_BINS + 1];
+  __shared__ double klt[CALIB_MAX_BINS];  // each bin's KL term, added in bin order below
   const int t = threadIdx.x, bins = P.bins;
   const double N = (double)P.rows * (double)P.n;
   {
@@ -127,8 +128,20 @@ __global__ __launch_bounds__(CALIB_SLICES*(CALIB_MAX_BINS + 1)) void calib_reduc
     if (b <= bins) {
       const int per = (nblk + CALIB_SLICES - 1) / CALIB_SLICES;
       const int k1 = min(nblk, (q + 1) * per);
+      // in order, four loads in flight (one at a time left the pass latency-bound)
+      const float* const col = P.partials + b;
+      const int64_t stride = bins + 1;
       double acc = 0.0;
-      for (int k = q * per; k < k1; ++k) acc += (double)P.partials[(int64_t)k * (bins + 1) + b];
+      int k = q * per;
+      for (; k + 3 < k1; k += 4) {
+        const float a0 = col[k * stride], a1 = col[(k + 1) * stride];
+        const float a2 = col[(k + 2) * stride], a3 = col[(k + 3) * stride];
+        acc += (double)a0;
+        acc += (double)a1;
+        acc += (double)a2;
+        acc += (double)a3;
+      }
+      for (; k < k1; ++k) acc += (double)col[k * stride];
       part[q][b] = acc;
     }
   }
@@ -141,14 +154,14 @@ __global__ __launch_bounds__(CALIB_SLICES*(CALIB_MAX_BINS + 1)) void calib_reduc
   __syncthreads();
   if (t < bins) {
     const double ps = (p[t] + (double)kCalibSmooth) / (1.0 + bins * (double)kCalibSmooth);
-    P.lb[t] = (float)log(bins * ps);
+    const double lg = log(bins * ps);
+    P.lb[t] = (float)lg;
+    klt[t] = ps * lg;
   }
+  __syncthreads();
   if (t == 0) {
     double kl = 0.0;
-    for (int b = 0; b < bins; ++b) {
-      const double ps = (p[b] + (double)kCalibSmooth) / (1.0 + bins * (double)kCalibSmooth);
-      kl += ps * log(bins * ps);
-    }
+    for (int b = 0; b < bins; ++b) kl += klt[b];
     const double rec = p[bins];  // squared error / N
     P.loss[0] = (float)(rec + P.lambda_kl * kl);
     P.loss[1] = (float)rec;
