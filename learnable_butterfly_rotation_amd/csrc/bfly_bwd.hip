@@ -66,9 +66,9 @@ struct BwdShape {
 // segments; each row of length N is segment a of row r of g, and its dL/dz
 // = sum_b O[b][a] g[r][b N + .] is formed from the m segments of g as they
 // are loaded (duidaima.com write-up, section "butterfly": the Kronecker
-// composite; the mix is the transpose of the forward's).  The segments'
-// loads are issued at the start of the row group, ahead of the next group's
-// prefetch, and consumed after the forward recompute.
+// composite; the mix is the transpose of the forward's).  A group's
+// segments are loaded while the group before it finishes (issued right after
+// that group's mix) and mixed after this group's forward recompute.
 template <int LOGN, bool CALIB, int KM = 0>
 __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, CalibGradArgs C) {
   using S = BwdShape<LOGN>;
