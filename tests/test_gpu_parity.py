@@ -887,6 +887,47 @@ def test_kron_backward(m, nb, rows):
     assert np.array_equal(host(dth), dth1)
 
 
+@pytest.mark.timeout(900)
+def test_kron_backward_workload_full():
+    """The Kronecker backward at its benchmark shape and call: 32768 fp32 rows
+    of n = 5120 = O5 (x) B1024 (the composite's theta_b and O5 from its seed),
+    x and G ~ N(0, 1) drawn by blocks of 2048 rows; the one-pass kernel.
+    dtheta_b over all rows against the oracle (summed block by block), dX on
+    three sampled blocks."""
+    w = inputs.kron_int4(rows=16)
+    th, mix = w["theta_b"], w["mix"]
+    rows, m, nb, blk = 32768, 5, 1024, 2048
+    n = m * nb
+    X = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    G = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    d64 = np.zeros(th.shape)
+    dabs = np.zeros(th.shape)
+    sampled = {0, rows // blk // 2, rows // blk - 1}
+    keep = {}
+    for k in range(rows // blk):
+        rng = np.random.default_rng(71000 + k)
+        x = rng.standard_normal((blk, n)).astype(np.float32)
+        g = rng.standard_normal((blk, n)).astype(np.float32)
+        X[k * blk:(k + 1) * blk].copy_(torch.from_numpy(x))
+        G[k * blk:(k + 1) * blk].copy_(torch.from_numpy(g))
+        ref = oracle.kron_backward(x, g, th, mix)
+        d64 += ref["dtheta"]
+        dabs += ref["dabs"]
+        if k in sampled:
+            keep[k] = (np.abs(g).max(axis=1), ref["dx"])
+    ws = torch.empty(B.bfly_kron_backward_workspace_bytes(rows, m, nb), dtype=torch.uint8,
+                     device="cuda")
+    dX = torch.empty_like(X)
+    dth = torch.empty(th.shape, dtype=torch.float32, device="cuda")
+    B.bfly_kron_backward(X, G, dX, dth, dev(mix), ws, theta_b=dev(th))
+    r = check_dtheta(host(dth), d64, dabs, nb)
+    print("kron backward dtheta:", r)
+    assert r["ok"], r
+    for k, (gmax, dx64) in keep.items():
+        r = check_f32(host(dX[k * blk:(k + 1) * blk]), dx64, gmax, n)
+        assert r["ok"], (k, r)
+
+
 # ---------------------------------------------------------------------------
 # wide Kronecker composites (m up to 64): mix pass, then the fused butterfly
 # ---------------------------------------------------------------------------
