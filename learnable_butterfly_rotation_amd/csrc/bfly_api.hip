@@ -586,12 +586,10 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
       !aligned(dtheta_b, 4) || !aligned(mix, 4) || (coeffs_b && !aligned(coeffs_b, 16)) ||
       (theta_b && !aligned(theta_b, 4)))
     return BFLY_ERR_ALIGN;
-  const hipError_t e0 = bfly::launch_kron_bwd_setup(mix, m, reinterpret_cast<float*>(workspace),
-                                                     (hipStream_t)hip_stream);  // O^T
-  if (e0 != hipSuccess) return hip_fail(e0);
   if (rows > 0 && m <= bfly::kKronBwdFusedM && dx != g) {
     // One pass: the backward kernel forms (O^T kron I) G from G's segments
-    // as it loads them (the same fp32 values as the mixing pass below).
+    // and O's columns as it loads them (the same fp32 values as the mixing
+    // pass below).
     char* wsb = static_cast<char*>(workspace) + o_bwd;
     const void* tab = coeffs_b;
     if (!tab) {
@@ -609,7 +607,7 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
     p.rows = rows * m;
     p.logn = l;
     p.nblk = bfly::backward_blocks(rows * m, l);
-    p.mixt = reinterpret_cast<const float*>(workspace);
+    p.mix = mix;
     p.m = m;
     const hipError_t e = bfly::launch_backward_kron(p, dtheta_b, (hipStream_t)hip_stream);
     return e == hipSuccess ? BFLY_OK : hip_fail(e);
@@ -617,7 +615,8 @@ bfly_status bfly_kron_backward(const float* x, const float* g, float* dx, float*
   const hipStream_t s = (hipStream_t)hip_stream;
   char* ws = static_cast<char*>(workspace);
   float* mix_t = reinterpret_cast<float*>(ws);
-  hipError_t e;
+  hipError_t e = bfly::launch_kron_bwd_setup(mix, m, mix_t, s);  // O^T
+  if (e != hipSuccess) return hip_fail(e);
   if (rows > 0) {
     // dL/dz = (O^T kron I) G: the mixing step with O^T (each thread reads all
     // m segments of its columns before writing them, so dx == g is safe)

@@ -166,14 +166,14 @@ __global__ void __launch_bounds__(BwdShape<LOGN>::NT) bwd_kernel(BwdParams P, Ca
       const int64_t avail = rows / m - r0;  // whole rows from r0 on
       const uint32_t nr = (uint32_t)(avail <= 0 ? 0 : (avail < R + 1 ? avail : R + 1));
       const auto rg = buffer_range32(P.g + r0 * ((int64_t)m * N), nr * (uint32_t)(m * N * 4));
-      const auto ro = buffer_range32(P.mixt, (uint32_t)(m * m * 4));
+      const auto ro = buffer_range32(P.mix, (uint32_t)(m * m * 4));
       const uint32_t at = (uint32_t)(a0 + team);  // < m + R
       const int rrel = (int)(at / (uint32_t)m), a = (int)(at - (uint32_t)rrel * (uint32_t)m);
       const uint32_t el = (uint32_t)lay<LOGE>(t, 0, BL);
       const uint32_t base = ((uint32_t)(rrel * m * N) + el) * 4u;
 #pragma unroll
       for (int b = 0; b < KM; ++b) {
-        om[b] = buf_ld4(ro, (uint32_t)(a * m + b) * 4u);
+        om[b] = buf_ld4(ro, (uint32_t)(b * m + a) * 4u);  // O[b][a]
 #pragma unroll
         for (int e = 0; e < E; ++e)
           gm[b][e] = buf_ld4(rg, base + (((uint32_t)(b * N) + ((uint32_t)e << BL)) * 4u));
@@ -670,7 +670,7 @@ static hipError_t launch_bwd_kron_m(const BwdParams& p, float* dtheta, hipStream
 }
 
 hipError_t launch_backward_kron(const BwdParams& p, float* dtheta, hipStream_t s) {
-  if (p.mixt == nullptr) return hipErrorInvalidValue;
+  if (p.mix == nullptr) return hipErrorInvalidValue;
   static_assert(kKronBwdFusedM == 5, "one kernel per segment count 2 .. 5");
   switch (p.m) {  // the segment count is a compile-time constant of each kernel
     case 2: return launch_bwd_kron_m<2>(p, dtheta, s);

@@ -190,8 +190,8 @@ struct BwdParams {
   int32_t nblk;       // number of partial slots = grid size
   // Kronecker composites (launch_backward_kron): g is [rows / m][m n] and
   // the kernel forms each segment's dL/dz = (O^T kron I) g as it loads it;
-  // mixt = O^T, [m][m] row-major.  m = 0 otherwise.
-  const float* mixt;
+  // mix = O, [m][m] row-major (the caller's).  m = 0 otherwise.
+  const float* mix;
   int32_t m;
 };
 
